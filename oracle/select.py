@@ -1,0 +1,118 @@
+"""Candidate page selection (test infrastructure).
+
+EntmaxKV summary section 2.B names two policies:
+
+1. Fixed-budget top-k: keep the k pages with the highest bounding-box upper
+   bounds.  Readings: ties go to the lower logical page id; k >= n keeps
+   every page; the result is returned in ascending page order.
+
+2. Gaussian-aware entmax selection: estimate the global alpha-entmax
+   threshold from the page-level Gaussian statistics by solving an
+   approximate normalisation equation for tau_hat, then keep the pages whose
+   estimated maximum score exceeds tau_hat minus a safety margin Delta.
+   Readings (the pages give no formula):
+     * the normalisation equation is the expected total entmax mass under the
+       per-page Gaussian score model,
+           F(t) = sum_p n_p E[(Y_p - t)_+^(1/(alpha-1))] = 1,
+         Y_p ~ N(mean_Y,p, sd_Y,p^2),
+       solved per query head;
+     * Delta is measured in the scaled domain where tau lives;
+     * a page is kept for a KV head when any query head of its group keeps
+       it: max_h (e_hat[h,p] - tau_hat[h]) > -Delta (strict);
+     * if that keeps nothing, the single page maximising that quantity is
+       kept (lowest page id on ties), since entmax over an empty set is
+       undefined.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erfc
+
+_INV_SQRT2 = 1.0 / math.sqrt(2.0)
+_INV_SQRT2PI = 1.0 / math.sqrt(2.0 * math.pi)
+
+
+def topk_pages(S: np.ndarray, k: int) -> np.ndarray:
+    """Ascending ids of the min(k, n) highest scores, lower id wins ties."""
+    S = np.asarray(S, dtype=np.float64)
+    n = S.size
+    order = np.lexsort((np.arange(n), -S))  # primary key -S, then id
+    return np.sort(order[: min(k, n)])
+
+
+def gauss_expected_mass(mu: np.ndarray, sd: np.ndarray, t: float, alpha: float) -> np.ndarray:
+    """E[(Y - t)_+^(1/(alpha-1))] for Y ~ N(mu, sd^2), per page.
+
+    With u = (mu - t)/sd, Phi(u) = erfc(-u/sqrt 2)/2, phi(u) = exp(-u^2/2)/sqrt(2 pi):
+      alpha=2   (exponent 1): (mu - t) Phi(u) + sd phi(u)
+      alpha=1.5 (exponent 2): ((mu - t)^2 + sd^2) Phi(u) + (mu - t) sd phi(u)
+    and (mu - t)_+^exponent when sd = 0.
+    """
+    mu = np.asarray(mu, dtype=np.float64)
+    sd = np.asarray(sd, dtype=np.float64)
+    a = mu - t
+    out = np.empty_like(mu)
+    z = sd <= 0.0
+    nz = ~z
+    if alpha == 2.0:
+        out[z] = np.maximum(a[z], 0.0)
+    elif alpha == 1.5:
+        out[z] = np.maximum(a[z], 0.0) ** 2
+    else:
+        raise ValueError("Gaussian expectation implemented for alpha in {1.5, 2}")
+    if np.any(nz):
+        s = sd[nz]
+        u = a[nz] / s
+        Phi = 0.5 * erfc(-u * _INV_SQRT2)
+        phi = np.exp(-0.5 * u * u) * _INV_SQRT2PI
+        if alpha == 2.0:
+            out[nz] = a[nz] * Phi + s * phi
+        else:
+            out[nz] = (a[nz] ** 2 + s * s) * Phi + a[nz] * s * phi
+    return out
+
+
+def gauss_tau_hat(mu: np.ndarray, sd: np.ndarray, count: np.ndarray, alpha: float,
+                  iters: int = 200) -> float:
+    """Solve F(t) = sum_p n_p E_p(t) = 1 by bisection.
+
+    F is continuous and strictly decreasing where positive.  Left end
+    t_lo = max_p mu_p - 1: there F >= 1, because E_p(t) >= (mu_p - t)_+^e
+    (Jensen, the integrand is convex in Y) and the top page alone gives
+    n_p * 1 >= 1.  Right end: step right from t_lo, doubling, until F <= 1.
+    """
+    mu = np.asarray(mu, dtype=np.float64)
+    sd = np.asarray(sd, dtype=np.float64)
+    n = np.asarray(count, dtype=np.float64)
+
+    def F(t):
+        return float(np.sum(n * gauss_expected_mass(mu, sd, t, alpha)))
+
+    lo = float(mu.max()) - 1.0
+    step = 1.0
+    hi = lo + step
+    while F(hi) > 1.0:
+        step *= 2.0
+        hi = lo + step
+    for _ in range(iters):
+        mid = 0.5 * (lo + hi)
+        if mid <= lo or mid >= hi:
+            break
+        if F(mid) >= 1.0:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
+def gauss_keep_pages(e_hat: np.ndarray, tau_hat: np.ndarray, delta: float) -> np.ndarray:
+    """e_hat: [G][n] estimated maxima of the group's heads, tau_hat: [G].
+    Ascending ids of kept pages (at least one)."""
+    e_hat = np.asarray(e_hat, dtype=np.float64)
+    margin = np.max(e_hat - np.asarray(tau_hat, dtype=np.float64)[:, None], axis=0)
+    keep = np.nonzero(margin > -delta)[0]
+    if keep.size == 0:
+        keep = np.array([int(np.argmax(margin))])  # argmax returns the first (lowest id)
+    return keep

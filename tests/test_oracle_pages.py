@@ -1,0 +1,112 @@
+"""Pins of the oracle's page metadata, bounding-box bound and top-k against
+what the EntmaxKV summary (sec. 2.A/2.B) fixes: the box bound is an upper
+bound on every token score of the page (and the tightest one the box allows,
+checked against all box vertices), and top-k keeps the k best pages (brute
+force over all k-subsets)."""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import metadata, scoring, select
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_derived.json")))
+
+
+def test_golden_bbox():
+    c = GOLD["bbox"][0]
+    k = np.array(c["keys"])
+    md = metadata.page_metadata(k, len(k), len(k))
+    np.testing.assert_array_equal(md["kmin"][0], c["kmin"])
+    np.testing.assert_array_equal(md["kmax"][0], c["kmax"])
+    U = scoring.bbox_bound(np.array(c["q"]), md["kmin"], md["kmax"], c["scale"])
+    assert U[0] == c["bound"]
+    np.testing.assert_allclose(k @ np.array(c["q"]), c["token_scores"])
+
+
+def test_metadata_invariants():
+    rng = np.random.default_rng(10)
+    for L, P in [(1, 4), (4, 4), (17, 4), (100, 16), (65, 64)]:
+        k = rng.standard_normal((L + 3, 5))
+        md = metadata.page_metadata(k, L, P)
+        n = metadata.page_count(L, P)
+        assert md["kmin"].shape == (n, 5) and md["count"].sum() == L
+        for p in range(n):
+            blk = k[p * P : p * P + md["count"][p]]
+            # per-token loop, independent of the vectorised code
+            for i in range(5):
+                col = [float(blk[t, i]) for t in range(len(blk))]
+                assert md["kmin"][p, i] == min(col) and md["kmax"][p, i] == max(col)
+                m = sum(col) / len(col)
+                assert md["mean"][p, i] == pytest.approx(m, abs=1e-13)
+                # E[k^2] - E[k]^2 (a different formula from the two-pass one)
+                assert md["var"][p, i] == pytest.approx(sum(c * c for c in col) / len(col) - m * m, abs=1e-12)
+        # tokens beyond L must not leak into the last page
+        k2 = k.copy()
+        k2[L:] = 1e9
+        np.testing.assert_array_equal(metadata.page_metadata(k2, L, P)["kmax"], md["kmax"])
+
+
+def test_bbox_is_upper_bound_and_tight():
+    rng = np.random.default_rng(11)
+    for _ in range(40):
+        d = 4
+        P = int(rng.integers(1, 9))
+        L = int(rng.integers(1, 40))
+        k = rng.standard_normal((L, d)) * rng.uniform(0.2, 3)
+        q = rng.standard_normal(d) * 2
+        md = metadata.page_metadata(k, L, P)
+        U = scoring.bbox_bound(q, md["kmin"], md["kmax"], 0.5)
+        for p in range(metadata.page_count(L, P)):
+            blk = k[p * P : p * P + md["count"][p]]
+            assert np.all(U[p] >= 0.5 * (blk @ q) - 1e-12)
+            # tightest: equals the max of q.k over the 2^d vertices of the box
+            verts = [np.where(np.array(bits) == 1, md["kmax"][p], md["kmin"][p])
+                     for bits in itertools.product([0, 1], repeat=d)]
+            assert U[p] == pytest.approx(0.5 * max(float(v @ q) for v in verts), abs=1e-12)
+            if md["count"][p] == 1:
+                assert U[p] == pytest.approx(0.5 * float(blk[0] @ q), abs=1e-12)
+
+
+def test_bbox_monotone_under_append():
+    rng = np.random.default_rng(12)
+    k = rng.standard_normal((16, 6))
+    q = rng.standard_normal(6)
+    prev = -np.inf
+    for L in range(1, 17):
+        md = metadata.page_metadata(k, L, 16)
+        U = scoring.bbox_bound(q, md["kmin"], md["kmax"], 1.0)[0]
+        assert U >= prev
+        prev = U
+
+
+def test_group_score_bounds_every_head():
+    rng = np.random.default_rng(13)
+    k = rng.standard_normal((64, 8))
+    md = metadata.page_metadata(k, 64, 8)
+    qg = rng.standard_normal((4, 8))
+    S = scoring.bbox_page_scores(qg, md["kmin"], md["kmax"], 0.3)
+    Us = [scoring.bbox_bound(qg[h], md["kmin"], md["kmax"], 0.3) for h in range(4)]
+    for U in Us:
+        assert np.all(S >= U)
+    # every page's score is attained by some head of the group
+    assert all(any(S[p] == U[p] for U in Us) for p in range(S.size))
+
+
+def test_topk_brute_force():
+    rng = np.random.default_rng(14)
+    for _ in range(60):
+        n = int(rng.integers(1, 11))
+        k = int(rng.integers(1, n + 3))
+        S = rng.integers(0, 4, n).astype(float)  # small integers force ties
+        got = select.topk_pages(S, k)
+        m = min(k, n)
+        best = None
+        for sub in itertools.combinations(range(n), m):  # lexicographic order
+            s = S[list(sub)].sum()
+            if best is None or s > best[0]:
+                best = (s, sub)
+        assert list(got) == list(best[1])
+        assert list(got) == sorted(got)
