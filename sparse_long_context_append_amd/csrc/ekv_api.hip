@@ -1,0 +1,292 @@
+// extern "C" entry points: host-side validation, workspace carving and
+// launches.  Nothing here allocates device memory; every argument problem is
+// reported before the first HIP call.
+#include <math.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "ekv_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ekv_status fail(ekv_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+ekv_status check_cache(const ekv_cache* c) {
+  if (!c) return fail(EKV_ERR_INVALID_ARG, "cache is NULL");
+  if (c->n_phys_pages <= 0) return fail(EKV_ERR_INVALID_ARG, "n_phys_pages must be > 0");
+  if (c->n_kv_heads <= 0) return fail(EKV_ERR_INVALID_ARG, "n_kv_heads must be > 0");
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(EKV_ERR_INVALID_ARG, "head_dim must be 64 or 128");
+  const int P = c->page_size;
+  if (P < 1 || P > 1024 || (P & (P - 1)) != 0)
+    return fail(EKV_ERR_INVALID_ARG, "page_size must be a power of two in [1, 1024]");
+  if (c->kv_dtype != EKV_F32 && c->kv_dtype != EKV_BF16) return fail(EKV_ERR_INVALID_ARG, "kv_dtype must be EKV_F32 or EKV_BF16");
+  if (!c->k || !c->v) return fail(EKV_ERR_INVALID_ARG, "cache k/v pointer is NULL");
+  if (!aligned16(c->k) || !aligned16(c->v) || !aligned16(c->k_box) || !aligned16(c->k_moments))
+    return fail(EKV_ERR_INVALID_ARG, "cache pointers must be 16-byte aligned");
+  const double elems = (double)c->n_phys_pages * c->n_kv_heads * P * c->head_dim;
+  if (elems >= 9.0e18) return fail(EKV_ERR_INVALID_ARG, "cache too large");
+  return EKV_OK;
+}
+
+ekv_status check_seqs(const ekv_cache* c, const ekv_seqs* s) {
+  if (!s) return fail(EKV_ERR_INVALID_ARG, "seqs is NULL");
+  if (s->batch <= 0) return fail(EKV_ERR_INVALID_ARG, "batch must be > 0");
+  if (s->max_pages <= 0) return fail(EKV_ERR_INVALID_ARG, "max_pages must be > 0");
+  if (!s->page_table || !s->seq_lens) return fail(EKV_ERR_INVALID_ARG, "page_table/seq_lens is NULL");
+  if ((long long)s->max_pages * c->page_size > 0x7fffffffLL)
+    return fail(EKV_ERR_INVALID_ARG, "max_pages * page_size must fit in int32");
+  if ((long long)s->batch * c->n_kv_heads > ekv::kMaxUnits)
+    return fail(EKV_ERR_UNSUPPORTED, "batch * n_kv_heads above 4096");
+  return EKV_OK;
+}
+
+ekv_status check_heads(const ekv_cache* c, int32_t n_q_heads, int* group) {
+  if (n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0)
+    return fail(EKV_ERR_INVALID_ARG, "n_q_heads must be a positive multiple of n_kv_heads");
+  const int G = n_q_heads / c->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(EKV_ERR_UNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8");
+  *group = G;
+  return EKV_OK;
+}
+
+ekv_status check_ws(const ekv_cache* c, const ekv_seqs* s, int32_t n_q_heads, void* ws, size_t ws_bytes,
+                    ekv::Layout* L) {
+  *L = ekv::make_layout(s->batch, c->n_kv_heads, n_q_heads, s->max_pages, c->page_size);
+  if (!ws) return fail(EKV_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned16(ws)) return fail(EKV_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  if (ws_bytes < L->total)
+    return fail(EKV_ERR_WORKSPACE, "workspace holds " + std::to_string(ws_bytes) + " bytes, needs " +
+                                       std::to_string(L->total));
+  return EKV_OK;
+}
+
+template <typename T> T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off);
+}
+
+ekv_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return EKV_OK;
+  return fail(EKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+  return cus;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ekv_workspace_size(const ekv_cache* cache, const ekv_seqs* seqs, int32_t n_q_heads) {
+  int G = 0;
+  if (check_cache(cache) != EKV_OK || check_seqs(cache, seqs) != EKV_OK ||
+      check_heads(cache, n_q_heads, &G) != EKV_OK)
+    return 0;
+  return ekv::make_layout(seqs->batch, cache->n_kv_heads, n_q_heads, seqs->max_pages, cache->page_size).total;
+}
+
+ekv_status ekv_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
+  if (!workspace || ws_bytes == 0) return fail(EKV_ERR_WORKSPACE, "workspace is NULL or empty");
+  if (!aligned16(workspace) || ws_bytes % 16 != 0)
+    return fail(EKV_ERR_WORKSPACE, "workspace must be 16-byte aligned with a size that is a multiple of 16");
+  return hip_status(ekv::launch_fill_zero(workspace, ws_bytes, (hipStream_t)stream), "workspace init");
+}
+
+ekv_status ekv_append_kv(const ekv_cache* cache, const ekv_seqs* seqs, const void* k_new, const void* v_new,
+                         int32_t n_new, void* workspace, size_t ws_bytes, void* stream) {
+  ekv_status st;
+  if ((st = check_cache(cache)) != EKV_OK) return st;
+  if ((st = check_seqs(cache, seqs)) != EKV_OK) return st;
+  if (n_new < 0) return fail(EKV_ERR_INVALID_ARG, "n_new must be >= 0");
+  if (n_new > 0 && (!k_new || !v_new)) return fail(EKV_ERR_INVALID_ARG, "k_new/v_new is NULL");
+  if ((long long)n_new > (long long)seqs->max_pages * cache->page_size)
+    return fail(EKV_ERR_INVALID_ARG, "n_new exceeds max_pages * page_size");
+  // append only touches the status word at the start of the workspace
+  if (!workspace || ws_bytes < 256 || !aligned16(workspace))
+    return fail(EKV_ERR_WORKSPACE, "workspace is NULL, unaligned or smaller than 256 bytes");
+  if (n_new == 0) return EKV_OK;
+  ekv::AppendArgs a{};
+  a.batch = seqs->batch; a.n_kv_heads = cache->n_kv_heads; a.page_size = cache->page_size;
+  a.head_dim = cache->head_dim; a.kv_dtype = cache->kv_dtype; a.max_pages = seqs->max_pages;
+  a.n_phys = cache->n_phys_pages; a.n_new = n_new;
+  a.page_table = seqs->page_table; a.seq_lens = seqs->seq_lens;
+  a.k = cache->k; a.v = cache->v; a.k_box = cache->k_box; a.k_moments = cache->k_moments;
+  a.k_new = k_new; a.v_new = v_new;
+  a.status = at<uint32_t>(workspace, 0);
+  return hip_status(ekv::launch_append(a, (hipStream_t)stream), "append_kv launch");
+}
+
+static ekv_status prepare_select(const ekv_cache* cache, const ekv_seqs* seqs, const float* q, int32_t n_q_heads,
+                                 const ekv_select_params* p, void* workspace, size_t ws_bytes,
+                                 ekv::SelectArgs* a, ekv::Layout* L) {
+  ekv_status st;
+  int G = 0;
+  if ((st = check_cache(cache)) != EKV_OK) return st;
+  if ((st = check_seqs(cache, seqs)) != EKV_OK) return st;
+  if ((st = check_heads(cache, n_q_heads, &G)) != EKV_OK) return st;
+  if (!q || !aligned16(q)) return fail(EKV_ERR_INVALID_ARG, "q is NULL or not 16-byte aligned");
+  if (!p) return fail(EKV_ERR_INVALID_ARG, "params is NULL");
+  if (!(p->scale > 0.f) || !isfinite(p->scale)) return fail(EKV_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (p->policy == EKV_SELECT_BBOX_TOPK) {
+    if (!cache->k_box) return fail(EKV_ERR_INVALID_ARG, "bounding-box selection needs cache->k_box");
+    if (p->top_k < 1) return fail(EKV_ERR_INVALID_ARG, "top_k must be >= 1");
+  } else if (p->policy == EKV_SELECT_GAUSS) {
+    if (!cache->k_moments) return fail(EKV_ERR_INVALID_ARG, "Gaussian selection needs cache->k_moments");
+    if (p->alpha != 1.5f && p->alpha != 2.0f)
+      return fail(EKV_ERR_UNSUPPORTED, "Gaussian selection supports alpha 1.5 and 2 only");
+    if (!(p->delta >= 0.f) || !isfinite(p->delta)) return fail(EKV_ERR_INVALID_ARG, "delta must be finite and >= 0");
+  } else {
+    return fail(EKV_ERR_INVALID_ARG, "unknown selection policy");
+  }
+  if (!(p->alpha > 1.f) || !isfinite(p->alpha)) return fail(EKV_ERR_INVALID_ARG, "alpha must be finite and > 1");
+  if ((st = check_ws(cache, seqs, n_q_heads, workspace, ws_bytes, L)) != EKV_OK) return st;
+  *a = ekv::SelectArgs{};
+  a->batch = seqs->batch; a->n_kv_heads = cache->n_kv_heads; a->n_q_heads = n_q_heads; a->group = G;
+  a->page_size = cache->page_size; a->head_dim = cache->head_dim; a->kv_dtype = cache->kv_dtype;
+  a->max_pages = seqs->max_pages; a->n_phys = cache->n_phys_pages;
+  a->page_table = seqs->page_table; a->seq_lens = seqs->seq_lens;
+  a->k_box = cache->k_box; a->k_moments = cache->k_moments; a->q = q;
+  a->policy = p->policy; a->top_k = p->top_k; a->alpha = p->alpha; a->scale = p->scale; a->delta = p->delta;
+  a->scores = at<float>(workspace, L->scores);
+  a->stats = at<float4>(workspace, L->stats);
+  a->tau_hat = at<double>(workspace, L->tau_hat);
+  a->status = at<uint32_t>(workspace, L->status);
+  return EKV_OK;
+}
+
+ekv_status ekv_select_pages(const ekv_cache* cache, const ekv_seqs* seqs, const float* q, int32_t n_q_heads,
+                            const ekv_select_params* params, int32_t* sel, int32_t* sel_count, int32_t cap,
+                            float* tau_hat, void* workspace, size_t ws_bytes, void* stream) {
+  ekv::SelectArgs a;
+  ekv::Layout L;
+  ekv_status st = prepare_select(cache, seqs, q, n_q_heads, params, workspace, ws_bytes, &a, &L);
+  if (st != EKV_OK) return st;
+  if (!sel || !sel_count) return fail(EKV_ERR_INVALID_ARG, "sel/sel_count is NULL");
+  if (cap < 1) return fail(EKV_ERR_INVALID_ARG, "cap must be >= 1");
+  if (params->policy == EKV_SELECT_BBOX_TOPK && cap < params->top_k)
+    return fail(EKV_ERR_CAPACITY, "cap must be >= top_k");
+  if (params->policy == EKV_SELECT_GAUSS && cap < seqs->max_pages)
+    return fail(EKV_ERR_CAPACITY, "Gaussian selection needs cap >= max_pages");
+  a.sel = sel; a.sel_count = sel_count; a.cap = cap; a.tau_hat_out = tau_hat;
+  hipStream_t s = (hipStream_t)stream;
+  if (params->policy == EKV_SELECT_BBOX_TOPK) {
+    if ((st = hip_status(ekv::launch_score_bbox(a, s), "score_bbox launch")) != EKV_OK) return st;
+    return hip_status(ekv::launch_topk(a, s), "topk launch");
+  }
+  if ((st = hip_status(ekv::launch_score_gauss(a, s), "score_gauss launch")) != EKV_OK) return st;
+  if ((st = hip_status(ekv::launch_tau_hat(a, s), "tau_hat launch")) != EKV_OK) return st;
+  return hip_status(ekv::launch_gauss_keep(a, s), "gauss_keep launch");
+}
+
+ekv_status ekv_score_pages(const ekv_cache* cache, const ekv_seqs* seqs, const float* q, int32_t n_q_heads,
+                           const ekv_select_params* params, float* scores, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  ekv::SelectArgs a;
+  ekv::Layout L;
+  ekv_status st = prepare_select(cache, seqs, q, n_q_heads, params, workspace, ws_bytes, &a, &L);
+  if (st != EKV_OK) return st;
+  if (!scores || !aligned16(scores)) return fail(EKV_ERR_INVALID_ARG, "scores is NULL or not 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (params->policy == EKV_SELECT_BBOX_TOPK) {
+    a.scores = scores;
+    return hip_status(ekv::launch_score_bbox(a, s), "score_bbox launch");
+  }
+  a.stats = reinterpret_cast<float4*>(scores);
+  return hip_status(ekv::launch_score_gauss(a, s), "score_gauss launch");
+}
+
+ekv_status ekv_entmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const float* q, int32_t n_q_heads,
+                             float alpha, float scale, const int32_t* sel, const int32_t* sel_count, int32_t cap,
+                             float* out, float* tau, int32_t* support_count, float* psum, int32_t* support_idx,
+                             int32_t support_cap, void* workspace, size_t ws_bytes, void* stream) {
+  ekv_status st;
+  int G = 0;
+  if ((st = check_cache(cache)) != EKV_OK) return st;
+  if ((st = check_seqs(cache, seqs)) != EKV_OK) return st;
+  if ((st = check_heads(cache, n_q_heads, &G)) != EKV_OK) return st;
+  if (!q || !aligned16(q)) return fail(EKV_ERR_INVALID_ARG, "q is NULL or not 16-byte aligned");
+  if (!out) return fail(EKV_ERR_INVALID_ARG, "out is NULL");
+  if (!(alpha > 1.f) || !isfinite(alpha)) return fail(EKV_ERR_INVALID_ARG, "alpha must be finite and > 1");
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(EKV_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (sel && (!sel_count || cap < 1)) return fail(EKV_ERR_INVALID_ARG, "sel needs sel_count and cap >= 1");
+  if (support_idx && support_cap < 1) return fail(EKV_ERR_INVALID_ARG, "support_idx needs support_cap >= 1");
+  ekv::Layout L;
+  if ((st = check_ws(cache, seqs, n_q_heads, workspace, ws_bytes, &L)) != EKV_OK) return st;
+  const int P = cache->page_size;
+  // work item: about 64 tokens (sparse) or 256 tokens (full cache) of one KV head
+  const int target = sel ? 64 : 256;
+  int ppi = P >= target ? 1 : target / P;
+  if (ppi > 256) ppi = 256;
+  const int n_units = seqs->batch * cache->n_kv_heads;
+  if (ekv::gather_lds_bytes(n_units, G, ppi, P) > ekv::kMaxGatherLds)
+    return fail(EKV_ERR_UNSUPPORTED, "decode work item does not fit in LDS");
+  ekv::DecodeArgs a{};
+  a.batch = seqs->batch; a.n_kv_heads = cache->n_kv_heads; a.n_q_heads = n_q_heads; a.group = G;
+  a.page_size = P; a.head_dim = cache->head_dim; a.kv_dtype = cache->kv_dtype;
+  a.max_pages = seqs->max_pages; a.n_phys = cache->n_phys_pages;
+  a.page_table = seqs->page_table; a.seq_lens = seqs->seq_lens;
+  a.k = cache->k; a.v = cache->v; a.q = q; a.alpha = alpha; a.scale = scale;
+  a.sel = sel; a.sel_count = sel_count; a.cap = sel ? cap : 0; a.ppi = ppi;
+  a.out = out; a.tau = tau; a.support_count = support_count; a.psum = psum;
+  a.support_idx = support_idx; a.support_cap = support_cap;
+  a.max_key = at<uint32_t>(workspace, L.max_key);
+  a.item_cnt = at<int32_t>(workspace, L.item_cnt);
+  a.item_max = at<float>(workspace, L.item_max);
+  a.cand_x = at<float>(workspace, L.cand_x);
+  a.cand_t = at<int32_t>(workspace, L.cand_t);
+  a.ovf_x = at<float>(workspace, L.ovf_x);
+  a.ovf_t = at<int32_t>(workspace, L.ovf_t);
+  a.status = at<uint32_t>(workspace, L.status);
+  // persistent grid: enough blocks to cover every item of the largest possible
+  // selection, capped at 16 blocks per compute unit
+  const long long per_unit = sel ? ((long long)(cap < seqs->max_pages ? cap : seqs->max_pages) + ppi - 1) / ppi
+                                 : ((long long)seqs->max_pages + ppi - 1) / ppi;
+  long long items = per_unit * n_units;
+  const long long cap_blocks = 16LL * device_cus();
+  if (items > cap_blocks) items = cap_blocks;
+  if (items < 1) items = 1;
+  return hip_status(ekv::launch_decode(a, (int)items, (hipStream_t)stream), "entmax_decode launch");
+}
+
+ekv_status ekv_read_device_status(void* workspace, size_t ws_bytes, int32_t* host_flags) {
+  if (!workspace || ws_bytes < 256) return fail(EKV_ERR_WORKSPACE, "workspace is NULL or too small");
+  if (!host_flags) return fail(EKV_ERR_INVALID_ARG, "host_flags is NULL");
+  uint32_t v = 0;
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost);
+  if (e == hipSuccess) {
+    const uint32_t zero = 0;
+    e = hipMemcpy(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice);
+  }
+  if (e != hipSuccess) return hip_status(e, "read device status");
+  *host_flags = (int32_t)v;
+  return EKV_OK;
+}
+
+const char* ekv_status_string(int32_t status) {
+  switch (status) {
+    case EKV_OK: return "ok";
+    case EKV_ERR_INVALID_ARG: return "invalid argument";
+    case EKV_ERR_UNSUPPORTED: return "unsupported";
+    case EKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case EKV_ERR_CAPACITY: return "selection capacity too small";
+    case EKV_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* ekv_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// Kernel argument blocks and launchers of the EntmaxKV HIP library.
+#pragma once
+
+#include "ekv_common.h"
+
+namespace ekv {
+
+// Limits the kernels are compiled for (checked on the host before launch).
+constexpr int kMaxGroup = 8;         // query heads per KV head
+constexpr int kMaxUnits = 4096;      // batch * n_kv_heads
+constexpr int kMaxItemTokens = 1024; // tokens in one decode work item
+constexpr int kLdsCands = 2048;      // candidates kept in LDS by the threshold solve
+
+struct AppendArgs {
+  int batch, n_kv_heads, page_size, head_dim, kv_dtype, max_pages, n_phys, n_new;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  void* k;
+  void* v;
+  void* k_box;
+  float* k_moments;
+  const void* k_new;
+  const void* v_new;
+  uint32_t* status;
+};
+
+struct SelectArgs {
+  int batch, n_kv_heads, n_q_heads, group, page_size, head_dim, kv_dtype, max_pages, n_phys;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const void* k_box;
+  const float* k_moments;
+  const float* q;
+  int policy, top_k;
+  float alpha, scale, delta;
+  int32_t* sel;
+  int32_t* sel_count;
+  int cap;
+  float* tau_hat_out;  // optional
+  float* scores;       // bbox page scores [B*Hkv*max_pages]
+  float4* stats;       // Gaussian page stats [B*Hq*max_pages]
+  double* tau_hat;     // [B*Hq]
+  uint32_t* status;
+};
+
+struct DecodeArgs {
+  int batch, n_kv_heads, n_q_heads, group, page_size, head_dim, kv_dtype, max_pages, n_phys;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const void* k;
+  const void* v;
+  const float* q;
+  float alpha, scale;
+  const int32_t* sel;  // NULL: every page of every sequence
+  const int32_t* sel_count;
+  int cap;
+  int ppi;  // pages per work item
+  float* out;
+  float* tau;            // optional
+  int32_t* support_count;  // optional
+  float* psum;           // optional
+  int32_t* support_idx;  // optional
+  int support_cap;
+  uint32_t* max_key;
+  int32_t* item_cnt;
+  float* item_max;
+  float* cand_x;
+  int32_t* cand_t;
+  float* ovf_x;
+  int32_t* ovf_t;
+  uint32_t* status;
+};
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_score_bbox(const SelectArgs& a, hipStream_t s);
+hipError_t launch_topk(const SelectArgs& a, hipStream_t s);
+hipError_t launch_score_gauss(const SelectArgs& a, hipStream_t s);
+hipError_t launch_tau_hat(const SelectArgs& a, hipStream_t s);
+hipError_t launch_gauss_keep(const SelectArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int grid_items, hipStream_t s);
+size_t gather_lds_bytes(int n_units, int group, int ppi, int page_size);
+constexpr size_t kMaxGatherLds = 60 * 1024;
+
+}  // namespace ekv

@@ -1,0 +1,127 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every
+function include/entmaxkv.h declares, sizes workspaces, and rejects invalid
+arguments with the documented status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_long_context_append_amd as ekv
+from sparse_long_context_append_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "entmaxkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ekv_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.lib_path):
+        pytest.skip("library not built")
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    syms = declared_symbols()
+    assert len(syms) >= 9
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def cache(**kw):
+    c = dict(n_phys_pages=256, n_kv_heads=8, page_size=16, head_dim=128, kv_dtype=B.EKV_BF16, reserved=0,
+             k=FAKE, v=FAKE, k_box=FAKE, k_moments=FAKE)
+    c.update(kw)
+    return B._Cache(**c)
+
+
+def seqs(**kw):
+    s = dict(batch=1, max_pages=256, page_table=FAKE, seq_lens=FAKE)
+    s.update(kw)
+    return B._Seqs(**s)
+
+
+def test_workspace_size(L):
+    n = L.ekv_workspace_size(ctypes.byref(cache()), ctypes.byref(seqs()), 32)
+    # candidate lists dominate: 4 lists of B*Hq*max_pages*P 4-byte entries
+    assert n >= 4 * 4 * 32 * 256 * 16
+    assert L.ekv_workspace_size(ctypes.byref(cache()), ctypes.byref(seqs()), 12) == 0  # not a multiple of 8
+    assert L.ekv_workspace_size(ctypes.byref(cache(head_dim=96)), ctypes.byref(seqs()), 32) == 0
+    assert L.ekv_workspace_size(ctypes.byref(cache(page_size=24)), ctypes.byref(seqs()), 32) == 0
+    assert L.ekv_workspace_size(ctypes.byref(cache(n_kv_heads=2)), ctypes.byref(seqs()), 64) == 0  # group 32
+    assert L.ekv_workspace_size(None, ctypes.byref(seqs()), 32) == 0
+
+
+def sp(**kw):
+    p = dict(policy=B.EKV_SELECT_BBOX_TOPK, top_k=8, alpha=1.5, scale=0.125, delta=0.5, reserved=0)
+    p.update(kw)
+    return B._SelectParams(**p)
+
+
+def call_select(L, c=None, s=None, q=FAKE, hq=32, p=None, sel=FAKE, cnt=FAKE, cap=64, ws=FAKE, wsb=1 << 40):
+    return L.ekv_select_pages(ctypes.byref(c or cache()), ctypes.byref(s or seqs()), q, hq,
+                              ctypes.byref(p or sp()), sel, cnt, cap, None, ws, wsb, None)
+
+
+def test_select_validation(L):
+    assert call_select(L, q=None) == B.EKV_ERR_INVALID_ARG
+    assert call_select(L, q=FAKE + 4) == B.EKV_ERR_INVALID_ARG  # misaligned
+    assert call_select(L, p=sp(top_k=0)) == B.EKV_ERR_INVALID_ARG
+    assert call_select(L, p=sp(policy=7)) == B.EKV_ERR_INVALID_ARG
+    assert call_select(L, p=sp(alpha=1.0)) == B.EKV_ERR_INVALID_ARG
+    assert call_select(L, p=sp(scale=0.0)) == B.EKV_ERR_INVALID_ARG
+    assert call_select(L, p=sp(policy=B.EKV_SELECT_GAUSS, alpha=1.25)) == B.EKV_ERR_UNSUPPORTED
+    assert call_select(L, c=cache(k_box=None)) == B.EKV_ERR_INVALID_ARG
+    assert call_select(L, c=cache(k_moments=None), p=sp(policy=B.EKV_SELECT_GAUSS)) == B.EKV_ERR_INVALID_ARG
+    assert call_select(L, cap=4) == B.EKV_ERR_CAPACITY
+    assert call_select(L, cap=64, p=sp(policy=B.EKV_SELECT_GAUSS)) == B.EKV_ERR_CAPACITY  # needs max_pages
+    assert call_select(L, ws=None) == B.EKV_ERR_WORKSPACE
+    assert call_select(L, wsb=1024) == B.EKV_ERR_WORKSPACE
+    assert "needs" in ekv.last_error()
+    assert call_select(L, s=seqs(batch=0)) == B.EKV_ERR_INVALID_ARG
+    assert call_select(L, s=seqs(batch=1024)) == B.EKV_ERR_UNSUPPORTED  # 8192 units
+    assert call_select(L, hq=20) == B.EKV_ERR_INVALID_ARG
+    assert call_select(L, sel=None) == B.EKV_ERR_INVALID_ARG
+
+
+def call_decode(L, q=FAKE, alpha=1.5, scale=0.125, sel=FAKE, cnt=FAKE, cap=64, out=FAKE, sidx=None, scap=0,
+                ws=FAKE, wsb=1 << 40, c=None):
+    return L.ekv_entmax_decode(ctypes.byref(c or cache()), ctypes.byref(seqs()), q, 32, alpha, scale, sel, cnt,
+                               cap, out, None, None, None, sidx, scap, ws, wsb, None)
+
+
+def test_decode_validation(L):
+    assert call_decode(L, out=None) == B.EKV_ERR_INVALID_ARG
+    assert call_decode(L, alpha=1.0) == B.EKV_ERR_INVALID_ARG
+    assert call_decode(L, alpha=float("nan")) == B.EKV_ERR_INVALID_ARG
+    assert call_decode(L, scale=-1.0) == B.EKV_ERR_INVALID_ARG
+    assert call_decode(L, cnt=None) == B.EKV_ERR_INVALID_ARG
+    assert call_decode(L, cap=0) == B.EKV_ERR_INVALID_ARG
+    assert call_decode(L, sidx=FAKE, scap=0) == B.EKV_ERR_INVALID_ARG
+    assert call_decode(L, wsb=100) == B.EKV_ERR_WORKSPACE
+    assert call_decode(L, c=cache(k=None)) == B.EKV_ERR_INVALID_ARG
+    assert call_decode(L, c=cache(kv_dtype=5)) == B.EKV_ERR_INVALID_ARG
+
+
+def test_append_validation(L):
+    f = L.ekv_append_kv
+    assert f(ctypes.byref(cache()), ctypes.byref(seqs()), FAKE, FAKE, -1, FAKE, 1 << 20, None) == B.EKV_ERR_INVALID_ARG
+    assert f(ctypes.byref(cache()), ctypes.byref(seqs()), None, FAKE, 4, FAKE, 1 << 20, None) == B.EKV_ERR_INVALID_ARG
+    assert f(ctypes.byref(cache()), ctypes.byref(seqs()), FAKE, FAKE, 4, None, 1 << 20, None) == B.EKV_ERR_WORKSPACE
+    assert f(ctypes.byref(cache()), ctypes.byref(seqs()), FAKE, FAKE, 10 ** 6, FAKE, 1 << 20, None) == B.EKV_ERR_INVALID_ARG
+    # n_new == 0 is a valid no-op that launches nothing
+    assert f(ctypes.byref(cache()), ctypes.byref(seqs()), None, None, 0, FAKE, 1 << 20, None) == B.EKV_OK
+
+
+def test_misc(L):
+    assert ekv.status_string(B.EKV_ERR_CAPACITY) == "selection capacity too small"
+    assert L.ekv_workspace_init(None, 0, None) == B.EKV_ERR_WORKSPACE
+    assert L.ekv_workspace_init(FAKE, 17, None) == B.EKV_ERR_WORKSPACE
+    flags = ctypes.c_int32(0)
+    assert L.ekv_read_device_status(None, 0, ctypes.byref(flags)) == B.EKV_ERR_WORKSPACE

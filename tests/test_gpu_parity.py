@@ -1,0 +1,229 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle, on
+seeded inputs of the five decode workloads (reduced sizes that still span
+several tiles and a ragged last page), plus metadata maintenance, edge cases
+and run-to-run determinism."""
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_common import SUPPORT_CAP, check_step, run_step
+from oracle import entmax, metadata
+from parity import kv_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _session(spec):
+    from workloads.upload import build_session
+    print(f"[case] {spec.name} B={spec.batch} Hq={spec.n_q_heads} Hkv={spec.n_kv_heads} d={spec.head_dim} "
+          f"P={spec.page_size} ctx={spec.context or (spec.ctx_lo, spec.ctx_hi)}", flush=True)
+    return build_session(spec)
+
+
+def all_units(spec):
+    return [(b, g) for b in range(spec.batch) for g in range(spec.n_kv_heads)]
+
+
+# ---------------------------------------------------------------- append ---
+@pytest.mark.parametrize("kv", ["bf16", "f32"])
+def test_append_bulk_equals_incremental_and_oracle(kv):
+    from sparse_long_context_append_amd.runtime import DecodeSession
+    import sparse_long_context_append_amd as ekv
+    spec = W.make_spec("c2", context=300, n_q_heads=8, n_kv_heads=2, n_needles=4, kv_dtype=kv)
+    table, nphys = W.page_table(spec)
+    dt = ekv.EKV_BF16 if kv == "bf16" else ekv.EKV_F32
+    mk = lambda: DecodeSession(batch=1, n_kv_heads=2, n_q_heads=8, head_dim=128, page_size=16, kv_dtype=dt,
+                               n_phys_pages=nphys, page_table=table)
+    ks = np.stack([W.keys(spec, 0, g) for g in range(2)], axis=1)[None]  # [1][L][Hkv][d]
+    vs = np.stack([W.values(spec, 0, g) for g in range(2)], axis=1)[None]
+    view = (lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)) if kv == "bf16" \
+        else (lambda a: torch.from_numpy(a).cuda())
+    bulk, inc, chunk = mk(), mk(), mk()
+    bulk.append(view(ks), view(vs))
+    for t in range(300):
+        inc.append(view(np.ascontiguousarray(ks[:, t:t + 1])), view(np.ascontiguousarray(vs[:, t:t + 1])))
+    for a, b in [(0, 7), (7, 107), (107, 300)]:
+        chunk.append(view(np.ascontiguousarray(ks[:, a:b])), view(np.ascontiguousarray(vs[:, a:b])))
+    torch.cuda.synchronize()
+    for other in (inc, chunk):
+        assert torch.equal(bulk.k, other.k) and torch.equal(bulk.v, other.v)
+        assert torch.equal(bulk.k_box, other.k_box)
+        assert torch.equal(bulk.k_moments, other.k_moments)  # bit-identical Welford order
+    box = bulk.k_box.float().cpu().numpy()
+    mom = bulk.k_moments.cpu().numpy()
+    for g in range(2):
+        kf = kv_f64(W.keys(spec, 0, g), kv)
+        md = metadata.page_metadata(kf, 300, 16)
+        for p in range(md["count"].size):
+            phys = table[0, p]
+            np.testing.assert_array_equal(box[phys, g, 0], md["kmin"][p])
+            np.testing.assert_array_equal(box[phys, g, 1], md["kmax"][p])
+            np.testing.assert_allclose(mom[phys, g, 0], md["mean"][p], atol=2e-6)
+            np.testing.assert_allclose(mom[phys, g, 1] / md["count"][p], md["var"][p], atol=2e-5)
+    assert bulk.device_status() == 0
+
+
+# ------------------------------------------------------------ workloads ---
+def test_c1_full_sparse_and_dense():
+    spec = W.make_spec("c1")
+    sess, _ = _session(spec)
+    q = W.queries(spec)
+    res = run_step(sess, spec, q, sparse=True)
+    check_step(spec, res, q, all_units(spec))
+    res = run_step(sess, spec, q, sparse=False)
+    check_step(spec, res, q, all_units(spec), sparse=False)
+    assert sess.device_status() == 0
+
+
+@pytest.mark.parametrize("ctx,P,topk", [(4099, 16, 64), (2500, 64, 7)])
+def test_c2_reduced(ctx, P, topk):
+    spec = W.make_spec("c2", context=ctx, page_size=P, top_k=topk, n_q_heads=8, n_kv_heads=2, n_needles=16)
+    sess, _ = _session(spec)
+    q = W.queries(spec)
+    check_step(spec, run_step(sess, spec, q), q, all_units(spec))
+    check_step(spec, run_step(sess, spec, q, sparse=False), q, all_units(spec), sparse=False)
+
+
+def test_c2_full():
+    spec = W.make_spec("c2")
+    sess, _ = _session(spec)
+    q = W.queries(spec)
+    cache = {}
+    check_step(spec, run_step(sess, spec, q), q, all_units(spec), kv_cache=cache)
+    check_step(spec, run_step(sess, spec, q, sparse=False), q, [(0, 0), (0, 5)], sparse=False, kv_cache=cache)
+
+
+def test_c3_reduced_gauss_alpha2():
+    spec = W.make_spec("c3", batch=2, context=8192 + 40, n_q_heads=8, n_kv_heads=2)
+    sess, _ = _session(spec)
+    q = W.queries(spec)
+    cache = {}
+    check_step(spec, run_step(sess, spec, q), q, all_units(spec), kv_cache=cache)
+    check_step(spec, run_step(sess, spec, q, sparse=False), q, all_units(spec), sparse=False, kv_cache=cache)
+
+
+def test_c4_reduced():
+    spec = W.make_spec("c4", context=65536 + 33, n_q_heads=8, n_kv_heads=2, n_needles=64, top_k=21)
+    sess, _ = _session(spec)
+    q = W.queries(spec)
+    cache = {}
+    check_step(spec, run_step(sess, spec, q), q, all_units(spec), kv_cache=cache)
+    check_step(spec, run_step(sess, spec, q, sparse=False), q, [(0, 1)], sparse=False, kv_cache=cache)
+
+
+def test_c5_reduced_with_appends():
+    """Permuted physical pages, mixed lengths, one appended token per sequence
+    per step, metadata maintained in the loop."""
+    from workloads.upload import step_tokens
+    spec = W.make_spec("c5", batch=4, ctx_lo=900, ctx_hi=3000, steps=5, n_q_heads=8, n_kv_heads=2)
+    sess, appended = _session(spec)
+    cache = {}
+    for s in range(spec.steps):
+        k1, v1 = step_tokens(spec, appended, s)
+        sess.append(k1, v1)
+        q = W.queries(spec, s)
+        check_step(spec, run_step(sess, spec, q), q, all_units(spec), kv_cache=cache)
+    assert sess.device_status() == 0
+
+
+# ----------------------------------------------------------- edge cases ---
+def test_topk_covering_every_page_equals_dense():
+    spec = W.make_spec("c2", context=1000, n_q_heads=8, n_kv_heads=2, n_needles=8, top_k=10 ** 6)
+    sess, _ = _session(spec)
+    q = W.queries(spec)
+    rs = run_step(sess, spec, q)
+    rd = run_step(sess, spec, q, sparse=False)
+    assert np.all(rs["cnt"] == 63)
+    np.testing.assert_array_equal(rs["out"], rd["out"])  # same token set, same order
+    check_step(spec, rs, q, all_units(spec))
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0])
+def test_all_keys_equal_large_support(alpha):
+    """Every key identical: every page ties (lowest ids win) and every token
+    is in the support, which overflows the on-chip candidate list."""
+    from sparse_long_context_append_amd.runtime import DecodeSession
+    import sparse_long_context_append_amd as ekv
+    L, P, d = 5000, 16, 64
+    npg = -(-L // P)
+    table = np.arange(npg, dtype=np.int32)[None]
+    sess = DecodeSession(batch=1, n_kv_heads=1, n_q_heads=2, head_dim=d, page_size=P, kv_dtype=ekv.EKV_F32,
+                         n_phys_pages=npg, page_table=table, cap=npg)
+    rng = np.random.default_rng(7)
+    k = np.repeat(rng.standard_normal((1, d)).astype(np.float32), L, axis=0)
+    v = rng.standard_normal((L, d)).astype(np.float32)
+    sess.append(torch.from_numpy(k[None, :, None]).cuda(), torch.from_numpy(v[None, :, None]).cuda())
+    q = torch.from_numpy(rng.standard_normal((1, 2, d)).astype(np.float32)).cuda()
+    sess.select(q, policy=ekv.EKV_SELECT_BBOX_TOPK, alpha=alpha, scale=0.125, top_k=5)
+    torch.cuda.synchronize()
+    assert sess.sel_count.item() == 5
+    assert sess.sel[0, 0, :5].tolist() == [0, 1, 2, 3, 4]
+    sess.decode(q, alpha=alpha, scale=0.125, sparse=False)
+    torch.cuda.synchronize()
+    assert np.all(sess.support_count.cpu().numpy() == L)
+    np.testing.assert_allclose(sess.psum.cpu().numpy(), 1.0, atol=1e-5)
+    np.testing.assert_allclose(sess.out.cpu().numpy()[0], np.tile(v.mean(axis=0), (2, 1)), atol=2e-3)
+
+
+def test_empty_and_single_token_sequences():
+    from sparse_long_context_append_amd.runtime import DecodeSession
+    import sparse_long_context_append_amd as ekv
+    P, d = 16, 128
+    table = np.array([[0, 1], [2, 3], [4, 5]], dtype=np.int32)
+    sess = DecodeSession(batch=3, n_kv_heads=1, n_q_heads=4, head_dim=d, page_size=P, kv_dtype=ekv.EKV_BF16,
+                         n_phys_pages=6, page_table=table, cap=2)
+    rng = np.random.default_rng(8)
+    k = torch.from_numpy(rng.standard_normal((1, 1, 1, d)).astype(np.float32)).cuda().to(torch.bfloat16)
+    v = torch.from_numpy(rng.standard_normal((1, 1, 1, d)).astype(np.float32)).cuda().to(torch.bfloat16)
+    sess.append(k, v, seq=1)  # sequence 0 and 2 stay empty
+    q = torch.from_numpy(rng.standard_normal((3, 4, d)).astype(np.float32)).cuda()
+    for pol in (ekv.EKV_SELECT_BBOX_TOPK, ekv.EKV_SELECT_GAUSS):
+        sess.select(q, policy=pol, alpha=1.5, scale=d ** -0.5, top_k=2, delta=0.5)
+        sess.decode(q, alpha=1.5, scale=d ** -0.5)
+        torch.cuda.synchronize()
+        assert sess.sel_count.cpu().tolist() == [[0], [1], [0]]
+        out = sess.out.cpu().numpy()
+        assert np.all(out[0] == 0) and np.all(out[2] == 0)
+        np.testing.assert_allclose(out[1], np.tile(v.float().cpu().numpy()[0, 0, 0], (4, 1)), atol=1e-6)
+        assert sess.support_count.cpu().tolist() == [[0] * 4, [1] * 4, [0] * 4]
+    assert sess.device_status() == 0
+
+
+def test_bad_page_table_entry_is_flagged_not_fatal():
+    from sparse_long_context_append_amd.runtime import DecodeSession
+    import sparse_long_context_append_amd as ekv
+    P, d = 16, 64
+    table = np.array([[0, 1, 2, 3]], dtype=np.int32)
+    sess = DecodeSession(batch=1, n_kv_heads=1, n_q_heads=1, head_dim=d, page_size=P, kv_dtype=ekv.EKV_F32,
+                         n_phys_pages=4, page_table=table, cap=4)
+    rng = np.random.default_rng(9)
+    sess.append(torch.from_numpy(rng.standard_normal((1, 64, 1, d)).astype(np.float32)).cuda(),
+                torch.from_numpy(rng.standard_normal((1, 64, 1, d)).astype(np.float32)).cuda())
+    q = torch.from_numpy(rng.standard_normal((1, 1, d)).astype(np.float32)).cuda()
+    assert sess.device_status() == 0
+    sess.page_table[0, 2] = 99  # outside the physical pool
+    sess.select(q, policy=ekv.EKV_SELECT_BBOX_TOPK, alpha=1.5, scale=0.125, top_k=4)
+    sess.decode(q, alpha=1.5, scale=0.125)
+    torch.cuda.synchronize()
+    assert sess.device_status() & 0x1  # EKV_DEV_BAD_PAGE
+    assert sess.device_status() == 0  # reading clears it
+    assert np.isfinite(sess.out.cpu().numpy()).all()
+    assert abs(sess.psum.item() - 1.0) <= 1e-5
+
+
+def test_run_twice_bit_identical():
+    spec = W.make_spec("c3", batch=2, context=4096 + 8, n_q_heads=8, n_kv_heads=2)
+    sess, _ = _session(spec)
+    q = W.queries(spec)
+    a = run_step(sess, spec, q)
+    b = run_step(sess, spec, q)
+    for key in ("sel", "cnt", "out", "tau", "psum", "count", "supp", "tau_hat"):
+        np.testing.assert_array_equal(a[key], b[key])
