@@ -1,0 +1,376 @@
+#!/usr/bin/env python
+"""Decode-step benchmark of the EntmaxKV sparse alpha-entmax path on one GPU.
+
+One step = select_pages + entmax_decode (sparse) over one batch of the
+workload; the cache is built beforehand with append_kv.  Before every timed
+step the L2 caches and the Infinity Cache are evicted by streaming a read
+over 1 GiB, and each step is bracketed by HIP events on the stream the
+kernels run on.
+
+Prints ONE JSON line.  `value` is the effective HBM bandwidth of the sparse
+step on the million-token workload: algorithmic bytes (page metadata, the
+page table, the selected K pages, the V rows of the support, q and the
+output) per step over the median step time.  The 128K Gaussian workload, the
+dense full-cache entmax decode, HIP-graph replay and the CPU oracle are
+reported beside it.
+"""
+from __future__ import annotations
+
+import os
+import sys
+
+_NCPU = len(os.sched_getaffinity(0))
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_v, str(_NCPU))
+
+import argparse  # noqa: E402
+import json  # noqa: E402
+import statistics  # noqa: E402
+import time  # noqa: E402
+
+import numpy as np  # noqa: E402
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "sparse entmax decode µs/step and effective HBM GB/s at 128K and 1M context"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- bytes ----
+def step_bytes(spec, sel, sel_count, lens, support_union, sparse=True):
+    """Algorithmic bytes of one step (what the method must move)."""
+    P, d, s = spec.page_size, spec.head_dim, spec.elem_bytes
+    G = spec.group
+    meta_rec = 2 * d * s if spec.policy == "bbox" else 2 * d * 4
+    total = 0
+    for b in range(spec.batch):
+        L = int(lens[b])
+        n_b = -(-L // P)
+        for g in range(spec.n_kv_heads):
+            if sparse:
+                total += n_b * meta_rec                     # page metadata
+                total += n_b * 4 / spec.n_kv_heads           # page-table share
+                pages = sel[b, g, : int(sel_count[b, g])].astype(np.int64)
+                valid = np.minimum(P, L - pages * P)
+                total += int(valid.sum()) * d * s            # valid K rows of the selected pages
+            else:
+                total += L * d * s                           # every K row
+                total += n_b * 4 / spec.n_kv_heads
+            total += int(support_union[b][g]) * d * s        # V rows of the support union
+            total += G * d * 4 * 2                           # q and output
+    return float(total)
+
+
+def support_union_sizes(spec, supp, count):
+    """Per (b, g): number of distinct tokens in the group's supports."""
+    G = spec.group
+    out = []
+    for b in range(spec.batch):
+        row = []
+        for g in range(spec.n_kv_heads):
+            toks = set()
+            exact = True
+            for h in range(g * G, (g + 1) * G):
+                c = int(count[b, h])
+                if c > supp.shape[2]:
+                    exact = False
+                    c = supp.shape[2]
+                toks.update(supp[b, h, :c].tolist())
+            row.append(len(toks) if exact else sum(int(count[b, h]) for h in range(g * G, (g + 1) * G)))
+        out.append(row)
+    return out
+
+
+# ---------------------------------------------------------------- timing ---
+class Timer:
+    """Per-step HIP-event timing on torch's current stream.  Before every
+    step the L2 caches and the 256 MB Infinity Cache are evicted by streaming
+    a read over a 1 GiB buffer (written once here).  A read leaves only clean
+    lines behind; a write-based flush would leave hundreds of MB of dirty
+    lines whose write-back the timed step would then pay for."""
+
+    def __init__(self, torch, flush_bytes=1 << 30):
+        self.torch = torch
+        self.flush = torch.ones(flush_bytes // 4, dtype=torch.float32, device="cuda")
+        self.sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def evict(self):
+        self.torch.sum(self.flush, dim=0, out=self.sink)
+
+    def run(self, fn, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.evict()
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e0, e1 in ev:
+            self.evict()
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+        return ms, wall
+
+
+def pct(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
+
+
+def measure(spec, steps, warmup, torch, timer, do_dense=True, do_graph=True):
+    import sparse_long_context_append_amd as ekv
+    from workloads.upload import build_session, queries_device
+    t0 = time.perf_counter()
+    sess, _ = build_session(spec)
+    log(f"{spec.name}: cache built in {time.perf_counter() - t0:.1f}s")
+    q = queries_device(spec)
+    pol = ekv.EKV_SELECT_BBOX_TOPK if spec.policy == "bbox" else ekv.EKV_SELECT_GAUSS
+    SC = 4096
+    supp = torch.full((spec.batch, spec.n_q_heads, SC), -1, dtype=torch.int32, device="cuda")
+
+    def sparse_step():
+        sess.select(q, policy=pol, alpha=spec.alpha, scale=spec.scale, top_k=spec.top_k, delta=spec.delta)
+        sess.decode(q, alpha=spec.alpha, scale=spec.scale, sparse=True)
+
+    def dense_step():
+        sess.decode(q, alpha=spec.alpha, scale=spec.scale, sparse=False)
+
+    scores = torch.empty((spec.batch, spec.n_kv_heads if pol == 0 else spec.n_q_heads, sess.max_pages)
+                         + (() if pol == 0 else (4,)), dtype=torch.float32, device="cuda")
+
+    def score_only():
+        ekv.score_pages(sess.cache, sess.seqs, q, spec.n_q_heads, policy=pol, alpha=spec.alpha, scale=spec.scale,
+                        scores=scores, ws=sess.ws)
+
+    res = {}
+    ms, wall = timer.run(sparse_step, steps, warmup)
+    res["sparse_ms"] = ms
+    res["sparse_wall_s"] = wall
+    # diagnostics of the step just timed (same inputs every step)
+    sess.decode(q, alpha=spec.alpha, scale=spec.scale, sparse=True, support_idx=supp, support_cap=SC)
+    torch.cuda.synchronize()
+    cnt = sess.sel_count.cpu().numpy()
+    sel = sess.sel.cpu().numpy()
+    lens = sess.seq_lens.cpu().numpy()
+    sc = sess.support_count.cpu().numpy()
+    union = support_union_sizes(spec, supp.cpu().numpy(), sc)
+    res["bytes"] = step_bytes(spec, sel, cnt, lens, union, sparse=True)
+    res["pages_selected"] = int(cnt.sum())
+    res["pages_total"] = int(sum(-(-int(L) // spec.page_size) for L in lens) * spec.n_kv_heads)
+    res["support_mean"] = float(sc.mean())
+    res["psum_err"] = float(np.abs(sess.psum.cpu().numpy() - 1.0).max())
+    sparse_out = sess.out.clone()
+    ms_s, _ = timer.run(score_only, steps, warmup)
+    res["score_ms"] = ms_s
+    npages = res["pages_total"]
+    rec = 2 * spec.head_dim * (spec.elem_bytes if pol == 0 else 4)
+    out_b = 4 if pol == 0 else 16 * spec.group  # one fp32 score / G float4 page stats per (page, KV head)
+    res["score_bytes"] = float(npages * (rec + out_b))
+    if do_graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            sparse_step()  # warm on the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            sparse_step()
+        ms_g, _ = timer.run(g.replay, steps, warmup)
+        res["graph_ms"] = ms_g
+        torch.cuda.synchronize()
+        # graph replays must give the eager result
+        assert torch.equal(sess.out, sparse_out), "graph replay differs from eager"
+    if do_dense:
+        ms_d, _ = timer.run(dense_step, max(5, steps // 3), 2)
+        res["dense_ms"] = ms_d
+        sess.decode(q, alpha=spec.alpha, scale=spec.scale, sparse=False, support_idx=supp, support_cap=SC)
+        torch.cuda.synchronize()
+        sc_d = sess.support_count.cpu().numpy()
+        union_d = support_union_sizes(spec, supp.cpu().numpy(), sc_d)
+        res["dense_bytes"] = step_bytes(spec, sel, cnt, lens, union_d, sparse=False)
+        res["dense_kv_bytes"] = float(sum(int(L) for L in lens) * spec.n_kv_heads * spec.head_dim
+                                      * spec.elem_bytes * 2)
+    status = sess.device_status()
+    assert status == 0, f"device status {status:#x}"
+    del sess
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------ CPU oracle ---
+def cpu_baseline(spec, units, reps=3):
+    """Time the oracle's sparse step (scoring from metadata, selection, exact
+    entmax over the kept pages) on `units` (b, g) of the workload; metadata
+    build is excluded.  Returns seconds per unit (median of reps)."""
+    from oracle import decode as odecode
+    from oracle import entmax, metadata, scoring, select
+
+    q = W.queries(spec).astype(np.float64)
+    prepared = []
+    for (b, g) in units:
+        k = entmax.stored_to_f64(W.keys(spec, b, g), spec.kv_dtype)
+        v = entmax.stored_to_f64(W.values(spec, b, g), spec.kv_dtype)
+        L = int(W.seq_lens(spec)[b])
+        md = metadata.page_metadata(k, L, spec.page_size)
+        prepared.append((b, g, k, v, L, md))
+    G = spec.group
+
+    def one_pass():
+        for (b, g, k, v, L, md) in prepared:
+            heads = range(g * G, (g + 1) * G)
+            if spec.policy == "bbox":
+                S = scoring.bbox_page_scores(q[b, heads], md["kmin"], md["kmax"], spec.scale)
+                pages = select.topk_pages(S, spec.top_k)
+            else:
+                eh, th = [], []
+                for h in heads:
+                    mu, sd, e = scoring.gauss_page_stats(q[b, h], md["mean"], md["var"], md["count"],
+                                                         spec.alpha, spec.scale)
+                    eh.append(e)
+                    th.append(select.gauss_tau_hat(mu, sd, md["count"], spec.alpha))
+                pages = select.gauss_keep_pages(np.array(eh), np.array(th), spec.delta)
+            toks = odecode.pages_to_tokens(pages, L, spec.page_size)
+            for h in heads:
+                odecode.decode_head(q[b, h], k, v, toks, spec.alpha, spec.scale)
+
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        one_pass()
+        times.append(time.perf_counter() - t0)
+    return statistics.median(times) / len(units)
+
+
+# -------------------------------------------------------------------- main -
+def summarize(spec, r):
+    med = statistics.median(r["sparse_ms"]) * 1e3  # us
+    out = {
+        "workload": spec.name,
+        "us_per_step": round(med, 2),
+        "us_p10": round(pct(r["sparse_ms"], 0.1) * 1e3, 2),
+        "us_p90": round(pct(r["sparse_ms"], 0.9) * 1e3, 2),
+        "bytes_per_step": int(r["bytes"]),
+        "effective_gbs": round(r["bytes"] / (med * 1e-6) / 1e9, 1),
+        "hbm_fraction": round(r["bytes"] / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "pages_selected": r["pages_selected"],
+        "pages_total": r["pages_total"],
+        "support_mean": round(r["support_mean"], 2),
+        "max_abs_psum_error": r["psum_err"],
+    }
+    if "graph_ms" in r:
+        gm = statistics.median(r["graph_ms"]) * 1e3
+        out["graph_us_per_step"] = round(gm, 2)
+        out["graph_effective_gbs"] = round(r["bytes"] / (gm * 1e-6) / 1e9, 1)
+    if "dense_ms" in r:
+        dm = statistics.median(r["dense_ms"]) * 1e3
+        out["dense_us_per_step"] = round(dm, 2)
+        out["dense_bytes_per_step"] = int(r["dense_bytes"])
+        out["dense_effective_gbs"] = round(r["dense_bytes"] / (dm * 1e-6) / 1e9, 1)
+        out["dense_full_kv_bytes"] = int(r["dense_kv_bytes"])
+        out["speedup_vs_dense"] = round(dm / med, 2)
+    sm = statistics.mean(r["score_ms"]) * 1e3
+    out["score_kernel_us"] = round(sm, 2)
+    out["score_kernel_gbs"] = round(r["score_bytes"] / (sm * 1e-6) / 1e9, 1)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c4", help="workload the headline value is measured on")
+    ap.add_argument("--also", default="c3", help="second workload reported in the same line ('' for none)")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--context", type=int, default=0, help="override the workload's context (scaling sweeps)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the decode path is a single-GPU path and no multi-GPU mode exists",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    timer = Timer(torch)
+    over = {"context": args.context} if args.context else {}
+    spec = W.make_spec(args.workload, **over)
+    log(f"device {torch.cuda.get_device_name(0)}; workload {spec.name}")
+    r = measure(spec, args.steps, args.warmup, torch, timer, not args.no_dense, not args.no_graph)
+    main_sum = summarize(spec, r)
+    extra = None
+    if args.also:
+        spec2 = W.make_spec(args.also)
+        r2 = measure(spec2, args.steps, args.warmup, torch, timer, not args.no_dense, not args.no_graph)
+        extra = summarize(spec2, r2)
+    cpu = None
+    if not args.no_cpu:
+        units = [(0, 0), (0, 1)]
+        per_unit = cpu_baseline(spec, units)
+        n_units = spec.batch * spec.n_kv_heads
+        cpu_us = per_unit * n_units * 1e6
+        cpu = {
+            "value": round(r["bytes"] / (cpu_us * 1e-6) / 1e9, 3),
+            "unit": "GB/s",
+            "us_per_step": round(cpu_us, 1),
+            "cores": int(os.environ.get("OMP_NUM_THREADS", _NCPU)),
+            "kind": "oracle",
+            "sample": (f"float64 numpy oracle sparse step (bbox scoring from prebuilt metadata, top-k, exact "
+                       f"entmax over the kept pages) on {len(units)} of {n_units} (sequence, KV head) units of "
+                       f"{spec.name}, median of 3, scaled to the whole step"),
+        }
+    med_us = main_sum["us_per_step"]
+    sm_us = main_sum["score_kernel_us"]
+    line = {
+        "metric": METRIC,
+        "value": main_sum["effective_gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(med_us / 1e3, 5),
+        "wall_ms_per_step_incl_flush": round(r["sparse_wall_s"] / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if spec.kv_dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{spec.name}: B={spec.batch}, Hq/Hkv={spec.n_q_heads}/{spec.n_kv_heads}, "
+                               f"d={spec.head_dim}, context={spec.context}, page={spec.page_size}, "
+                               f"{spec.policy} select, alpha={spec.alpha}",
+                   "global_batch": spec.batch, "seq_len": spec.context, "parallelism": "none"},
+        "us_per_step": med_us,
+        "hbm_fraction": main_sum["hbm_fraction"],
+        "detail": main_sum,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "score_bbox" if spec.policy == "bbox" else "score_gauss",
+            "achieved": main_sum["score_kernel_gbs"],
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(main_sum["score_kernel_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "launch_us": sm_us,
+        },
+        "cpu_baseline": cpu,
+    }
+    if extra is not None:
+        line["also"] = extra
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

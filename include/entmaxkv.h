@@ -165,8 +165,8 @@ ekv_status ekv_append_kv(const ekv_cache* cache, const ekv_seqs* seqs, const voi
 /*
  * Score pages and select candidates for every (sequence, KV head); the
  * selection is shared by the KV head's query-head group.
- *   q          [batch][n_q_heads][head_dim] float32; n_q_heads a multiple
- *              of n_kv_heads, group size at most 16
+ *   q          [batch][n_q_heads][head_dim] float32, 16-byte aligned;
+ *              n_q_heads = G * n_kv_heads with G in {1, 2, 4, 8}
  *   sel        [batch][n_kv_heads][cap] int32: ascending logical page ids
  *   sel_count  [batch][n_kv_heads] int32: number of valid entries in sel
  *   tau_hat    optional [batch][n_q_heads] float32 (EKV_SELECT_GAUSS only):
@@ -175,7 +175,8 @@ ekv_status ekv_append_kv(const ekv_cache* cache, const ekv_seqs* seqs, const voi
  *   scale * sum_i max(q_i k_min_i, q_i k_max_i), the tightest upper bound
  *   the box gives on q.k (summary sec. 2.A); keeps the min(top_k, n_b)
  *   highest, lower page id first on equal scores.  Needs cap >= top_k
- *   (else EKV_ERR_CAPACITY).
+ *   (else EKV_ERR_CAPACITY) and max_pages <= 65535 (else
+ *   EKV_ERR_UNSUPPORTED).
  * GAUSS: per query head, page scores are modelled as Gaussian with mean
  *   (alpha-1) scale q.mu and variance ((alpha-1) scale)^2 sum_i q_i^2 var_i;
  *   tau_hat solves sum_p n_p E[(Y_p - t)_+^(1/(alpha-1))] = 1; a page is kept

@@ -73,6 +73,13 @@ def lib() -> ctypes.CDLL:
     """The loaded library (loaded on first use; raises if it was not built)."""
     global _LIB
     if _LIB is None:
+        # Load PyTorch's HIP runtime first when PyTorch is present, so the
+        # library binds to the same runtime copy (and device context) as the
+        # tensors it is handed.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         if not os.path.exists(lib_path):
             raise RuntimeError(f"{lib_path} is missing: build it with python -m sparse_long_context_append_amd._build")
         L = ctypes.CDLL(lib_path)

@@ -142,6 +142,7 @@ static ekv_status prepare_select(const ekv_cache* cache, const ekv_seqs* seqs, c
   if (p->policy == EKV_SELECT_BBOX_TOPK) {
     if (!cache->k_box) return fail(EKV_ERR_INVALID_ARG, "bounding-box selection needs cache->k_box");
     if (p->top_k < 1) return fail(EKV_ERR_INVALID_ARG, "top_k must be >= 1");
+    if (seqs->max_pages > 65535) return fail(EKV_ERR_UNSUPPORTED, "top-k selection supports up to 65535 pages per sequence");
   } else if (p->policy == EKV_SELECT_GAUSS) {
     if (!cache->k_moments) return fail(EKV_ERR_INVALID_ARG, "Gaussian selection needs cache->k_moments");
     if (p->alpha != 1.5f && p->alpha != 2.0f)
@@ -160,7 +161,10 @@ static ekv_status prepare_select(const ekv_cache* cache, const ekv_seqs* seqs, c
   a->k_box = cache->k_box; a->k_moments = cache->k_moments; a->q = q;
   a->policy = p->policy; a->top_k = p->top_k; a->alpha = p->alpha; a->scale = p->scale; a->delta = p->delta;
   a->scores = at<float>(workspace, L->scores);
-  a->stats = at<float4>(workspace, L->stats);
+  a->score_stride = ekv::score_stride(seqs->max_pages);
+  a->musd = at<float2>(workspace, L->musd);
+  a->ehat = at<float>(workspace, L->ehat);
+  a->stats_out = nullptr;
   a->tau_hat = at<double>(workspace, L->tau_hat);
   a->status = at<uint32_t>(workspace, L->status);
   return EKV_OK;
@@ -201,9 +205,10 @@ ekv_status ekv_score_pages(const ekv_cache* cache, const ekv_seqs* seqs, const f
   hipStream_t s = (hipStream_t)stream;
   if (params->policy == EKV_SELECT_BBOX_TOPK) {
     a.scores = scores;
+    a.score_stride = seqs->max_pages;
     return hip_status(ekv::launch_score_bbox(a, s), "score_bbox launch");
   }
-  a.stats = reinterpret_cast<float4*>(scores);
+  a.stats_out = reinterpret_cast<float4*>(scores);
   return hip_status(ekv::launch_score_gauss(a, s), "score_gauss launch");
 }
 
@@ -225,39 +230,27 @@ ekv_status ekv_entmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const
   ekv::Layout L;
   if ((st = check_ws(cache, seqs, n_q_heads, workspace, ws_bytes, &L)) != EKV_OK) return st;
   const int P = cache->page_size;
-  // work item: about 64 tokens (sparse) or 256 tokens (full cache) of one KV head
-  const int target = sel ? 64 : 256;
-  int ppi = P >= target ? 1 : target / P;
-  if (ppi > 256) ppi = 256;
-  const int n_units = seqs->batch * cache->n_kv_heads;
-  if (ekv::gather_lds_bytes(n_units, G, ppi, P) > ekv::kMaxGatherLds)
-    return fail(EKV_ERR_UNSUPPORTED, "decode work item does not fit in LDS");
   ekv::DecodeArgs a{};
   a.batch = seqs->batch; a.n_kv_heads = cache->n_kv_heads; a.n_q_heads = n_q_heads; a.group = G;
   a.page_size = P; a.head_dim = cache->head_dim; a.kv_dtype = cache->kv_dtype;
   a.max_pages = seqs->max_pages; a.n_phys = cache->n_phys_pages;
   a.page_table = seqs->page_table; a.seq_lens = seqs->seq_lens;
   a.k = cache->k; a.v = cache->v; a.q = q; a.alpha = alpha; a.scale = scale;
-  a.sel = sel; a.sel_count = sel_count; a.cap = sel ? cap : 0; a.ppi = ppi;
+  a.sel = sel; a.sel_count = sel_count; a.cap = sel ? cap : 0;
   a.out = out; a.tau = tau; a.support_count = support_count; a.psum = psum;
   a.support_idx = support_idx; a.support_cap = support_cap;
-  a.max_key = at<uint32_t>(workspace, L.max_key);
+  a.max_items = (int)L.max_items;
   a.item_cnt = at<int32_t>(workspace, L.item_cnt);
   a.item_max = at<float>(workspace, L.item_max);
   a.cand_x = at<float>(workspace, L.cand_x);
   a.cand_t = at<int32_t>(workspace, L.cand_t);
+  a.cand_r = at<int32_t>(workspace, L.cand_r);
   a.ovf_x = at<float>(workspace, L.ovf_x);
   a.ovf_t = at<int32_t>(workspace, L.ovf_t);
+  a.ovf_r = at<int32_t>(workspace, L.ovf_r);
   a.status = at<uint32_t>(workspace, L.status);
-  // persistent grid: enough blocks to cover every item of the largest possible
-  // selection, capped at 16 blocks per compute unit
-  const long long per_unit = sel ? ((long long)(cap < seqs->max_pages ? cap : seqs->max_pages) + ppi - 1) / ppi
-                                 : ((long long)seqs->max_pages + ppi - 1) / ppi;
-  long long items = per_unit * n_units;
-  const long long cap_blocks = 16LL * device_cus();
-  if (items > cap_blocks) items = cap_blocks;
-  if (items < 1) items = 1;
-  return hip_status(ekv::launch_decode(a, (int)items, (hipStream_t)stream), "entmax_decode launch");
+  // about 16 gather blocks per compute unit
+  return hip_status(ekv::launch_decode(a, 16 * device_cus(), (hipStream_t)stream), "entmax_decode launch");
 }
 
 ekv_status ekv_read_device_status(void* workspace, size_t ws_bytes, int32_t* host_flags) {

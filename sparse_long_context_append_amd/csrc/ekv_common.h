@@ -12,45 +12,129 @@ namespace ekv {
 constexpr int kWave = 64;
 
 // ---------------------------------------------------------------------------
-// Workspace layout.  The control words come first and are zero when idle
-// (ekv_workspace_init zeroes the whole buffer; every kernel that changes a
-// control word restores it before the step ends).
+// Workspace layout.  The status word comes first; ekv_workspace_init zeroes
+// the whole buffer.  Every other region is fully rewritten by the step that
+// reads it, so nothing carries over between calls.
 // ---------------------------------------------------------------------------
+constexpr int kItemTokens = 64;  // tokens of one decode work item
+
 struct Layout {
   size_t status;    // u32 device status bits
-  size_t max_key;   // u32 [B*Hq] running max of the decode scores (ordered key, 0 = empty)
-  size_t scores;    // f32 [B*Hkv*max_pages] bounding-box page scores
-  size_t stats;     // float4 [B*Hq*max_pages] Gaussian (mean_Y, sd_Y, e_hat, n_p)
+  size_t scores;    // f32 [B*Hkv][score_stride] bounding-box page scores
+  size_t musd;      // float2 [B*Hq*max_pages] Gaussian page score (mean_Y, sd_Y)
+  size_t ehat;      // f32 [B*Hq*max_pages] estimated page maximum
   size_t tau_hat;   // f64 [B*Hq]
-  size_t item_cnt;  // i32 [B*Hq*max_pages] candidates kept by each decode work item
-  size_t item_max;  // f32 [B*Hq*max_pages] per item maximum score
-  size_t cand_x;    // f32 [B*Hq*max_pages*P] candidate scores, one region per item
-  size_t cand_t;    // i32 [B*Hq*max_pages*P] candidate logical token ids
-  size_t ovf_x;     // f32 [B*Hq*max_pages*P] compacted candidates (large sets)
-  size_t ovf_t;     // i32 [B*Hq*max_pages*P]
+  size_t item_cnt;  // i32 [B*Hq*max_items] candidates kept by each decode work item
+  size_t item_max;  // f32 [B*Hq*max_items] per item maximum score
+  size_t cand_x;    // f32 [B*Hq*max_items*64] candidate scores, one region per item
+  size_t cand_t;    // i32 [...] candidate logical token ids
+  size_t cand_r;    // i32 [...] candidate physical rows (page * P + slot)
+  size_t ovf_x;     // f32 [B*Hq*max_items*64] compacted candidates (large sets)
+  size_t ovf_t;     // i32 [...]
+  size_t ovf_r;     // i32 [...]
   size_t total;
+  size_t max_items; // per (sequence, query head)
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+// row stride of the internal page-score buffer: 16-byte aligned rows
+inline int score_stride(int max_pages) { return (max_pages + 3) & ~3; }
 
 inline Layout make_layout(int B, int Hkv, int Hq, int max_pages, int P) {
   Layout L{};
   size_t off = 0;
   const size_t bh = size_t(B) * Hq;
-  const size_t tok = size_t(max_pages) * P;
+  L.max_items = (size_t(max_pages) * P + kItemTokens - 1) / kItemTokens;
+  const size_t tok = L.max_items * kItemTokens;
   L.status = off;   off = align256(off + 4);
-  L.max_key = off;  off = align256(off + 4 * bh);
-  L.scores = off;   off = align256(off + 4 * size_t(B) * Hkv * max_pages);
-  L.stats = off;    off = align256(off + 16 * bh * max_pages);
+  L.scores = off;   off = align256(off + 4 * size_t(B) * Hkv * score_stride(max_pages));
+  L.musd = off;     off = align256(off + 8 * bh * max_pages);
+  L.ehat = off;     off = align256(off + 4 * bh * max_pages);
   L.tau_hat = off;  off = align256(off + 8 * bh);
-  L.item_cnt = off; off = align256(off + 4 * bh * max_pages);
-  L.item_max = off; off = align256(off + 4 * bh * max_pages);
+  L.item_cnt = off; off = align256(off + 4 * bh * L.max_items);
+  L.item_max = off; off = align256(off + 4 * bh * L.max_items);
   L.cand_x = off;   off = align256(off + 4 * bh * tok);
   L.cand_t = off;   off = align256(off + 4 * bh * tok);
+  L.cand_r = off;   off = align256(off + 4 * bh * tok);
   L.ovf_x = off;    off = align256(off + 4 * bh * tok);
   L.ovf_t = off;    off = align256(off + 4 * bh * tok);
+  L.ovf_r = off;    off = align256(off + 4 * bh * tok);
   L.total = off;
   return L;
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core helpers (gfx950 v_mfma_f32_16x16x32_bf16).  Lane l holds
+// A[row l%16][k 8(l/16)..+8), B[k 8(l/16)..+8][col l%16] and returns
+// D[rows 4(l/16)..+4][col l%16].
+// ---------------------------------------------------------------------------
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma_bf16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Split c into three bf16 limbs with c = l0 + l1 + l2 up to 2^-24 |c|: each
+// limb is the bf16 rounding of what the previous ones left, and the fp32
+// subtractions are exact.  limb(i) returns the bits of limb i.
+__device__ __forceinline__ void split3_bf16(float c, uint32_t* l0, uint32_t* l1, uint32_t* l2) {
+  *l0 = bf16_rne_bits(c);
+  const float r1 = c - __uint_as_float(*l0 << 16);
+  *l1 = bf16_rne_bits(r1);
+  const float r2 = r1 - __uint_as_float(*l1 << 16);
+  *l2 = bf16_rne_bits(r2);
+}
+
+// A operand of a 16-row limb product: chunk (kb, ln) holds, for row ln%16 =
+// 4h + l and k = 32 kb + 8 (ln/16) + j (j < 8), limb l of coefficient
+// coef(h, k); rows with h >= G or l = 3 are zero.  Thread t owns chunks
+// t, t + blockDim, ...; limb_fetch reads the raw values its chunks need
+// (issue it before other loads so it is not queued behind them) and
+// limb_build writes each chunk with one conflict-free 16-byte LDS store.
+template <int KB> struct LimbChunks {
+  static constexpr int kPerThread = (KB * kWave + 255) / 256;  // for 256-thread blocks
+  float v[kPerThread][8];
+};
+
+template <int KB, int G, typename Fetch8>
+__device__ __forceinline__ void limb_fetch(LimbChunks<KB>& lc, Fetch8 fetch8) {
+#pragma unroll
+  for (int i = 0; i < LimbChunks<KB>::kPerThread; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    const int kb = c >> 6, ln = c & 63, row = ln & 15, kg = ln >> 4, h = row >> 2;
+    if (c < KB * kWave && h < G && (row & 3) < 3) fetch8(h, 32 * kb + 8 * kg, lc.v[i]);
+  }
+}
+
+template <int KB, int G, typename Coef>
+__device__ __forceinline__ void limb_build(u32x4_t (*s_a)[kWave], const LimbChunks<KB>& lc, Coef coef) {
+#pragma unroll
+  for (int i = 0; i < LimbChunks<KB>::kPerThread; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c >= KB * kWave) break;
+    const int kb = c >> 6, ln = c & 63, row = ln & 15, kg = ln >> 4;
+    const int h = row >> 2, limb = row & 3;
+    uint32_t wv[4] = {0u, 0u, 0u, 0u};
+    if (h < G && limb < 3) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t l0, l1, l2;
+        split3_bf16(coef(32 * kb + 8 * kg + j, lc.v[i][j]), &l0, &l1, &l2);
+        const uint32_t bits = limb == 0 ? l0 : (limb == 1 ? l1 : l2);
+        wv[j >> 1] |= (bits & 0xffffu) << (16 * (j & 1));
+      }
+    }
+    s_a[kb][ln] = u32x4_t{wv[0], wv[1], wv[2], wv[3]};
+  }
 }
 
 // ---------------------------------------------------------------------------

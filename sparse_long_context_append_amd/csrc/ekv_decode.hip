@@ -2,25 +2,28 @@
 // sec. 2.C: load only the selected pages' keys and values and compute the
 // alpha-entmax weights over that reduced set).
 //
-// gather_score  persistent grid over work items; an item is up to `ppi`
-//               consecutive entries of a (sequence, KV head)'s page list.
-//               Each K row is read once with 16-byte lane loads and scored
-//               against every query head of the group (x = (alpha-1) scale
-//               q.k, float32).  The item keeps only candidates that can be
-//               in the support: x > m - 1, where m is a lower bound on the
-//               head's maximum (its own maximum, or the running maximum
-//               published with an integer atomic) - the threshold satisfies
-//               tau >= max x - 1 because the top token's weight is at most 1.
+// gather_score  grid of (slot, unit) blocks over work items of 64 consecutive
+//               tokens of a (sequence, KV head)'s page list.  Each K row is read once
+//               and scored against every query head of the group,
+//               x = (alpha-1) scale q.k.  For bf16 keys and groups of up to
+//               4 heads the scores come from the matrix cores (16 tokens x
+//               4 heads x 3 limbs of q per instruction), otherwise from the
+//               vector ALUs.  An item keeps only tokens that can be in the
+//               support: x > (item max) - 1, since the threshold satisfies
+//               tau >= (head max) - 1 >= (item max) - 1 (the top token's
+//               weight is at most 1).
 // tau_v         one block per (sequence, query head): collects the
-//               candidates above (final max) - 1, finds the exact threshold
-//               and support, and accumulates sum_j p_j v_j over the support
-//               (rows split across the block, fixed-order combine).
+//               candidates above (head max) - 1, finds the exact threshold
+//               and support in float64, and accumulates sum_j p_j v_j over
+//               the support rows (rows split across the block, fixed-order
+//               combine, so results are bitwise reproducible).
 #include "ekv_kernels.h"
 
 namespace ekv {
 
 constexpr int kDecThreads = 256;
 constexpr int kTauThreads = 256;
+constexpr int kTauItemChunk = 1024;
 
 __device__ __forceinline__ int dec_len(const DecodeArgs& a, int b) {
   const int L = a.seq_lens[b];
@@ -36,151 +39,304 @@ __device__ __forceinline__ int unit_pages(const DecodeArgs& a, int u) {
   return min(max(a.sel_count[u], 0), min(a.cap, n_b));
 }
 
-template <int DT, int D, int G>
-__global__ __launch_bounds__(kDecThreads) void gather_score_kernel(DecodeArgs a) {
-  using E = Elem<DT>;
-  constexpr int EPL = E::kPerVec;
-  constexpr int LPR = D / EPL;         // lanes per K row
-  static_assert(LPR <= kWave && G <= LPR, "layout");
-  constexpr int RPW = kWave / LPR;     // rows per wave load
-  constexpr int NW = kDecThreads / kWave;
-  constexpr int RPI = NW * RPW;        // rows per block iteration
-  // dynamic LDS: prefix[n_units + 1] | x[G][ppi * P] | phys[ppi] | np[ppi] | lp[ppi]
-  extern __shared__ int smem[];
-  __shared__ int redi[17];
+__device__ __forceinline__ int unit_items(const DecodeArgs& a, int u) {
+  return (int)(((long long)unit_pages(a, u) * a.page_size + kItemTokens - 1) / kItemTokens);
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int sub = lane % LPR, dim0 = sub * EPL, rloc = lane / LPR;
-  const int P = a.page_size, Hkv = a.n_kv_heads, ppi = a.ppi;
-  const int n_units = a.batch * Hkv;
-  const int tpi = ppi * P;
-  const size_t max_tok = (size_t)a.max_pages * P;
-  int* s_prefix = smem;
-  float* s_xall = reinterpret_cast<float*>(smem + n_units + 1);
-  int* s_phys = smem + n_units + 1 + G * tpi;
-  int* s_np = s_phys + ppi;
-  int* s_lp = s_np + ppi;
+// Token r of item j of unit u: its physical row (page * P + slot), logical
+// token id, and whether it holds a valid key.
+struct TokenRef {
+  int phys, slot, logical;
+  bool valid;
+};
 
-  // item prefix over units (same on every block)
-  int running = 0;
-  for (int u0 = 0; u0 < n_units; u0 += kDecThreads) {
-    const int u = u0 + tid;
-    const int items = u < n_units ? (unit_pages(a, u) + ppi - 1) / ppi : 0;
-    int tot;
-    const int ex = block_exclusive_scan(items, redi, &tot);
-    if (u < n_units) s_prefix[u] = running + ex;
-    running += tot;
+__device__ __forceinline__ TokenRef token_ref(const DecodeArgs& a, int u, int b, int L, int n_b, int npu, int j,
+                                              int r) {
+  TokenRef t{-1, 0, 0, false};
+  const int P = a.page_size;
+  const long long T = (long long)j * kItemTokens + r;
+  if (T >= (long long)npu * P) return t;
+  const int k = (int)(T / P);
+  t.slot = (int)(T - (long long)k * P);
+  const int lp = a.sel ? a.sel[(size_t)u * a.cap + k] : k;
+  if (lp < 0 || lp >= n_b) {
+    set_status(a.status, EKV_DEV_BAD_PAGE);
+    return t;
   }
-  if (tid == 0) s_prefix[n_units] = running;
-  __syncthreads();
-  const int total_items = running;
+  const int phys = a.page_table[(size_t)b * a.max_pages + lp];
+  if (phys < 0 || phys >= a.n_phys) {
+    set_status(a.status, EKV_DEV_BAD_PAGE);
+    return t;
+  }
+  t.phys = phys;
+  t.logical = lp * P + t.slot;
+  t.valid = t.slot < L - lp * P;
+  return t;
+}
 
-  int cur_u = -1;
-  float qr[G][EPL];
-  for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
-    // unit of this item: last u with s_prefix[u] <= item
-    int lo = 0, hi = n_units;  // invariant: s_prefix[lo] <= item < s_prefix[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_prefix[mid] <= item) lo = mid; else hi = mid;
+// Sizes of one unit (sequence b, KV head g) of a (slot, unit) grid.
+struct UnitCtx {
+  int L, n_b, npu, n_items;
+};
+
+// References of token r in items j0 .. j0+SUB-1 of unit u, resolved in two
+// dependent rounds whose loads all travel together: round one reads the
+// page-list entries (and, when `first`, the sequence length and selection
+// count), round two the page-table entries.  Entries are range-checked
+// against the table before the length is known and against the length
+// afterwards.
+template <int SUB>
+__device__ __forceinline__ void resolve_refs(const DecodeArgs& a, int u, int b, int j0, int r, bool first,
+                                             UnitCtx* ctx, TokenRef* tr) {
+  const int P = a.page_size;
+  const int capk = a.sel ? min(a.cap, a.max_pages) : a.max_pages;
+  long long T[SUB];
+  int lp[SUB], ph[SUB];
+#pragma unroll
+  for (int s = 0; s < SUB; ++s) {
+    T[s] = (long long)(j0 + s) * kItemTokens + r;
+    const int k = (int)(T[s] / P);
+    lp[s] = k < capk ? (a.sel ? a.sel[(size_t)u * a.cap + k] : k) : -1;
+  }
+  if (first) {
+    int L = a.seq_lens[b];
+    const int cnt = a.sel ? a.sel_count[u] : 0;
+    if (L < 0 || (long long)L > (long long)a.max_pages * P) L = L < 0 ? 0 : a.max_pages * P;
+    ctx->L = L;
+    ctx->n_b = pages_of(L, P);
+    ctx->npu = a.sel ? min(max(cnt, 0), min(a.cap, ctx->n_b)) : ctx->n_b;
+    ctx->n_items = (int)(((long long)ctx->npu * P + kItemTokens - 1) / kItemTokens);
+  }
+#pragma unroll
+  for (int s = 0; s < SUB; ++s)
+    ph[s] = (lp[s] >= 0 && lp[s] < a.max_pages) ? a.page_table[(size_t)b * a.max_pages + lp[s]] : -1;
+#pragma unroll
+  for (int s = 0; s < SUB; ++s) {
+    const int k = (int)(T[s] / P);
+    const int slot = (int)(T[s] - (long long)k * P);
+    tr[s] = TokenRef{-1, slot, 0, false};
+    if (T[s] >= (long long)ctx->npu * P) continue;
+    if (lp[s] < 0 || lp[s] >= ctx->n_b || ph[s] < 0 || ph[s] >= a.n_phys) {
+      set_status(a.status, EKV_DEV_BAD_PAGE);
+      continue;
     }
-    const int u = lo, j = item - s_prefix[u];
-    const int b = u / Hkv, g = u % Hkv;
-    const int L = dec_len(a, b);
-    const int n_b = pages_of(L, P);
-    const int npu = unit_pages(a, u);
-    const int k0 = j * ppi, npg = min(k0 + ppi, npu) - k0;
-    if (tid < npg) {
-      int lp = a.sel ? a.sel[(size_t)u * a.cap + k0 + tid] : k0 + tid;
-      int phys = -1, np = 0;
-      if (lp < 0 || lp >= n_b) {
-        set_status(a.status, EKV_DEV_BAD_PAGE);
-        lp = 0;
+    tr[s].phys = ph[s];
+    tr[s].logical = lp[s] * P + slot;
+    tr[s].valid = slot < ctx->L - lp[s] * P;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core gather (bf16 keys, G <= 4).  Grid (slots, units): block
+// (s, u) takes super-items s, s + slots, ... of unit u, a super-item being
+// SUB consecutive 64-token items whose loads are all issued before any is
+// used.  A rows 4h + l hold limb l of q_h (alpha-1) scale; B columns are the
+// 16 tokens of a wave; the fp32 accumulator runs over the D/32 k blocks.
+// Lane l ends with head l/16 of token l%16: x = (c0 + c1) + c2.
+// ---------------------------------------------------------------------------
+template <int D, int G, int SUB>
+__global__ __launch_bounds__(kDecThreads) void gather_mfma_kernel(DecodeArgs a, int slots) {
+  constexpr int KB = D / 32;
+  __shared__ u32x4_t s_a[KB][kWave];
+  __shared__ float s_max[SUB][4][4];
+  __shared__ int s_cnt[SUB][4][4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int u = blockIdx.y, Hkv = a.n_kv_heads;
+  const int b = u / Hkv, g = u - b * Hkv;
+  const size_t tok_per_bh = (size_t)a.max_items * kItemTokens;
+  const int r = 16 * w + col;  // this lane's token within an item
+
+  // loads, in order: q for the A operand, then the first super-item's
+  // references (resolved speculatively with the unit's size)
+  const float qs = (a.alpha - 1.f) * a.scale;
+  const float* qg = a.q + ((size_t)b * a.n_q_heads + (size_t)g * G) * D;
+  LimbChunks<KB> lc;
+  limb_fetch<KB, G>(lc, [&](int h, int k0, float* v) {
+    const float4* qv = reinterpret_cast<const float4*>(qg + (size_t)h * D + k0);
+    const float4 q0 = qv[0], q1 = qv[1];
+    v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w; v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
+  });
+  UnitCtx ctx;
+  TokenRef tr[SUB];
+  resolve_refs<SUB>(a, u, b, blockIdx.x * SUB, r, true, &ctx, tr);
+  bool a_ready = false;
+  const int n_super = (ctx.n_items + SUB - 1) / SUB;
+  for (int sj = blockIdx.x; sj < n_super; sj += slots) {
+    if (sj != (int)blockIdx.x) resolve_refs<SUB>(a, u, b, sj * SUB, r, false, &ctx, tr);
+    u32x4_t bv[SUB][KB];
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      if (tr[s].phys >= 0) {
+        const uint16_t* row = reinterpret_cast<const uint16_t*>(a.k) +
+                              (((size_t)tr[s].phys * Hkv + g) * a.page_size + tr[s].slot) * D + 8 * grp;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) bv[s][kb] = *reinterpret_cast<const u32x4_t*>(row + 32 * kb);
       } else {
-        phys = a.page_table[(size_t)b * a.max_pages + lp];
-        if (phys < 0 || phys >= a.n_phys) {
-          set_status(a.status, EKV_DEV_BAD_PAGE);
-          phys = -1;
-        } else {
-          np = min(P, L - lp * P);
-        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) bv[s][kb] = u32x4_t{0u, 0u, 0u, 0u};
       }
-      s_lp[tid] = lp;
-      s_phys[tid] = phys;
-      s_np[tid] = np;
     }
-    if (u != cur_u) {
-      cur_u = u;
-      const float qs = (a.alpha - 1.f) * a.scale;
+    if (!a_ready) {  // q limbs: coefficients q_h (alpha-1) scale (block-uniform)
+      limb_build<KB, G>(s_a, lc, [qs](int, float qv) { return qv * qs; });
+      __syncthreads();
+      a_ready = true;
+    }
+    float x[SUB];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float* qh = a.q + ((size_t)b * a.n_q_heads + (size_t)g * G + h) * D + dim0;
+    for (int s = 0; s < SUB; ++s) {
+      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) qr[h][e] = qh[e] * qs;
-      }
+      for (int kb = 0; kb < KB; ++kb) c = mfma_bf16(s_a[kb][lane], bv[s][kb], c);
+      x[s] = tr[s].valid && grp < G ? (c[0] + c[1]) + c[2] : -INFINITY;
+      // per-head item maximum (the 16 lanes of one head share grp)
+      float m = x[s];
+      m = fmaxf(m, __shfl_xor(m, 1, kWave));
+      m = fmaxf(m, __shfl_xor(m, 2, kWave));
+      m = fmaxf(m, __shfl_xor(m, 4, kWave));
+      m = fmaxf(m, __shfl_xor(m, 8, kWave));
+      if (col == 0) s_max[s][w][grp] = m;
     }
     __syncthreads();
-    const int ntok = npg * P;
-    for (int r0 = 0; r0 < ntok; r0 += RPI) {
-      const int r = r0 + w * RPW + rloc;
-      const int kk = r / P, slot = r - kk * P;
-      const bool valid = r < ntok && slot < s_np[min(kk, npg - 1)];
+    // candidates: above (super-item maximum) - 1, a lower bound on tau
+    float m[SUB], msup = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      m[s] = fmaxf(fmaxf(s_max[s][0][grp], s_max[s][1][grp]), fmaxf(s_max[s][2][grp], s_max[s][3][grp]));
+      msup = fmaxf(msup, m[s]);
+    }
+    bool keep[SUB];
+    uint32_t bits[SUB];
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      keep[s] = grp < G && msup > -INFINITY && (double)x[s] > (double)msup - 1.0;
+      const unsigned long long bal = __ballot(keep[s]);
+      bits[s] = (uint32_t)(bal >> (16 * grp)) & 0xffffu;
+      if (col == 0) s_cnt[s][w][grp] = __popc(bits[s]);
+    }
+    __syncthreads();
+    if (grp < G) {
+      const size_t bh = (size_t)b * a.n_q_heads + (size_t)g * G + grp;
+#pragma unroll
+      for (int s = 0; s < SUB; ++s) {
+        const int j = sj * SUB + s;
+        if (j >= ctx.n_items) break;
+        int off = 0, tot = 0;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+          off += ww < w ? s_cnt[s][ww][grp] : 0;
+          tot += s_cnt[s][ww][grp];
+        }
+        if (keep[s]) {
+          const int pos = off + __popc(bits[s] & ((1u << col) - 1u));
+          const size_t at = bh * tok_per_bh + (size_t)j * kItemTokens + pos;
+          a.cand_x[at] = x[s];
+          a.cand_t[at] = tr[s].logical;
+          a.cand_r[at] = tr[s].phys * a.page_size + tr[s].slot;
+        }
+        if (w == 0 && col == 0) {
+          a.item_cnt[bh * a.max_items + j] = tot;
+          a.item_max[bh * a.max_items + j] = m[s];
+        }
+      }
+    }
+    __syncthreads();  // s_max / s_cnt are rewritten by the next super-item
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Vector-ALU gather (fp32 keys or groups of 8): LPR lanes per K row, every
+// load of the item issued up front, fp32 dot products reduced across the
+// row's lanes; scores staged in LDS, then one wave per head compacts.
+// ---------------------------------------------------------------------------
+template <int DT, int D, int G>
+__global__ __launch_bounds__(kDecThreads) void gather_valu_kernel(DecodeArgs a, int slots) {
+  using E = Elem<DT>;
+  constexpr int EPL = E::kPerVec;
+  constexpr int LPR = D / EPL;           // lanes per K row
+  static_assert(LPR <= kWave && G <= LPR, "layout");
+  constexpr int RPW = kWave / LPR;       // rows per wave load
+  constexpr int RPI = 4 * RPW;           // rows per block load
+  constexpr int NIT = kItemTokens / RPI; // loads per lane per item
+  __shared__ float s_x[G][kItemTokens];
+  __shared__ int s_t[kItemTokens], s_r[kItemTokens];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int sub = lane % LPR, dim0 = sub * EPL, rloc = lane / LPR;
+  const int u = blockIdx.y, Hkv = a.n_kv_heads;
+  const int b = u / Hkv, g = u - b * Hkv;
+  const size_t tok_per_bh = (size_t)a.max_items * kItemTokens;
+  UnitCtx ctx;
+  TokenRef tr[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it)
+    resolve_refs<1>(a, u, b, blockIdx.x, it * RPI + w * RPW + rloc, it == 0, &ctx, &tr[it]);
+  float qr[G][EPL];
+  const float qs = (a.alpha - 1.f) * a.scale;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float* qh = a.q + ((size_t)b * a.n_q_heads + (size_t)g * G + h) * D + dim0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qr[h][e] = qh[e] * qs;
+  }
+  for (int j = blockIdx.x; j < ctx.n_items; j += slots) {
+    if (j != (int)blockIdx.x) {
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) resolve_refs<1>(a, u, b, j, it * RPI + w * RPW + rloc, false, &ctx, &tr[it]);
+    }
+    uint4 v[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int r = it * RPI + w * RPW + rloc;
+      if (tr[it].phys >= 0)
+        v[it] = ldg16(reinterpret_cast<const char*>(a.k) +
+                      ((((size_t)tr[it].phys * Hkv + g) * a.page_size + tr[it].slot) * D + dim0) * E::kBytes);
+      if (sub == 0) {
+        s_t[r] = tr[it].logical;
+        s_r[r] = tr[it].phys * a.page_size + tr[it].slot;
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int r = it * RPI + w * RPW + rloc;
       float acc[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) acc[h] = 0.f;
-      if (valid) {
-        const char* row = reinterpret_cast<const char*>(a.k) +
-                          ((((size_t)s_phys[kk] * Hkv + g) * P + slot) * D + dim0) * E::kBytes;
+      if (tr[it].valid) {
         float f[EPL];
-        E::unpack(ldg16(row), f);
+        E::unpack(v[it], f);
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
 #pragma unroll
           for (int h = 0; h < G; ++h) acc[h] = fmaf(qr[h][e], f[e], acc[h]);
       }
 #pragma unroll
-      for (int m = 1; m < LPR; m <<= 1) {
+      for (int m = 1; m < LPR; m <<= 1)
 #pragma unroll
         for (int h = 0; h < G; ++h) acc[h] += __shfl_xor(acc[h], m, kWave);
-      }
-      if (r < ntok && sub < G) {
-        float v = acc[0];
+      if (sub < G) {
+        float xv = acc[0];
 #pragma unroll
-        for (int h = 1; h < G; ++h) if (sub == h) v = acc[h];
-        s_xall[sub * tpi + r] = valid ? v : -INFINITY;
+        for (int h = 1; h < G; ++h) if (sub == h) xv = acc[h];
+        s_x[sub][r] = tr[it].valid ? xv : -INFINITY;
       }
     }
     __syncthreads();
-    // per head: item maximum, candidate threshold, ordered compaction
-    for (int h = w; h < G; h += NW) {
-      float m = -INFINITY;
-      for (int r = lane; r < ntok; r += kWave) m = fmaxf(m, s_xall[h * tpi + r]);
-      m = wave_max(m);
+    for (int h = w; h < G; h += 4) {
+      const float x = s_x[h][lane];
+      const float m = wave_max(x);
+      const bool keep = m > -INFINITY && (double)x > (double)m - 1.0;
+      const unsigned long long bal = __ballot(keep);
       const size_t bh = (size_t)b * a.n_q_heads + (size_t)g * G + h;
-      int cnt = 0;
-      if (m > -INFINITY) {
-        uint32_t old = 0;
-        if (lane == 0) old = atomicMax(&a.max_key[bh], f2key(m));
-        old = __shfl(old, 0, kWave);
-        const double thr = (double)fmaxf(m, old ? key2f(old) : m) - 1.0;
-        const size_t region = bh * max_tok + (size_t)j * ppi * P;
-        for (int r0 = 0; r0 < ntok; r0 += kWave) {
-          const int r = r0 + lane;
-          const float x = r < ntok ? s_xall[h * tpi + r] : -INFINITY;
-          const bool keep = (double)x > thr;
-          const unsigned long long bal = __ballot(keep);
-          if (keep) {
-            const int pos = cnt + __popcll(bal & ((1ull << lane) - 1ull));
-            const int kk = r / P;
-            a.cand_x[region + pos] = x;
-            a.cand_t[region + pos] = s_lp[kk] * P + (r - kk * P);
-          }
-          cnt += __popcll(bal);
-        }
+      if (keep) {
+        const int pos = __popcll(bal & ((1ull << lane) - 1ull));
+        const size_t at = bh * tok_per_bh + (size_t)j * kItemTokens + pos;
+        a.cand_x[at] = x;
+        a.cand_t[at] = s_t[lane];
+        a.cand_r[at] = s_r[lane];
       }
       if (lane == 0) {
-        a.item_cnt[bh * a.max_pages + j] = cnt;
-        a.item_max[bh * a.max_pages + j] = m;
+        a.item_cnt[bh * a.max_items + j] = __popcll(bal);
+        a.item_max[bh * a.max_items + j] = m;
       }
     }
     __syncthreads();
@@ -200,105 +356,49 @@ __global__ __launch_bounds__(kDecThreads) void gather_score_kernel(DecodeArgs a)
 // t takes the larger of the two, so every failed round drops >= 1 element.
 // For other alpha only Newton runs, to convergence.
 // ---------------------------------------------------------------------------
-template <int DT, int D>
-__global__ __launch_bounds__(kTauThreads) void tau_v_kernel(DecodeArgs a) {
-  using E = Elem<DT>;
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int G = a.group, g = h / G, Hkv = a.n_kv_heads, P = a.page_size;
-  const int u = b * Hkv + g;
-  const size_t bh = (size_t)b * a.n_q_heads + h;
-  const size_t max_tok = (size_t)a.max_pages * P;
-  __shared__ float lx[kLdsCands];
-  __shared__ int lt[kLdsCands];
-  __shared__ double redd[16];
-  __shared__ int redi[17];
-  __shared__ float vpart[kTauThreads / (D / E::kPerVec)][D];
+// (d)^(1/(alpha-1)) for d > 0: AK = 0 for alpha 2, 1 for alpha 1.5, 2 otherwise
+// (compile-time, so the common cases carry no pow).
+template <int AK> __device__ __forceinline__ double entmax_pow(double d, double beta) {
+  if (AK == 0) return d;
+  if (AK == 1) return d * d;
+  return pow(d, beta);
+}
 
-  const int ppi = a.ppi;
-  const int npu = unit_pages(a, u);
-  const int n_items = (npu + ppi - 1) / ppi;
-  const uint32_t mk = a.max_key[bh];
-  __syncthreads();
-  if (tid == 0) a.max_key[bh] = 0u;  // leave the control word clean for the next step
-  float* out = a.out + bh * D;
-  if (n_items == 0 || mk == 0u) {
-    for (int e = tid; e < D; e += blockDim.x) out[e] = 0.f;
-    if (tid == 0) {
-      if (a.tau) a.tau[bh] = -INFINITY;
-      if (a.support_count) a.support_count[bh] = 0;
-      if (a.psum) a.psum[bh] = 0.f;
-    }
-    return;
-  }
-  const double m = key2f(mk);
-  const double thr = m - 1.0;
-  const int32_t* icnt = a.item_cnt + bh * a.max_pages;
-  const float* cx = a.cand_x + bh * max_tok;
-  const int32_t* ct = a.cand_t + bh * max_tok;
+template <bool WAVE, typename T> __device__ __forceinline__ T red_sum(T v, T* red) {
+  return WAVE ? wave_sum(v) : block_sum(v, red);
+}
+template <bool WAVE, typename T> __device__ __forceinline__ T red_min(T v, T* red) {
+  return WAVE ? wave_min(v) : block_min(v, red);
+}
 
-  // ---- collect candidates above m - 1, in item order ----
-  int N = 0;
-  for (int j0 = 0; j0 < n_items; j0 += kTauThreads) {
-    const int j = j0 + tid;
-    int c = 0;
-    if (j < n_items) {
-      const size_t base = (size_t)j * ppi * P;
-      const int n = icnt[j];
-      for (int i = 0; i < n; ++i) c += (double)cx[base + i] > thr;
-    }
-    int tot;
-    block_exclusive_scan(c, redi, &tot);
-    N += tot;
-  }
-  const bool in_lds = N <= kLdsCands;
-  float* xs = in_lds ? lx : a.ovf_x + bh * max_tok;
-  int32_t* ts = in_lds ? lt : a.ovf_t + bh * max_tok;
-  int run = 0;
-  for (int j0 = 0; j0 < n_items; j0 += kTauThreads) {
-    const int j = j0 + tid;
-    int c = 0, n = 0;
-    size_t base = 0;
-    if (j < n_items) {
-      base = (size_t)j * ppi * P;
-      n = icnt[j];
-      for (int i = 0; i < n; ++i) c += (double)cx[base + i] > thr;
-    }
-    int tot;
-    int pos = run + block_exclusive_scan(c, redi, &tot);
-    for (int i = 0; i < n; ++i) {
-      const float x = cx[base + i];
-      if ((double)x > thr) { xs[pos] = x; ts[pos] = ct[base + i]; ++pos; }
-    }
-    run += tot;
-  }
-  __syncthreads();
-
-  // ---- threshold ----
-  const double alpha = a.alpha;
-  const bool sparsemax = a.alpha == 2.0f, ent15 = a.alpha == 1.5f;
-  const double beta = 1.0 / (alpha - 1.0);
+// Exact threshold of the N candidate scores xs (all threads of the calling
+// wave, or of the block, take part; every one gets the result).
+template <bool WAVE, int AK>
+__device__ double solve_threshold(const float* xs, int N, double m, double thr, float alpha_f, double* redd) {
+  const int idx = WAVE ? (threadIdx.x & 63) : threadIdx.x;
+  const int stride = WAVE ? kWave : blockDim.x;
+  constexpr bool sparsemax = AK == 0, ent15 = AK == 1;
+  const double beta = 1.0 / ((double)alpha_f - 1.0);
   double t = thr, tau = thr, t_prev = thr;
   for (int it = 0; it < 4096; ++it) {
     tau = t;  // fallback if the iteration cap is ever reached
-    double s1 = 0.0, s2 = 0.0, f = 0.0, fd = 0.0, xmin = INFINITY;
-    double cnt = 0.0;
-    for (int i = tid; i < N; i += blockDim.x) {
+    double s1 = 0.0, s2 = 0.0, f = 0.0, fd = 0.0, xmin = INFINITY, cnt = 0.0;
+    for (int i = idx; i < N; i += stride) {
       const double x = xs[i];
       if (x > t) {
         const double y = x - m, d = x - t;
         cnt += 1.0; s1 += y; s2 += y * y; xmin = fmin(xmin, x);
-        if (sparsemax) { f += d; fd += 1.0; }
-        else if (ent15) { f += d * d; fd += 2.0 * d; }
-        else { const double pw = pow(d, beta); f += pw; fd += beta * pw / d; }
+        const double pw = entmax_pow<AK>(d, beta);
+        f += pw;
+        fd += sparsemax ? 1.0 : (ent15 ? 2.0 * d : beta * pw / d);
       }
     }
-    cnt = block_sum(cnt, redd);
-    s1 = block_sum(s1, redd);
-    s2 = block_sum(s2, redd);
-    f = block_sum(f, redd);
-    fd = block_sum(fd, redd);
-    xmin = block_min(xmin, redd);
+    cnt = red_sum<WAVE>(cnt, redd);
+    s1 = red_sum<WAVE>(s1, redd);
+    s2 = red_sum<WAVE>(s2, redd);
+    f = red_sum<WAVE>(f, redd);
+    fd = red_sum<WAVE>(fd, redd);
+    xmin = red_min<WAVE>(xmin, redd);
     if (cnt == 0.0) { tau = t_prev; break; }  // only reachable through rounding
     t_prev = t;
     if (sparsemax || ent15) {
@@ -323,6 +423,276 @@ __global__ __launch_bounds__(kTauThreads) void tau_v_kernel(DecodeArgs a) {
       if (step <= 1e-15 * fmax(1.0, fabs(t))) break;
     }
   }
+  return tau;
+}
+
+// Exact threshold of at most blockDim.x candidates by the pairwise support
+// test: with f(t) = sum_j (x_j - t)_+^e decreasing and f(tau) = 1, x_i is in
+// the support iff f(x_i) < 1.  Thread i evaluates f(x_i) (float64); then tau
+// follows from the closed form on the support (alpha 2 or 1.5) or from
+// Newton's method on it, started below tau at the largest excluded score
+// (other alpha).  All threads of the block take part and get the result.
+template <int AK>
+__device__ double solve_pairwise(const float* xs, int N, double m, float alpha_f, double* red) {
+  const int i = threadIdx.x, lane = i & 63;
+  constexpr bool sparsemax = AK == 0, ent15 = AK == 1;
+  const double beta = 1.0 / ((double)alpha_f - 1.0);
+  const bool has = i < N;
+  const double xi = has ? (double)xs[i] : 0.0;
+  // every wave keeps all N scores in registers (lane l holds x[l + 64 r]) and
+  // broadcasts them with readlane, so the inner loop makes no memory access
+  constexpr int R = kTauThreads / kWave;
+  float xr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) xr[r] = (lane + kWave * r < N) ? xs[lane + kWave * r] : 0.f;
+  double f = 0.0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int nr = min(kWave, N - kWave * r);
+    for (int l = 0; l < nr; ++l) {
+      const float xj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xr[r]), l));
+      const double d = (double)xj - xi;
+      if (d > 0.0) f += entmax_pow<AK>(d, beta);
+    }
+  }
+  const bool in = has && f < 1.0;
+  const double y = xi - m;
+  double c = in ? 1.0 : 0.0, s1 = in ? y : 0.0, s2 = in ? y * y : 0.0;
+  c = block_sum(c, red);
+  s1 = block_sum(s1, red);
+  s2 = block_sum(s2, red);
+  if (sparsemax) return m + (s1 - 1.0) / c;
+  if (ent15) {
+    const double mu = s1 / c;
+    const double disc = (1.0 - c * (s2 / c - mu * mu)) / c;
+    return m + mu - sqrt(fmax(disc, 0.0));
+  }
+  // other alpha: Newton on g(t) = sum_S (x - t)^beta - 1 from the largest excluded score
+  double lo = (has && !in) ? xi : m - 1.0;
+  lo = block_max(lo, red);
+  double t = lo;
+  for (int it = 0; it < 100; ++it) {
+    double g = 0.0, gd = 0.0;
+    if (in) {
+      const double d = xi - t;
+      const double pw = entmax_pow<AK>(d, beta);
+      g = pw;
+      gd = beta * pw / d;
+    }
+    g = block_sum(g, red);
+    gd = block_sum(gd, red);
+    const double step = (g - 1.0) / gd;
+    if (!(step > 0.0)) break;
+    t += step;
+    if (step <= 1e-15 * fmax(1.0, fabs(t))) break;
+  }
+  return t;
+}
+
+// On-chip scratch of the threshold stage (one instance per block).
+struct TauSmem {
+  float lx[kLdsCands];
+  int lt[kLdsCands];
+  int lr[kLdsCands];
+  int s_pre[kTauItemChunk + 1];
+  float vpart[2048];  // row-group partial outputs (RPB x D <= 2048)
+  double redd[16];
+  int redi[17];
+  double s_tau;
+  uint32_t s_mkey[4];
+  int s_kcnt[4];
+  int s_flag;
+};
+
+// Threshold, support and output of query head h of sequence b from the
+// candidate lists of its unit; the whole block takes part.
+template <int DT, int D, int AK>
+__device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
+  using E = Elem<DT>;
+  const int tid = threadIdx.x;
+  const int G = a.group, g = h / G, Hkv = a.n_kv_heads, P = a.page_size;
+  const int u = b * Hkv + g;
+  const size_t bh = (size_t)b * a.n_q_heads + h;
+  const size_t tok_per_bh = (size_t)a.max_items * kItemTokens;
+  float* lx = sm.lx;
+  int* lt = sm.lt;
+  int* lr = sm.lr;
+  int* s_pre = sm.s_pre;
+  double* redd = sm.redd;
+  int* redi = sm.redi;
+  constexpr int EPL = E::kPerVec;
+  constexpr int LPR = D / EPL;
+  constexpr int RPB = kTauThreads / LPR;
+  static_assert(RPB * D <= 2048, "vpart");
+  float (*vpart)[D] = reinterpret_cast<float (*)[D]>(sm.vpart);
+  __syncthreads();  // sm may still be in use by the caller
+
+  const int n_items = unit_items(a, u);
+  float* out = a.out + bh * D;
+  const int32_t* icnt = a.item_cnt + bh * a.max_items;
+  const float* imax = a.item_max + bh * a.max_items;
+  const float* cx = a.cand_x + bh * tok_per_bh;
+  const int32_t* ct = a.cand_t + bh * tok_per_bh;
+  const int32_t* cr = a.cand_r + bh * tok_per_bh;
+
+  // ---- item counts and maxima (one round of loads) ----
+  constexpr int IPT = 4;  // items per thread when n_items <= 1024
+  constexpr int RPT = 16;  // raw candidates per thread when they number <= 4096
+  const int tid_w = tid >> 6;
+  const bool few_items = n_items <= IPT * kTauThreads;
+  int loc[IPT], lsum = 0;
+  float lmax = -INFINITY;
+  if (few_items) {
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int jj = IPT * tid + i;
+      loc[i] = jj < n_items ? icnt[jj] : 0;
+      lmax = fmaxf(lmax, jj < n_items ? imax[jj] : -INFINITY);
+      lsum += loc[i];
+    }
+  } else {
+    for (int j = tid; j < n_items; j += blockDim.x) lmax = fmaxf(lmax, imax[j]);
+  }
+  const float mf = block_max(lmax, reinterpret_cast<float*>(redd));
+  if (!(mf > -INFINITY)) {  // no pages, or every page invalid (flagged): empty result
+    for (int e = tid; e < D; e += blockDim.x) out[e] = 0.f;
+    if (tid == 0) {
+      if (a.tau) a.tau[bh] = -INFINITY;
+      if (a.support_count) a.support_count[bh] = 0;
+      if (a.psum) a.psum[bh] = 0.f;
+    }
+    return;
+  }
+  const double m = mf;
+  const double thr = m - 1.0;
+
+  // ---- collect candidates above m - 1, in item order ----
+  int N = 0;
+  bool in_lds = true, done = false;
+  if (few_items) {
+    int raw_tot;
+    int base = block_exclusive_scan(lsum, redi, &raw_tot);
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      if (IPT * tid + i < n_items) s_pre[IPT * tid + i] = base;
+      base += loc[i];
+    }
+    if (tid == 0) s_pre[n_items] = raw_tot;
+    __syncthreads();
+    if (raw_tot <= RPT * kTauThreads) {
+      // thread t reads raw candidates [RPT t, RPT t + RPT): one round of loads
+      float xv[RPT];
+      int tv[RPT], rv[RPT];
+      const int i0 = RPT * tid;
+      int item = 0;
+      if (i0 < raw_tot) {
+        int lo = 0, hi = n_items;  // s_pre[lo] <= i0 < s_pre[hi]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s_pre[mid] <= i0) lo = mid; else hi = mid;
+        }
+        item = lo;
+      }
+#pragma unroll
+      for (int c = 0; c < RPT; ++c) {
+        const int i = i0 + c;
+        xv[c] = -INFINITY;
+        tv[c] = rv[c] = 0;
+        if (i < raw_tot) {
+          while (s_pre[item + 1] <= i) ++item;
+          const size_t at = (size_t)item * kItemTokens + (i - s_pre[item]);
+          xv[c] = cx[at];
+          tv[c] = ct[at];
+          rv[c] = cr[at];
+        }
+      }
+      int kc = 0;
+#pragma unroll
+      for (int c = 0; c < RPT; ++c) kc += (double)xv[c] > thr;
+      int pos = block_exclusive_scan(kc, redi, &N);
+#pragma unroll
+      for (int c = 0; c < RPT; ++c)
+        if ((double)xv[c] > thr) { lx[pos] = xv[c]; lt[pos] = tv[c]; lr[pos] = rv[c]; ++pos; }
+      done = true;
+    }
+  }
+  if (!done) {
+    // general case: chunks of items; pass 0 counts, pass 1 writes (to LDS
+    // when the kept candidates fit, else to the workspace list)
+    for (int pass = 0; pass < 2; ++pass) {
+      int run = 0;
+      for (int c0 = 0; c0 < n_items; c0 += kTauItemChunk) {
+        const int nc = min(kTauItemChunk, n_items - c0);
+        int lc[4], sum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int jj = 4 * tid + i;
+          lc[i] = jj < nc ? icnt[c0 + jj] : 0;
+          sum += lc[i];
+        }
+        int raw_tot;
+        int base = block_exclusive_scan(sum, redi, &raw_tot);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (4 * tid + i < nc) s_pre[4 * tid + i] = base;
+          base += lc[i];
+        }
+        if (tid == 0) s_pre[nc] = raw_tot;
+        __syncthreads();
+        for (int i0 = 0; i0 < raw_tot; i0 += blockDim.x) {
+          const int i = i0 + tid;
+          float x = -INFINITY;
+          size_t at = 0;
+          if (i < raw_tot) {
+            int lo = 0, hi = nc;  // s_pre[lo] <= i < s_pre[hi]
+            while (hi - lo > 1) {
+              const int mid = (lo + hi) >> 1;
+              if (s_pre[mid] <= i) lo = mid; else hi = mid;
+            }
+            at = (size_t)(c0 + lo) * kItemTokens + (i - s_pre[lo]);
+            x = cx[at];
+          }
+          const bool keep = (double)x > thr;
+          int tot;
+          const int pos = run + block_exclusive_scan(keep ? 1 : 0, redi, &tot);
+          if (pass == 1 && keep) {
+            if (in_lds) {
+              lx[pos] = x; lt[pos] = ct[at]; lr[pos] = cr[at];
+            } else {
+              a.ovf_x[bh * tok_per_bh + pos] = x;
+              a.ovf_t[bh * tok_per_bh + pos] = ct[at];
+              a.ovf_r[bh * tok_per_bh + pos] = cr[at];
+            }
+          }
+          run += tot;
+        }
+        __syncthreads();
+      }
+      N = run;
+      if (pass == 0) in_lds = N <= kLdsCands;
+    }
+  }
+  __syncthreads();
+  float* xs = in_lds ? lx : a.ovf_x + bh * tok_per_bh;
+  int32_t* ts = in_lds ? lt : a.ovf_t + bh * tok_per_bh;
+  int32_t* rs = in_lds ? lr : a.ovf_r + bh * tok_per_bh;
+
+  // ---- threshold: one wave when the candidates are few, else the block ----
+  double tau;
+  double& s_tau = sm.s_tau;
+  if (N <= kTauThreads) {
+    tau = solve_pairwise<AK>(xs, N, m, a.alpha, redd);
+  } else if (N <= 8 * kWave) {
+    if (tid_w == 0) {
+      tau = solve_threshold<true, AK>(xs, N, m, thr, a.alpha, redd);
+      if ((tid & 63) == 0) s_tau = tau;
+    }
+    __syncthreads();
+    tau = s_tau;
+  } else {
+    tau = solve_threshold<false, AK>(xs, N, m, thr, a.alpha, redd);
+  }
+  const double beta = 1.0 / ((double)a.alpha - 1.0);
 
   // ---- support, weights, compaction in place (p replaces x) ----
   double ps = 0.0;
@@ -330,13 +700,13 @@ __global__ __launch_bounds__(kTauThreads) void tau_v_kernel(DecodeArgs a) {
   for (int i0 = 0; i0 < N; i0 += kTauThreads) {
     const int i = i0 + tid;
     float x = 0.f;
-    int tok = 0;
+    int tok = 0, row = 0;
     bool in = false;
-    if (i < N) { x = xs[i]; tok = ts[i]; in = (double)x > tau; }
+    if (i < N) { x = xs[i]; tok = ts[i]; row = rs[i]; in = (double)x > tau; }
     double p = 0.0;
     if (in) {
       const double d = (double)x - tau;
-      p = sparsemax ? d : (ent15 ? d * d : pow(d, beta));
+      p = entmax_pow<AK>(d, beta);
       ps += p;
     }
     int tot;
@@ -344,6 +714,7 @@ __global__ __launch_bounds__(kTauThreads) void tau_v_kernel(DecodeArgs a) {
     if (in) {
       xs[pos] = (float)p;
       ts[pos] = tok;
+      rs[pos] = row;
       if (a.support_idx && pos < a.support_cap) a.support_idx[bh * a.support_cap + pos] = tok;
     }
     nsup += tot;
@@ -352,23 +723,18 @@ __global__ __launch_bounds__(kTauThreads) void tau_v_kernel(DecodeArgs a) {
   ps = block_sum(ps, redd);
 
   // ---- sum_j p_j v_j ----
-  constexpr int EPL = E::kPerVec;
-  constexpr int LPR = D / EPL;
-  constexpr int RPB = kTauThreads / LPR;
   const int rr = tid / LPR, sub = tid % LPR;
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
   for (int s = rr; s < nsup; s += RPB) {
-    const int tok = ts[s];
+    const int row = rs[s];
     const float p = xs[s];
-    const int lp = tok / P, slot = tok - lp * P;
-    const int phys = a.page_table[(size_t)b * a.max_pages + lp];
-    if (phys < 0 || phys >= a.n_phys) continue;
-    const char* row = reinterpret_cast<const char*>(a.v) +
-                      ((((size_t)phys * Hkv + g) * P + slot) * D + (size_t)sub * EPL) * E::kBytes;
+    const int phys = row / P, slot = row - phys * P;
+    const char* vrow = reinterpret_cast<const char*>(a.v) +
+                       ((((size_t)phys * Hkv + g) * P + slot) * D + (size_t)sub * EPL) * E::kBytes;
     float f[EPL];
-    E::unpack(ldg16(row), f);
+    E::unpack(ldg16(vrow), f);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, f[e], acc[e]);
   }
@@ -387,33 +753,68 @@ __global__ __launch_bounds__(kTauThreads) void tau_v_kernel(DecodeArgs a) {
   }
 }
 
-size_t gather_lds_bytes(int n_units, int group, int ppi, int page_size) {
-  return 4 * ((size_t)n_units + 1 + (size_t)group * ppi * page_size + 3 * (size_t)ppi);
+template <int DT, int D, int AK>
+__global__ __launch_bounds__(kTauThreads) void tau_v_kernel(DecodeArgs a) {
+  __shared__ TauSmem sm;
+  tau_v_block<DT, D, AK>(a, blockIdx.y, blockIdx.x, sm);
 }
 
 template <int DT, int D>
-static hipError_t decode_dispatch(const DecodeArgs& a, int grid_items, hipStream_t s) {
-  const dim3 g1(grid_items), b1(kDecThreads);
-  const size_t lds = gather_lds_bytes(a.batch * a.n_kv_heads, a.group, a.ppi, a.page_size);
-  switch (a.group) {
-    case 1: hipLaunchKernelGGL((gather_score_kernel<DT, D, 1>), g1, b1, lds, s, a); break;
-    case 2: hipLaunchKernelGGL((gather_score_kernel<DT, D, 2>), g1, b1, lds, s, a); break;
-    case 4: hipLaunchKernelGGL((gather_score_kernel<DT, D, 4>), g1, b1, lds, s, a); break;
-    case 8: hipLaunchKernelGGL((gather_score_kernel<DT, D, 8>), g1, b1, lds, s, a); break;
-    default: return hipErrorInvalidValue;
+static hipError_t decode_dispatch(const DecodeArgs& a, int slots, int sub, hipStream_t s) {
+  const dim3 g1(slots, a.batch * a.n_kv_heads), b1(kDecThreads);
+  if (DT == EKV_BF16 && a.group <= 4) {
+    if (sub == 4) {
+      switch (a.group) {
+        case 1: hipLaunchKernelGGL((gather_mfma_kernel<D, 1, 4>), g1, b1, 0, s, a, slots); break;
+        case 2: hipLaunchKernelGGL((gather_mfma_kernel<D, 2, 4>), g1, b1, 0, s, a, slots); break;
+        default: hipLaunchKernelGGL((gather_mfma_kernel<D, 4, 4>), g1, b1, 0, s, a, slots); break;
+      }
+    } else {
+      switch (a.group) {
+        case 1: hipLaunchKernelGGL((gather_mfma_kernel<D, 1, 1>), g1, b1, 0, s, a, slots); break;
+        case 2: hipLaunchKernelGGL((gather_mfma_kernel<D, 2, 1>), g1, b1, 0, s, a, slots); break;
+        default: hipLaunchKernelGGL((gather_mfma_kernel<D, 4, 1>), g1, b1, 0, s, a, slots); break;
+      }
+    }
+  } else {
+    switch (a.group) {
+      case 1: hipLaunchKernelGGL((gather_valu_kernel<DT, D, 1>), g1, b1, 0, s, a, slots); break;
+      case 2: hipLaunchKernelGGL((gather_valu_kernel<DT, D, 2>), g1, b1, 0, s, a, slots); break;
+      case 4: hipLaunchKernelGGL((gather_valu_kernel<DT, D, 4>), g1, b1, 0, s, a, slots); break;
+      case 8: hipLaunchKernelGGL((gather_valu_kernel<DT, D, 8>), g1, b1, 0, s, a, slots); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((tau_v_kernel<DT, D>), dim3(a.n_q_heads, a.batch), dim3(kTauThreads), 0, s, a);
+  const dim3 g2(a.n_q_heads, a.batch), b2(kTauThreads);
+  if (a.alpha == 2.0f) hipLaunchKernelGGL((tau_v_kernel<DT, D, 0>), g2, b2, 0, s, a);
+  else if (a.alpha == 1.5f) hipLaunchKernelGGL((tau_v_kernel<DT, D, 1>), g2, b2, 0, s, a);
+  else hipLaunchKernelGGL((tau_v_kernel<DT, D, 2>), g2, b2, 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int grid_items, hipStream_t s) {
+// Gather grid: (slots, units).  A unit has at most `items` 64-token items
+// (the largest possible selection); on the matrix-core path items are
+// grouped into super-items of four for the full cache (more loads in flight
+// per block) and taken one by one for a selection.  slots is chosen so the
+// grid holds about `target_blocks` blocks, and never exceeds the work.
+hipError_t launch_decode(const DecodeArgs& a, int target_blocks, hipStream_t s) {
+  const long long pages = a.sel ? (a.cap < a.max_pages ? a.cap : a.max_pages) : a.max_pages;
+  const long long items = (pages * a.page_size + kItemTokens - 1) / kItemTokens;
+  const bool mfma = a.kv_dtype == EKV_BF16 && a.group <= 4;
+  const int sub = mfma ? 4 : 1;
+  const long long supers = (items + sub - 1) / sub;
+  const int units = a.batch * a.n_kv_heads;
+  long long slots = (target_blocks + units - 1) / units;
+  if (slots > supers) slots = supers;
+  if (slots < 1) slots = 1;
+  if (slots > 65535) slots = 65535;
   if (a.kv_dtype == EKV_BF16)
-    return a.head_dim == 128 ? decode_dispatch<EKV_BF16, 128>(a, grid_items, s)
-                             : decode_dispatch<EKV_BF16, 64>(a, grid_items, s);
-  return a.head_dim == 128 ? decode_dispatch<EKV_F32, 128>(a, grid_items, s)
-                           : decode_dispatch<EKV_F32, 64>(a, grid_items, s);
+    return a.head_dim == 128 ? decode_dispatch<EKV_BF16, 128>(a, (int)slots, sub, s)
+                             : decode_dispatch<EKV_BF16, 64>(a, (int)slots, sub, s);
+  return a.head_dim == 128 ? decode_dispatch<EKV_F32, 128>(a, (int)slots, sub, s)
+                           : decode_dispatch<EKV_F32, 64>(a, (int)slots, sub, s);
 }
 
 __global__ void fill_zero_kernel(uint4* p, size_t n16) {

@@ -8,8 +8,7 @@ namespace ekv {
 // Limits the kernels are compiled for (checked on the host before launch).
 constexpr int kMaxGroup = 8;         // query heads per KV head
 constexpr int kMaxUnits = 4096;      // batch * n_kv_heads
-constexpr int kMaxItemTokens = 1024; // tokens in one decode work item
-constexpr int kLdsCands = 2048;      // candidates kept in LDS by the threshold solve
+constexpr int kLdsCands = 1024;      // candidates kept in LDS by the threshold solve
 
 struct AppendArgs {
   int batch, n_kv_heads, page_size, head_dim, kv_dtype, max_pages, n_phys, n_new;
@@ -37,8 +36,11 @@ struct SelectArgs {
   int32_t* sel_count;
   int cap;
   float* tau_hat_out;  // optional
-  float* scores;       // bbox page scores [B*Hkv*max_pages]
-  float4* stats;       // Gaussian page stats [B*Hq*max_pages]
+  float* scores;       // bbox page scores [B*Hkv][score_stride]
+  int score_stride;
+  float2* musd;        // Gaussian page score (mean_Y, sd_Y) [B*Hq*max_pages]
+  float* ehat;         // estimated page maximum [B*Hq*max_pages]
+  float4* stats_out;   // optional (mean_Y, sd_Y, e_hat, n_p) copy for diagnostics
   double* tau_hat;     // [B*Hq]
   uint32_t* status;
 };
@@ -54,20 +56,21 @@ struct DecodeArgs {
   const int32_t* sel;  // NULL: every page of every sequence
   const int32_t* sel_count;
   int cap;
-  int ppi;  // pages per work item
   float* out;
   float* tau;            // optional
   int32_t* support_count;  // optional
   float* psum;           // optional
   int32_t* support_idx;  // optional
   int support_cap;
-  uint32_t* max_key;
+  int max_items;  // per (sequence, query head)
   int32_t* item_cnt;
   float* item_max;
   float* cand_x;
   int32_t* cand_t;
+  int32_t* cand_r;
   float* ovf_x;
   int32_t* ovf_t;
+  int32_t* ovf_r;
   uint32_t* status;
 };
 
@@ -78,8 +81,6 @@ hipError_t launch_topk(const SelectArgs& a, hipStream_t s);
 hipError_t launch_score_gauss(const SelectArgs& a, hipStream_t s);
 hipError_t launch_tau_hat(const SelectArgs& a, hipStream_t s);
 hipError_t launch_gauss_keep(const SelectArgs& a, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs& a, int grid_items, hipStream_t s);
-size_t gather_lds_bytes(int n_units, int group, int ppi, int page_size);
-constexpr size_t kMaxGatherLds = 60 * 1024;
+hipError_t launch_decode(const DecodeArgs& a, int target_blocks, hipStream_t s);
 
 }  // namespace ekv

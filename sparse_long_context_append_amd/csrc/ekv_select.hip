@@ -1,11 +1,14 @@
 // Page scoring and candidate selection (EntmaxKV summary sec. 2.A and 2.B).
 //
-// score_bbox   streams every page's k_min/k_max record once, coalesced, and
-//              forms the box upper bound of q.k for each query head of the
-//              KV head's group; the page score is the group maximum.
+// score_bbox   streams every page's k_min/k_max record once and forms the
+//              box upper bound of q.k for each query head of the KV head's
+//              group; the page score is the group maximum.  For bf16 records
+//              and groups of up to 4 heads the dot products run on the
+//              matrix cores (q split into three bf16 limbs, see below);
+//              otherwise on the vector ALUs in float64.
 // topk         per (sequence, KV head): radix select of the k-th largest
-//              score on order-preserving integer keys, then an ordered
-//              compaction (lower page id first among equal scores).
+//              score on order-preserving integer keys held in registers,
+//              then an ordered compaction (lower page id first on ties).
 // score_gauss  streams every page's (mean, M2) record once and forms the
 //              Gaussian score model (mean_Y, sd_Y, estimated max) per head.
 // tau_hat      per (sequence, query head): Newton's method on the expected
@@ -17,9 +20,11 @@
 namespace ekv {
 
 constexpr int kScoreThreads = 256;
-constexpr int kBboxPagesPerBlock = 64;
-constexpr int kGaussPagesPerBlock = 32;
+constexpr int kBboxPagesPerBlock = 64;   // 16 pages per wave
+constexpr int kGaussPagesPerBlock = 64;  // 8 lane groups per wave, 2 pages each
 constexpr int kSelThreads = 1024;
+constexpr int kTauHatThreads = 256;
+constexpr int kTauHatLds = 6144;         // pages whose (mean, sd) fit in LDS
 
 __device__ __forceinline__ int clamp_len(int L, int max_pages, int P, uint32_t* status) {
   if (L < 0 || (long long)L > (long long)max_pages * P) {
@@ -29,140 +34,228 @@ __device__ __forceinline__ int clamp_len(int L, int max_pages, int P, uint32_t* 
   return L;
 }
 
-// ---------------------------------------------------------------------------
-// Bounding-box scoring.  A page record is k_min[D] followed by k_max[D].
-// Lane `sub` of the LPP lanes that cover one record holds 16 bytes of either
-// half; its coefficients are min(q,0) for the k_min half and max(q,0) for the
-// k_max half, so the record's dot product with those coefficients is
-// sum_i max(q_i kmin_i, q_i kmax_i) (for q_i >= 0 the max takes kmax_i, for
-// q_i < 0 it takes kmin_i).  Accumulation is float64, reductions in a fixed
-// butterfly order.
-// ---------------------------------------------------------------------------
-template <int DT, int D, int G>
-__global__ __launch_bounds__(kScoreThreads) void score_bbox_kernel(SelectArgs a) {
-  using E = Elem<DT>;
-  constexpr int EPL = E::kPerVec;
-  constexpr int LPH = D / EPL;
-  constexpr int LPP = 2 * LPH;
-  static_assert(LPP <= kWave && kWave % LPP == 0, "page record must tile a wave");
-  constexpr int PPW = kWave / LPP;
-  constexpr int NW = kScoreThreads / kWave;
-  const int b = blockIdx.z, g = blockIdx.y;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int sub = lane % LPP, half = sub / LPH, dim0 = (sub % LPH) * EPL;
-  const int P = a.page_size, Hkv = a.n_kv_heads;
-  const int L = clamp_len(a.seq_lens[b], a.max_pages, P, a.status);
-  const int n_b = pages_of(L, P);
+// Physical page of logical page p of sequence b.  The table entry is read
+// before the sequence length is known (p < max_pages keeps it inside the
+// table), so the two loads travel together; the length check follows.
+__device__ __forceinline__ int page_phys_spec(const SelectArgs& a, int b, int p, int* n_b_out) {
+  const int raw = p < a.max_pages ? a.page_table[(size_t)b * a.max_pages + p] : -1;
+  const int L = clamp_len(a.seq_lens[b], a.max_pages, a.page_size, a.status);
+  const int n_b = pages_of(L, a.page_size);
+  *n_b_out = n_b;
+  if (p >= n_b) return -1;
+  if (raw < 0 || raw >= a.n_phys) {
+    set_status(a.status, EKV_DEV_BAD_PAGE);
+    return -1;
+  }
+  return raw;
+}
 
-  double c[G][EPL];
+__device__ __forceinline__ int page_phys(const SelectArgs& a, int b, int p, int n_b) {
+  if (p >= n_b) return -1;
+  const int phys = a.page_table[(size_t)b * a.max_pages + p];
+  if (phys < 0 || phys >= a.n_phys) {
+    set_status(a.status, EKV_DEV_BAD_PAGE);
+    return -1;
+  }
+  return phys;
+}
+
+// ---------------------------------------------------------------------------
+// Bounding-box score on the matrix cores.
+//
+// The box bound is linear in the record: with c_h = [min(q_h,0) | max(q_h,0)]
+// over the record [k_min | k_max], sum_i max(q_i kmin_i, q_i kmax_i) = c_h .
+// record (q_i >= 0 picks kmax_i, q_i < 0 picks kmin_i).  So the scores of 16
+// pages are one 16 x 2D by 2D x 16 product.  The A rows are 4h + l, holding
+// limb l of c_h: c = l0 + l1 + l2 in bf16 with the remainder below 2^-24 |c|,
+// and bf16 x bf16 products are exact in fp32, so the products carry the full
+// fp32 coefficient.  Each 32-wide k block is accumulated from zero by the
+// matrix core and the block sums are added in float64.
+// ---------------------------------------------------------------------------
+template <int D, int G, int NG>
+__global__ __launch_bounds__(kScoreThreads) void score_bbox_mfma_kernel(SelectArgs a) {
+  constexpr int K = 2 * D;   // record length (bf16 elements)
+  constexpr int KB = K / 32;  // k blocks
+  __shared__ u32x4_t s_a[KB][kWave];
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int Hkv = a.n_kv_heads;
+  // wave w handles page groups ng*4 + w (16 pages each) of this block
+  const int p0 = blockIdx.x * (64 * NG) + col;
+
+  // loads, in order: q for the A operand, page-table entries, page records
+  const float* qg = a.q + ((size_t)b * a.n_q_heads + (size_t)g * G) * D;
+  LimbChunks<KB> lc;
+  limb_fetch<KB, G>(lc, [&](int h, int k0, float* v) {
+    const int half = k0 >= D;
+    const float4* qv = reinterpret_cast<const float4*>(qg + (size_t)h * D + (k0 - half * D));
+    const float4 q0 = qv[0], q1 = qv[1];
+    v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w; v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
+  });
+  int phys[NG];
+  int n_b = 0;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float* qh = a.q + ((size_t)b * a.n_q_heads + (size_t)g * G + h) * D + dim0;
+  for (int ng = 0; ng < NG; ++ng) phys[ng] = page_phys_spec(a, b, p0 + (ng * 4 + w) * 16, &n_b);
+  u32x4_t bv[NG][KB];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const double qv = qh[e];
-      c[h][e] = half ? fmax(qv, 0.0) : fmin(qv, 0.0);
+  for (int ng = 0; ng < NG; ++ng) {
+    if (phys[ng] >= 0) {
+      const uint16_t* rec = reinterpret_cast<const uint16_t*>(a.k_box) + ((size_t)phys[ng] * Hkv + g) * K + 8 * grp;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) bv[ng][kb] = *reinterpret_cast<const u32x4_t*>(rec + 32 * kb);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) bv[ng][kb] = u32x4_t{0u, 0u, 0u, 0u};
     }
   }
-  float* out = a.scores + ((size_t)b * Hkv + g) * a.max_pages;
-  const int p_begin = blockIdx.x * kBboxPagesPerBlock;
-  for (int base = p_begin; base < p_begin + kBboxPagesPerBlock; base += NW * PPW) {
-    const int p = base + w * PPW + lane / LPP;
-    bool valid = p < n_b;
-    double acc[G];
+  // coefficients [min(q,0) | max(q,0)] over the record, as bf16 limbs
+  limb_build<KB, G>(s_a, lc, [](int k, float qv) { return k >= D ? fmaxf(qv, 0.f) : fminf(qv, 0.f); });
+  __syncthreads();
+
 #pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = 0.0;
-    if (valid) {
-      const int phys = a.page_table[(size_t)b * a.max_pages + p];
-      if (phys < 0 || phys >= a.n_phys) {
-        set_status(a.status, EKV_DEV_BAD_PAGE);
-        valid = false;
-      } else {
-        const char* rec = reinterpret_cast<const char*>(a.k_box) +
-                          (((size_t)phys * Hkv + g) * 2 + half) * D * E::kBytes + (size_t)dim0 * E::kBytes;
-        float f[EPL];
-        E::unpack(ldg16(rec), f);
+  for (int ng = 0; ng < NG; ++ng) {
+    double U = 0.0;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const f32x4_t c = mfma_bf16(s_a[kb][lane], bv[ng][kb], f32x4_t{0.f, 0.f, 0.f, 0.f});
+      U += ((double)c[0] + (double)c[1]) + (double)c[2];
+    }
+    // lane holds head `grp` of page `col`; the page score is the group maximum
+    double S = grp < G ? U : -INFINITY;
+    S = fmax(S, __shfl_xor(S, 16, kWave));
+    S = fmax(S, __shfl_xor(S, 32, kWave));
+    const int p = p0 + (ng * 4 + w) * 16;
+    if (grp == 0 && p < a.max_pages)
+      a.scores[((size_t)b * Hkv + g) * a.score_stride + p] = phys[ng] >= 0 ? float(S * (double)a.scale) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Bounding-box score on the vector ALUs (fp32 records or groups > 4): four
+// lanes per page record, each lane walks a quarter of the record in 16-byte
+// loads issued together; coefficients min(q,0) / max(q,0) as above, float64
+// accumulation, a two-step reduction across the four lanes.
+// ---------------------------------------------------------------------------
+template <int DT, int D, int G>
+__global__ __launch_bounds__(kScoreThreads) void score_bbox_valu_kernel(SelectArgs a) {
+  using E = Elem<DT>;
+  constexpr int EPL = E::kPerVec;
+  constexpr int VEC = 2 * D / EPL;  // 16-byte vectors per record
+  constexpr int NL = VEC / 4;       // loads per lane (four lanes per record)
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int sub = lane & 3;
+  const int Hkv = a.n_kv_heads;
+  const int p = blockIdx.x * kBboxPagesPerBlock + w * 16 + (lane >> 2);
+  int n_b;
+  const int phys = page_phys_spec(a, b, p, &n_b);
+  uint4 v[NL];
+  if (phys >= 0) {
+    const char* rec = reinterpret_cast<const char*>(a.k_box) + ((size_t)phys * Hkv + g) * 2 * D * E::kBytes;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) v[i] = ldg16(rec + 16 * (sub + 4 * i));
+  }
+  double acc[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) acc[h] = 0.0;
+  if (phys >= 0) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      float f[EPL];
+      E::unpack(v[i], f);
+      const int e0 = EPL * (sub + 4 * i);
+      const bool half = e0 >= D;
+      const int dim0 = e0 - (half ? D : 0);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float* qh = a.q + ((size_t)b * a.n_q_heads + (size_t)g * G + h) * D + dim0;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-          const double kv = f[e];
-#pragma unroll
-          for (int h = 0; h < G; ++h) acc[h] = fma(c[h][e], kv, acc[h]);
+          const double qv = qh[e];
+          acc[h] = fma(half ? fmax(qv, 0.0) : fmin(qv, 0.0), (double)f[e], acc[h]);
         }
       }
     }
+  }
 #pragma unroll
-    for (int m = 1; m < LPP; m <<= 1) {
+  for (int h = 0; h < G; ++h) {
+    acc[h] += __shfl_xor(acc[h], 1, kWave);
+    acc[h] += __shfl_xor(acc[h], 2, kWave);
+  }
+  if (sub == 0 && p < a.max_pages) {
+    double s = acc[0];
 #pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] += __shfl_xor(acc[h], m, kWave);
-    }
-    if (sub == 0 && p < a.max_pages && p < p_begin + kBboxPagesPerBlock) {
-      double s = acc[0];
-#pragma unroll
-      for (int h = 1; h < G; ++h) s = fmax(s, acc[h]);
-      out[p] = valid ? float(s * (double)a.scale) : -INFINITY;
-    }
+    for (int h = 1; h < G; ++h) s = fmax(s, acc[h]);
+    a.scores[((size_t)b * Hkv + g) * a.score_stride + p] = phys >= 0 ? float(s * (double)a.scale) : -INFINITY;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Top-k.  One block per (KV head, sequence).  Each thread owns a contiguous
-// run of pages so the final compaction writes ascending page ids.
+// Top-k.  One 1024-thread block per (KV head, sequence).  Thread t owns the
+// contiguous pages [t E, t E + E), E = ceil(n / 1024); keys stay in
+// registers when E <= 16 (up to 16384 pages), else are re-read from L2.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t block_and_u32(uint32_t v, uint32_t* red) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v &= __shfl_xor(v, m, kWave);
-  __syncthreads();
-  if (lane == 0) red[w] = v;
-  __syncthreads();
-  uint32_t r = red[0];
-  for (int i = 1; i < nw; ++i) r &= red[i];
-  return r;
-}
-__device__ __forceinline__ uint32_t block_or_u32(uint32_t v, uint32_t* red) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v |= __shfl_xor(v, m, kWave);
-  __syncthreads();
-  if (lane == 0) red[w] = v;
-  __syncthreads();
-  uint32_t r = red[0];
-  for (int i = 1; i < nw; ++i) r |= red[i];
-  return r;
-}
-
-__global__ __launch_bounds__(kSelThreads) void topk_kernel(SelectArgs a) {
-  const int g = blockIdx.x, b = blockIdx.y;
-  const int unit = b * a.n_kv_heads + g;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int P = a.page_size;
-  const int L = clamp_len(a.seq_lens[b], a.max_pages, P, a.status);
-  const int n_b = pages_of(L, P);
-  const int k_eff = min(a.top_k, n_b);
-  const float* s = a.scores + (size_t)unit * a.max_pages;
-  int32_t* out = a.sel + (size_t)unit * a.cap;
-  if (k_eff >= n_b) {
-    for (int p = tid; p < n_b; p += blockDim.x) out[p] = p;
-    if (tid == 0) a.sel_count[unit] = n_b;
-    return;
+// Visit this thread's keys in page order: from registers (E > 0, loop fully
+// unrolled so the array stays in registers) or from memory (E == 0).
+#define EKV_FOR_KEYS(BODY)                                  \
+  if (E > 0) {                                              \
+    _Pragma("unroll") for (int i = 0; i < KE; ++i) {        \
+      if (i < cnt) {                                        \
+        const uint32_t k = keys[i];                         \
+        BODY                                                \
+      }                                                     \
+    }                                                       \
+  } else {                                                  \
+    for (int i = 0; i < cnt; ++i) {                         \
+      const uint32_t k = f2key(s[e0 + i]);                  \
+      BODY                                                  \
+    }                                                       \
   }
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t red[16];
+
+template <int E>  // keys per thread held in registers (0: read from memory)
+__device__ void topk_block(const SelectArgs& a, const float* s, int n_b, int k_eff, int32_t* out, int unit) {
+  constexpr int KE = E > 0 ? E : 1;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
+  __shared__ uint32_t hist[2][256];
+  __shared__ uint32_t red[2][16];
   __shared__ int redi[17];
-  __shared__ uint32_t sh_digit, sh_above;
-  const int per = (n_b + blockDim.x - 1) / blockDim.x;
+  __shared__ uint32_t sh_digit[2], sh_above[2];
+  const int per = E > 0 ? E : (n_b + blockDim.x - 1) / blockDim.x;
   const int e0 = min(tid * per, n_b), e1 = min(e0 + per, n_b);
-
-  uint32_t kand = 0xffffffffu, kor = 0u;
-  for (int e = e0; e < e1; ++e) {
-    const uint32_t k = f2key(s[e]);
-    kand &= k;
-    kor |= k;
+  const int cnt = e1 - e0;
+  uint32_t keys[KE];
+  if (E > 0) {
+    // rows are 16-byte aligned and e0 is a multiple of 4: vector loads
+#pragma unroll
+    for (int i = 0; i < KE; i += 4) {
+      if (i + 4 <= cnt) {
+        const float4 v = *reinterpret_cast<const float4*>(s + e0 + i);
+        keys[i] = f2key(v.x); keys[(i + 1) % KE] = f2key(v.y);
+        keys[(i + 2) % KE] = f2key(v.z); keys[(i + 3) % KE] = f2key(v.w);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (i + q < KE) keys[i + q] = (i + q < cnt) ? f2key(s[e0 + i + q]) : 0u;
+      }
+    }
   }
-  kand = block_and_u32(kand, red);
-  kor = block_or_u32(kor, red);
+  // bits shared by every key (AND and OR in one reduction) and cleared histograms
+  uint32_t kand = 0xffffffffu, kor = 0u;
+  EKV_FOR_KEYS(kand &= k; kor |= k;)
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    kand &= __shfl_xor(kand, m, kWave);
+    kor |= __shfl_xor(kor, m, kWave);
+  }
+  for (int i = tid; i < 512; i += blockDim.x) (&hist[0][0])[i] = 0u;
+  if (lane == 0) { red[0][w] = kand; red[1][w] = kor; }
+  __syncthreads();
+  kand = red[0][0];
+  kor = red[1][0];
+  for (int i = 1; i < nw; ++i) { kand &= red[0][i]; kor |= red[1][i]; }
   const uint32_t diff = kand ^ kor;
-  uint32_t prefix, mask;
+  uint32_t prefix, mask = 0u;
   int rem = k_eff;
   if (diff == 0u) {
     prefix = kand;  // every score equal: the k lowest page ids
@@ -171,19 +264,16 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(SelectArgs a) {
     const int start = (top / 8) * 8;
     mask = (start + 8 >= 32) ? 0u : ~((1u << (start + 8)) - 1u);
     prefix = kand & mask;
-    for (int shift = start; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += blockDim.x) hist[i] = 0u;
-      __syncthreads();
-      for (int e = e0; e < e1; ++e) {
-        const uint32_t k = f2key(s[e]);
-        if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
-      }
+    int buf = 0;
+    for (int shift = start; shift >= 0; shift -= 8, buf ^= 1) {
+      uint32_t* hb = hist[buf];
+      EKV_FOR_KEYS(if ((k & mask) == prefix) atomicAdd(&hb[(k >> shift) & 255u], 1u);)
       __syncthreads();
       if (w == 0) {
-        const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2],
-                       c3 = hist[4 * lane + 3];
-        // suffix sum over lanes: S_l = sum of bins >= 4 l
-        uint32_t S = c0 + c1 + c2 + c3;
+        const uint32_t c0 = hb[4 * lane], c1 = hb[4 * lane + 1], c2 = hb[4 * lane + 2], c3 = hb[4 * lane + 3];
+        // this histogram is used again two passes later: clear it now
+        hb[4 * lane] = 0u; hb[4 * lane + 1] = 0u; hb[4 * lane + 2] = 0u; hb[4 * lane + 3] = 0u;
+        uint32_t S = c0 + c1 + c2 + c3;  // suffix sum over lanes: bins >= 4 lane
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
           const uint32_t t = __shfl_down(S, o, kWave);
@@ -199,120 +289,142 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(SelectArgs a) {
             if (above + cs[bin] >= (uint32_t)rem) { digit = 4 * lane + bin; break; }
             above += cs[bin];
           }
-          sh_digit = (uint32_t)digit;
-          sh_above = above;
+          sh_digit[buf] = (uint32_t)digit;
+          sh_above[buf] = above;
         }
       }
       __syncthreads();
-      prefix |= sh_digit << shift;
+      prefix |= sh_digit[buf] << shift;
       mask |= 0xffu << shift;
-      rem -= (int)sh_above;
-      __syncthreads();
+      rem -= (int)sh_above[buf];
     }
   }
-  const uint32_t kstar = prefix;  // key of the k-th largest score
-  // rem = how many pages with key == kstar to take (the lowest ids first)
-  int c_eq = 0;
-  for (int e = e0; e < e1; ++e) c_eq += (f2key(s[e]) == kstar);
+  const uint32_t kstar = prefix;  // key of the k-th largest; take `rem` of the ties
+  // one scan of (greater, equal) counts packed in 16 bits each (n <= 65535)
+  int c_gt = 0, c_eq = 0;
+  EKV_FOR_KEYS(c_gt += (k > kstar); c_eq += (k == kstar);)
   int tot;
-  const int eq_before = block_exclusive_scan(c_eq, redi, &tot);
-  int c_sel = 0, r = eq_before;
-  for (int e = e0; e < e1; ++e) {
-    const uint32_t k = f2key(s[e]);
-    if (k > kstar) ++c_sel;
-    else if (k == kstar) { if (r < rem) ++c_sel; ++r; }
+  const int packed = block_exclusive_scan(c_gt | (c_eq << 16), redi, &tot);
+  const int gt_before = packed & 0xffff, eq_before = packed >> 16;
+  int pos = gt_before + min(eq_before, rem);
+  int r = eq_before;
+  EKV_FOR_KEYS(bool take = k > kstar; if (k == kstar) { take = r < rem; ++r; } if (take) out[pos++] = e0 + i;)
+  if (tid == 0) a.sel_count[unit] = k_eff;
+}
+#undef EKV_FOR_KEYS
+
+__global__ __launch_bounds__(kSelThreads) void topk_kernel(SelectArgs a) {
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int unit = b * a.n_kv_heads + g;
+  const int tid = threadIdx.x;
+  const int P = a.page_size;
+  const int L = clamp_len(a.seq_lens[b], a.max_pages, P, a.status);
+  const int n_b = pages_of(L, P);
+  const int k_eff = min(a.top_k, n_b);
+  const float* s = a.scores + (size_t)unit * a.score_stride;
+  int32_t* out = a.sel + (size_t)unit * a.cap;
+  if (k_eff >= n_b) {
+    for (int p = tid; p < n_b; p += blockDim.x) out[p] = p;
+    if (tid == 0) a.sel_count[unit] = n_b;
+    return;
   }
-  int pos = block_exclusive_scan(c_sel, redi, &tot);
-  r = eq_before;
-  for (int e = e0; e < e1; ++e) {
-    const uint32_t k = f2key(s[e]);
-    bool take = k > kstar;
-    if (k == kstar) { take = r < rem; ++r; }
-    if (take) out[pos++] = e;
+  const int per = (n_b + kSelThreads - 1) / kSelThreads;
+  if (n_b > 65535) {  // packed 16-bit counts would overflow: the host rejects such shapes
+    set_status(a.status, EKV_DEV_OVERFLOW);
+    if (tid == 0) a.sel_count[unit] = 0;
+    return;
   }
-  if (tid == 0) a.sel_count[unit] = tot;
+  if (per <= 4) topk_block<4>(a, s, n_b, k_eff, out, unit);
+  else if (per <= 16) topk_block<16>(a, s, n_b, k_eff, out, unit);
+  else topk_block<0>(a, s, n_b, k_eff, out, unit);
 }
 
 // ---------------------------------------------------------------------------
 // Gaussian scoring.  A page record is mean[D] followed by M2[D] (float32).
-// Lanes of the mean half accumulate sum_i q_i mean_i, lanes of the M2 half
-// sum_i q_i^2 M2_i; after the in-half butterfly one exchange gives every lane
-// both sums.
+// Eight lanes per record; lane s loads the 16-byte vectors s, s+8, s+16, ...
+// so each load instruction covers 128 contiguous bytes of 8 records.  Mean
+// vectors accumulate sum_i q_i mean_i, M2 vectors sum_i q_i^2 M2_i (fp32
+// within the lane, float64 across the eight lanes).
 // ---------------------------------------------------------------------------
 template <int D, int G>
 __global__ __launch_bounds__(kScoreThreads) void score_gauss_kernel(SelectArgs a) {
-  constexpr int EPL = 4;
-  constexpr int LPH = D / EPL;
-  constexpr int LPP = 2 * LPH;
-  static_assert(LPP <= kWave && kWave % LPP == 0 && G <= LPP, "layout");
-  constexpr int PPW = kWave / LPP;
-  constexpr int NW = kScoreThreads / kWave;
+  constexpr int VEC = 2 * D / 4;  // 16-byte vectors per record
+  constexpr int NL = VEC / 8;     // loads per lane per page
+  constexpr int NLH = NL / 2;     // of them in the mean half
+  constexpr int NP = kGaussPagesPerBlock / 32;  // pages per lane group
   const int b = blockIdx.z, g = blockIdx.y;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int sub = lane % LPP, half = sub / LPH, dim0 = (sub % LPH) * EPL;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int sub = lane & 7;
   const int P = a.page_size, Hkv = a.n_kv_heads;
+  // lane group (lane / 8) of wave w takes pages base + 32 n + 8 w + lane / 8
+  const int pbase = blockIdx.x * kGaussPagesPerBlock + w * 8 + (lane >> 3);
+  int phys[NP];
+  int n_b = 0;
+#pragma unroll
+  for (int n = 0; n < NP; ++n) phys[n] = page_phys_spec(a, b, pbase + 32 * n, &n_b);
   const int L = clamp_len(a.seq_lens[b], a.max_pages, P, a.status);
-  const int n_b = pages_of(L, P);
-  const double a1s = ((double)a.alpha - 1.0) * (double)a.scale;
-
-  double c[G][EPL];
+  float4 v[NP][NL];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float* qh = a.q + ((size_t)b * a.n_q_heads + (size_t)g * G + h) * D + dim0;
+  for (int n = 0; n < NP; ++n) {
+    if (phys[n] >= 0) {
+      const float4* rec = reinterpret_cast<const float4*>(a.k_moments + ((size_t)phys[n] * Hkv + g) * 2 * D);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const double qv = qh[e];
-      c[h][e] = half ? qv * qv : qv;
+      for (int i = 0; i < NL; ++i) v[n][i] = rec[sub + 8 * i];
     }
   }
-  const int p_begin = blockIdx.x * kGaussPagesPerBlock;
-  for (int base = p_begin; base < p_begin + kGaussPagesPerBlock; base += NW * PPW) {
-    const int p = base + w * PPW + lane / LPP;
-    bool valid = p < n_b;
-    double acc[G];
+  const double a1s = ((double)a.alpha - 1.0) * (double)a.scale;
 #pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = 0.0;
-    if (valid) {
-      const int phys = a.page_table[(size_t)b * a.max_pages + p];
-      if (phys < 0 || phys >= a.n_phys) {
-        set_status(a.status, EKV_DEV_BAD_PAGE);
-        valid = false;
-      } else {
-        const float* rec = a.k_moments + (((size_t)phys * Hkv + g) * 2 + half) * D + dim0;
-        const float4 v = *reinterpret_cast<const float4*>(rec);
-        const double f[4] = {v.x, v.y, v.z, v.w};
+  for (int n = 0; n < NP; ++n) {
+    float fa[G], fb[G];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e)
+    for (int h = 0; h < G; ++h) { fa[h] = 0.f; fb[h] = 0.f; }
+    if (phys[n] >= 0) {
 #pragma unroll
-          for (int h = 0; h < G; ++h) acc[h] = fma(c[h][e], f[e], acc[h]);
+      for (int h = 0; h < G; ++h) {
+        const float* qh = a.q + ((size_t)b * a.n_q_heads + (size_t)g * G + h) * D;
+#pragma unroll
+        for (int i = 0; i < NLH; ++i) {
+          const float4 qv = *reinterpret_cast<const float4*>(qh + 4 * (sub + 8 * i));
+          const float4 mv = v[n][i], sv = v[n][i + NLH];
+          fa[h] = fmaf(qv.x, mv.x, fa[h]); fa[h] = fmaf(qv.y, mv.y, fa[h]);
+          fa[h] = fmaf(qv.z, mv.z, fa[h]); fa[h] = fmaf(qv.w, mv.w, fa[h]);
+          fb[h] = fmaf(qv.x * qv.x, sv.x, fb[h]); fb[h] = fmaf(qv.y * qv.y, sv.y, fb[h]);
+          fb[h] = fmaf(qv.z * qv.z, sv.z, fb[h]); fb[h] = fmaf(qv.w * qv.w, sv.w, fb[h]);
+        }
       }
     }
+    double A[G], Bv[G];
 #pragma unroll
-    for (int m = 1; m < LPH; m <<= 1) {
+    for (int h = 0; h < G; ++h) {
+      A[h] = fa[h];
+      Bv[h] = fb[h];
 #pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] += __shfl_xor(acc[h], m, kWave);
+      for (int m = 1; m < 8; m <<= 1) {
+        A[h] += __shfl_xor(A[h], m, kWave);
+        Bv[h] += __shfl_xor(Bv[h], m, kWave);
+      }
     }
-    double other[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) other[h] = __shfl_xor(acc[h], LPH, kWave);
-    if (sub < G && p < a.max_pages && p < p_begin + kGaussPagesPerBlock) {
-      double A = 0.0, Bv = 0.0;
+    const int p = pbase + 32 * n;
+    if (sub < G && p < a.max_pages) {
+      double As = 0.0, Bs = 0.0;
 #pragma unroll
       for (int h = 0; h < G; ++h)
-        if (h == sub) { A = half ? other[h] : acc[h]; Bv = half ? acc[h] : other[h]; }
-      const int hq = g * G + sub;
-      float4 r;
-      if (valid) {
+        if (h == sub) { As = A[h]; Bs = Bv[h]; }
+      float mu = 0.f, sd = 0.f, eh = -INFINITY, npf = 0.f;
+      if (phys[n] >= 0) {
         const int np = min(P, L - p * P);
-        const double mu = a1s * A;
-        const double var = a1s * a1s * Bv / (double)np;
-        const double sd = sqrt(fmax(var, 0.0));
-        const double ehat = mu + sd * sqrt(2.0 * log((double)np));
-        r = make_float4((float)mu, (float)sd, (float)ehat, (float)np);
-      } else {
-        r = make_float4(0.f, 0.f, -INFINITY, 0.f);
+        const double mud = a1s * As;
+        const double var = a1s * a1s * Bs / (double)np;
+        const double sdd = sqrt(fmax(var, 0.0));
+        mu = (float)mud;
+        sd = (float)sdd;
+        eh = (float)(mud + sdd * sqrt(2.0 * log((double)np)));
+        npf = (float)np;
       }
-      a.stats[((size_t)b * a.n_q_heads + hq) * a.max_pages + p] = r;
+      const size_t at = ((size_t)b * a.n_q_heads + (size_t)g * G + sub) * a.max_pages + p;
+      a.musd[at] = make_float2(mu, sd);
+      a.ehat[at] = eh;
+      if (a.stats_out) a.stats_out[at] = make_float4(mu, sd, eh, npf);
     }
   }
 }
@@ -321,22 +433,27 @@ __global__ __launch_bounds__(kScoreThreads) void score_gauss_kernel(SelectArgs a
 // tau_hat: Newton's method on F(t) = sum_p n_p E_p(t) - 1.  F is convex and
 // decreasing, and F(max mu - 1) >= 0 (the top page alone contributes at
 // least n_p * 1^e by Jensen's inequality), so Newton iterates started there
-// increase monotonically to the root.  With u = (mu - t)/sd:
+// increase monotonically to the root.  With a = mu - t, u = a / sd:
 //   exponent 1 (alpha=2):   E = a Phi(u) + sd phi(u),               E' = -Phi(u)
 //   exponent 2 (alpha=1.5): E = (a^2 + sd^2) Phi(u) + a sd phi(u),  E' = -2 (a Phi + sd phi)
-// with a = mu - t; a page with sd = 0 contributes (a)_+^e.  Pages more than
-// 10 standard deviations below t contribute less than 1e-23 sd^e and are
-// skipped.
+// and (a)_+^e when sd = 0.  A page with u < -7 contributes below
+// 2e-13 n_p sd^e; since t only grows, such pages are dropped from the live
+// list for good.  Per-page terms are evaluated in fp32 and summed in fp64
+// (the result carries about 1e-7 relative error, far inside the selector's
+// tolerance); the step stops when it falls below 2e-7 |t|.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kSelThreads) void tau_hat_kernel(SelectArgs a) {
+__global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
+  constexpr int PPT = kTauHatLds / kTauHatThreads;  // pages per thread held in registers
   const int h = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x;
   const int P = a.page_size;
   const int L = clamp_len(a.seq_lens[b], a.max_pages, P, a.status);
   const int n_b = pages_of(L, P);
   const size_t bh = (size_t)b * a.n_q_heads + h;
-  const float4* st = a.stats + bh * a.max_pages;
+  const float2* st = a.musd + bh * a.max_pages;
+  __shared__ float2 live[kTauHatLds];
   __shared__ double redd[16];
+  __shared__ int redi[17];
   if (n_b == 0) {
     if (tid == 0) {
       a.tau_hat[bh] = 0.0;
@@ -344,44 +461,94 @@ __global__ __launch_bounds__(kSelThreads) void tau_hat_kernel(SelectArgs a) {
     }
     return;
   }
-  double mu_max = -INFINITY;
-  for (int p = tid; p < n_b; p += blockDim.x) mu_max = fmax(mu_max, (double)st[p].x);
-  mu_max = block_max(mu_max, redd);
+  const float last_n = (float)(L - (n_b - 1) * P);  // tokens of the last page
+  const bool in_regs = n_b <= kTauHatLds;
+  // thread t owns pages [PPT t, PPT t + PPT): one round of loads
+  float2 ms[PPT];
+  const int p0 = PPT * tid;
+  float mu_max = -INFINITY;
+  if (in_regs) {
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      ms[i] = p0 + i < n_b ? st[p0 + i] : make_float2(-INFINITY, 0.f);
+      mu_max = fmaxf(mu_max, ms[i].x);
+    }
+  } else {
+    for (int p = tid; p < n_b; p += blockDim.x) mu_max = fmaxf(mu_max, st[p].x);
+  }
+  mu_max = block_max(mu_max, reinterpret_cast<float*>(redd));
+  const double t0 = (double)mu_max - 1.0;
+  const float t0f = (float)t0;
+  // live pages at t0 (u > -7, or zero spread and above t0), compacted in
+  // page order so the summation order is fixed
+  int n_live = 0;
+  if (in_regs) {
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i)
+      c += (p0 + i < n_b) && (ms[i].y > 0.f ? (ms[i].x - t0f) > -7.f * ms[i].y : ms[i].x > t0f);
+    int pos = block_exclusive_scan(c, redi, &n_live);
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const bool keep = (p0 + i < n_b) && (ms[i].y > 0.f ? (ms[i].x - t0f) > -7.f * ms[i].y : ms[i].x > t0f);
+      if (keep) {
+        float2 v = ms[i];
+        if (p0 + i == n_b - 1 && last_n != (float)P) v.y = -v.y - 1.f;  // mark the partial page
+        live[pos++] = v;
+      }
+    }
+  }
+  __syncthreads();
   const bool quad = a.alpha == 1.5f;
-  const double kInvSqrt2 = 0.70710678118654752440, kInvSqrt2Pi = 0.39894228040143267794;
-  double t = mu_max - 1.0;
-  for (int it = 0; it < 100; ++it) {
+  const float kInvSqrt2 = 0.70710678118654752440f, kInvSqrt2Pi = 0.39894228040143267794f;
+  double t = t0;
+  for (int it = 0; it < 64; ++it) {
+    const float tf = (float)t;
     double F = 0.0, dF = 0.0;
-    for (int p = tid; p < n_b; p += blockDim.x) {
-      const float4 s = st[p];
-      const double mu = s.x, sd = s.y, n = s.w;
-      const double am = mu - t;
-      if (sd <= 0.0) {
-        if (am > 0.0) {
-          if (quad) { F += n * am * am; dF -= n * 2.0 * am; }
-          else { F += n * am; dF -= n; }
-        }
-        continue;
-      }
-      const double u = am / sd;
-      if (u < -10.0) continue;
-      const double Phi = 0.5 * erfc(-u * kInvSqrt2);
-      const double phi = exp(-0.5 * u * u) * kInvSqrt2Pi;
-      const double e1 = am * Phi + sd * phi;  // E[(Y - t)_+]
-      if (quad) {
-        F += n * ((am * am + sd * sd) * Phi + am * sd * phi);
-        dF -= n * 2.0 * e1;
+    const int nloop = in_regs ? n_live : n_b;
+    for (int i = tid; i < nloop; i += blockDim.x) {
+      float mu, sd, n;
+      if (in_regs) {
+        const float2 v = live[i];
+        mu = v.x;
+        sd = v.y;
+        n = (float)P;
+        if (sd < 0.f) { sd = -sd - 1.f; n = last_n; }
       } else {
-        F += n * e1;
-        dF -= n * Phi;
+        const float2 v = st[i];
+        mu = v.x;
+        sd = v.y;
+        n = i == n_b - 1 ? last_n : (float)P;
       }
+      const float am = mu - tf;
+      float e, de;
+      if (sd <= 0.f) {
+        const float pos = fmaxf(am, 0.f);
+        e = quad ? pos * pos : pos;
+        de = quad ? -2.f * pos : (am > 0.f ? -1.f : 0.f);
+      } else {
+        const float u = am / sd;
+        if (u < -7.f) continue;
+        const float Phi = 0.5f * erfcf(-u * kInvSqrt2);
+        const float phi = expf(-0.5f * u * u) * kInvSqrt2Pi;
+        const float e1 = am * Phi + sd * phi;  // E[(Y - t)_+]
+        if (quad) {
+          e = (am * am + sd * sd) * Phi + am * sd * phi;
+          de = -2.f * e1;
+        } else {
+          e = e1;
+          de = -Phi;
+        }
+      }
+      F += (double)n * (double)e;
+      dF += (double)n * (double)de;
     }
     F = block_sum(F, redd);
     dF = block_sum(dF, redd);
     const double step = (F - 1.0) / (-dF);
     if (!(step > 0.0)) break;
     t += step;
-    if (step <= 1e-14 * fmax(1.0, fabs(t))) break;
+    if (step <= 2e-7 * fmax(1.0, fabs(t))) break;
   }
   if (tid == 0) {
     a.tau_hat[bh] = t;
@@ -392,10 +559,12 @@ __global__ __launch_bounds__(kSelThreads) void tau_hat_kernel(SelectArgs a) {
 // ---------------------------------------------------------------------------
 // Keep pages whose estimated maximum beats tau_hat - delta for some head of
 // the group; ordered compaction; at least one page (the best margin, lowest
-// id on ties).
+// id on ties).  Thread t owns a contiguous run of pages whose estimates are
+// all read in one round; one block scan places the kept pages.
 // ---------------------------------------------------------------------------
 template <int G>
 __global__ __launch_bounds__(kSelThreads) void gauss_keep_kernel(SelectArgs a) {
+  constexpr int PPT = 8;  // pages per thread held in registers (n_b <= 8192)
   const int g = blockIdx.x, b = blockIdx.y;
   const int unit = b * a.n_kv_heads + g;
   const int tid = threadIdx.x;
@@ -411,36 +580,59 @@ __global__ __launch_bounds__(kSelThreads) void gauss_keep_kernel(SelectArgs a) {
     return;
   }
   double tau[G];
-  const float4* st[G];
+  const float* eh[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const size_t bh = (size_t)b * a.n_q_heads + (size_t)g * G + h;
     tau[h] = a.tau_hat[bh];
-    st[h] = a.stats + bh * a.max_pages;
+    eh[h] = a.ehat + bh * a.max_pages;
   }
   const double ndelta = -(double)a.delta;
-  const int per = (n_b + blockDim.x - 1) / blockDim.x;
-  const int e0 = min(tid * per, n_b), e1 = min(e0 + per, n_b);
-  auto margin = [&](int p) {
-    double m = -INFINITY;
-#pragma unroll
-    for (int h = 0; h < G; ++h) m = fmax(m, (double)st[h][p].z - tau[h]);
-    return m;
-  };
-  int c = 0;
   double best = -INFINITY;
   int best_p = 0x7fffffff;
-  for (int p = e0; p < e1; ++p) {
-    const double m = margin(p);
-    if (m > ndelta) ++c;
-    if (m > best) { best = m; best_p = p; }
+  int run = 0;
+  const int per = (n_b + blockDim.x - 1) / blockDim.x;
+  if (per <= PPT) {
+    const int p0 = per * tid;
+    float e[G][PPT];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < PPT; ++i) e[h][i] = (i < per && p0 + i < n_b) ? eh[h][p0 + i] : -INFINITY;
+    bool keep[PPT];
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      double mg = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < G; ++h) mg = fmax(mg, (double)e[h][i] - tau[h]);
+      keep[i] = i < per && p0 + i < n_b && mg > ndelta;
+      c += keep[i];
+      if (i < per && p0 + i < n_b && mg > best) { best = mg; best_p = p0 + i; }
+    }
+    int pos = block_exclusive_scan(c, redi, &run);
+#pragma unroll
+    for (int i = 0; i < PPT; ++i)
+      if (keep[i]) out[pos++] = p0 + i;
+  } else {
+    for (int p0 = 0; p0 < n_b; p0 += blockDim.x) {
+      const int p = p0 + tid;
+      bool keep = false;
+      if (p < n_b) {
+        double mg = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < G; ++h) mg = fmax(mg, (double)eh[h][p] - tau[h]);
+        keep = mg > ndelta;
+        if (mg > best) { best = mg; best_p = p; }
+      }
+      int tot;
+      const int pos = run + block_exclusive_scan(keep ? 1 : 0, redi, &tot);
+      if (keep) out[pos] = p;
+      run += tot;
+    }
   }
-  int tot;
-  int pos = block_exclusive_scan(c, redi, &tot);
-  if (tot > 0) {
-    for (int p = e0; p < e1; ++p)
-      if (margin(p) > ndelta) out[pos++] = p;
-    if (tid == 0) a.sel_count[unit] = tot;
+  if (run > 0) {
+    if (tid == 0) a.sel_count[unit] = run;
     return;
   }
   // floor: the single best page
@@ -463,22 +655,40 @@ __global__ __launch_bounds__(kSelThreads) void gauss_keep_kernel(SelectArgs a) {
 // Launchers
 // ---------------------------------------------------------------------------
 template <int DT, int D>
-static hipError_t bbox_dispatch_g(const SelectArgs& a, dim3 grid, hipStream_t s) {
+static hipError_t bbox_dispatch(const SelectArgs& a, hipStream_t s) {
+  const dim3 blk(kScoreThreads);
+  if (DT == EKV_BF16 && a.group <= 4) {
+    // four 16-page groups per wave when that still leaves >= 512 blocks
+    const long long recs = (long long)a.max_pages * a.n_kv_heads * a.batch;
+    const bool fat = recs >= 512LL * 256;
+    const int ppb = fat ? 256 : 64;
+    const dim3 grid((a.max_pages + ppb - 1) / ppb, a.n_kv_heads, a.batch);
+#define EKV_BBOX(GG)                                                                                 \
+  if (fat) hipLaunchKernelGGL((score_bbox_mfma_kernel<D, GG, 4>), grid, blk, 0, s, a);              \
+  else hipLaunchKernelGGL((score_bbox_mfma_kernel<D, GG, 1>), grid, blk, 0, s, a);
+    switch (a.group) {
+      case 1: EKV_BBOX(1); break;
+      case 2: EKV_BBOX(2); break;
+      default: EKV_BBOX(4); break;
+    }
+#undef EKV_BBOX
+    return hipGetLastError();
+  }
+  const dim3 grid((a.max_pages + kBboxPagesPerBlock - 1) / kBboxPagesPerBlock, a.n_kv_heads, a.batch);
   switch (a.group) {
-    case 1: hipLaunchKernelGGL((score_bbox_kernel<DT, D, 1>), grid, dim3(kScoreThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((score_bbox_kernel<DT, D, 2>), grid, dim3(kScoreThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((score_bbox_kernel<DT, D, 4>), grid, dim3(kScoreThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((score_bbox_kernel<DT, D, 8>), grid, dim3(kScoreThreads), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((score_bbox_valu_kernel<DT, D, 1>), grid, blk, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((score_bbox_valu_kernel<DT, D, 2>), grid, blk, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((score_bbox_valu_kernel<DT, D, 4>), grid, blk, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((score_bbox_valu_kernel<DT, D, 8>), grid, blk, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_score_bbox(const SelectArgs& a, hipStream_t s) {
-  dim3 grid((a.max_pages + kBboxPagesPerBlock - 1) / kBboxPagesPerBlock, a.n_kv_heads, a.batch);
   if (a.kv_dtype == EKV_BF16)
-    return a.head_dim == 128 ? bbox_dispatch_g<EKV_BF16, 128>(a, grid, s) : bbox_dispatch_g<EKV_BF16, 64>(a, grid, s);
-  return a.head_dim == 128 ? bbox_dispatch_g<EKV_F32, 128>(a, grid, s) : bbox_dispatch_g<EKV_F32, 64>(a, grid, s);
+    return a.head_dim == 128 ? bbox_dispatch<EKV_BF16, 128>(a, s) : bbox_dispatch<EKV_BF16, 64>(a, s);
+  return a.head_dim == 128 ? bbox_dispatch<EKV_F32, 128>(a, s) : bbox_dispatch<EKV_F32, 64>(a, s);
 }
 
 hipError_t launch_topk(const SelectArgs& a, hipStream_t s) {
@@ -504,7 +714,7 @@ hipError_t launch_score_gauss(const SelectArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_tau_hat(const SelectArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(tau_hat_kernel, dim3(a.n_q_heads, a.batch), dim3(kSelThreads), 0, s, a);
+  hipLaunchKernelGGL(tau_hat_kernel, dim3(a.n_q_heads, a.batch), dim3(kTauHatThreads), 0, s, a);
   return hipGetLastError();
 }
 
