@@ -166,6 +166,7 @@ static ekv_status prepare_select(const ekv_cache* cache, const ekv_seqs* seqs, c
   a->ehat = at<float>(workspace, L->ehat);
   a->stats_out = nullptr;
   a->tau_hat = at<double>(workspace, L->tau_hat);
+  a->done = at<uint32_t>(workspace, L->sel_done);
   a->status = at<uint32_t>(workspace, L->status);
   return EKV_OK;
 }
@@ -190,8 +191,7 @@ ekv_status ekv_select_pages(const ekv_cache* cache, const ekv_seqs* seqs, const 
     return hip_status(ekv::launch_topk(a, s), "topk launch");
   }
   if ((st = hip_status(ekv::launch_score_gauss(a, s), "score_gauss launch")) != EKV_OK) return st;
-  if ((st = hip_status(ekv::launch_tau_hat(a, s), "tau_hat launch")) != EKV_OK) return st;
-  return hip_status(ekv::launch_gauss_keep(a, s), "gauss_keep launch");
+  return hip_status(ekv::launch_tau_hat(a, s), "tau_hat launch");
 }
 
 ekv_status ekv_score_pages(const ekv_cache* cache, const ekv_seqs* seqs, const float* q, int32_t n_q_heads,

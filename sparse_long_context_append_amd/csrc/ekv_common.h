@@ -20,6 +20,8 @@ constexpr int kItemTokens = 64;  // tokens of one decode work item
 
 struct Layout {
   size_t status;    // u32 device status bits
+  size_t sel_done;  // u32 [B*Hkv] per-unit arrival counters of the selection stage (zero between calls)
+  size_t dec_done;  // u32 [B*Hkv] per-unit arrival counters of the decode stage (zero between calls)
   size_t scores;    // f32 [B*Hkv][score_stride] bounding-box page scores
   size_t musd;      // float2 [B*Hq*max_pages] Gaussian page score (mean_Y, sd_Y)
   size_t ehat;      // f32 [B*Hq*max_pages] estimated page maximum
@@ -47,6 +49,8 @@ inline Layout make_layout(int B, int Hkv, int Hq, int max_pages, int P) {
   L.max_items = (size_t(max_pages) * P + kItemTokens - 1) / kItemTokens;
   const size_t tok = L.max_items * kItemTokens;
   L.status = off;   off = align256(off + 4);
+  L.sel_done = off; off = align256(off + 4 * size_t(B) * Hkv);
+  L.dec_done = off; off = align256(off + 4 * size_t(B) * Hkv);
   L.scores = off;   off = align256(off + 4 * size_t(B) * Hkv * score_stride(max_pages));
   L.musd = off;     off = align256(off + 8 * bh * max_pages);
   L.ehat = off;     off = align256(off + 4 * bh * max_pages);

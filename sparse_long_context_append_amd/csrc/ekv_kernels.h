@@ -42,6 +42,7 @@ struct SelectArgs {
   float* ehat;         // estimated page maximum [B*Hq*max_pages]
   float4* stats_out;   // optional (mean_Y, sd_Y, e_hat, n_p) copy for diagnostics
   double* tau_hat;     // [B*Hq]
+  uint32_t* done;      // [B*Hkv] arrival counters, zero between calls
   uint32_t* status;
 };
 
@@ -80,7 +81,6 @@ hipError_t launch_score_bbox(const SelectArgs& a, hipStream_t s);
 hipError_t launch_topk(const SelectArgs& a, hipStream_t s);
 hipError_t launch_score_gauss(const SelectArgs& a, hipStream_t s);
 hipError_t launch_tau_hat(const SelectArgs& a, hipStream_t s);
-hipError_t launch_gauss_keep(const SelectArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int target_blocks, hipStream_t s);
 
 }  // namespace ekv

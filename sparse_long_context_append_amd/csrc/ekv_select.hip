@@ -23,8 +23,9 @@ constexpr int kScoreThreads = 256;
 constexpr int kBboxPagesPerBlock = 64;   // 16 pages per wave
 constexpr int kGaussPagesPerBlock = 64;  // 8 lane groups per wave, 2 pages each
 constexpr int kSelThreads = 1024;
-constexpr int kTauHatThreads = 256;
-constexpr int kTauHatLds = 6144;         // pages whose (mean, sd) fit in LDS
+constexpr int kTauHatThreads = 1024;
+constexpr int kTauHatPPT = 8;            // pages per thread held in registers (n_b <= 8192)
+constexpr int kTauHatLive = 4096;        // pages alive at the start point kept in LDS
 
 __device__ __forceinline__ int clamp_len(int L, int max_pages, int P, uint32_t* status) {
   if (L < 0 || (long long)L > (long long)max_pages * P) {
@@ -430,142 +431,70 @@ __global__ __launch_bounds__(kScoreThreads) void score_gauss_kernel(SelectArgs a
 }
 
 // ---------------------------------------------------------------------------
-// tau_hat: Newton's method on F(t) = sum_p n_p E_p(t) - 1.  F is convex and
-// decreasing, and F(max mu - 1) >= 0 (the top page alone contributes at
-// least n_p * 1^e by Jensen's inequality), so Newton iterates started there
-// increase monotonically to the root.  With a = mu - t, u = a / sd:
-//   exponent 1 (alpha=2):   E = a Phi(u) + sd phi(u),               E' = -Phi(u)
-//   exponent 2 (alpha=1.5): E = (a^2 + sd^2) Phi(u) + a sd phi(u),  E' = -2 (a Phi + sd phi)
-// and (a)_+^e when sd = 0.  A page with u < -7 contributes below
-// 2e-13 n_p sd^e; since t only grows, such pages are dropped from the live
-// list for good.  Per-page terms are evaluated in fp32 and summed in fp64
-// (the result carries about 1e-7 relative error, far inside the selector's
-// tolerance); the step stops when it falls below 2e-7 |t|.
+// tau_hat solves F(t) = sum_p n_p E_p(t) = 1 for one (sequence, query head),
+// where E_p(t) is the expected value of (Y - t)_+^e for the page's Gaussian
+// score Y ~ N(mu, sd^2) and e = 1/(alpha-1).  With a = mu - t, u = a / sd:
+//   e = 1 (alpha=2):   E = a Phi(u) + sd phi(u),               E' = -Phi(u)
+//   e = 2 (alpha=1.5): E = (a^2 + sd^2) Phi(u) + a sd phi(u),  E' = -2 (a Phi + sd phi)
+// and E = (a)_+^e when sd = 0.  F is continuous and strictly decreasing
+// where positive, so the root is unique.
+//
+// Start: E_p(t) >= (mu_p - t)_+^e (Jensen), so every page alone bounds the
+// root from below by mu_p - n_p^{-(alpha-1)}; the largest of these is t0.
+// t only matters above t0, where a page with u < -7 contributes below
+// 2e-13 n_p sd^e: such pages are dropped once, at t0.  The iteration is
+// Newton's method on log F (exact in one step for an exponential tail, and
+// quadratic near the root), kept inside a bracket [lo, hi] with F(lo) >= 1 >
+// F(hi) and replaced by bisection whenever it would leave it.  Per-page terms
+// are evaluated in fp32 and summed in fp64; the step stops below
+// 2e-7 max(1, |t|).
+//
+// The last block of a (sequence, KV head) to finish (arrival counter) keeps
+// the pages whose estimated maximum beats tau_hat - delta for some head of
+// the group, in ascending order, at least one page (the best margin, lowest
+// id on ties).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
-  constexpr int PPT = kTauHatLds / kTauHatThreads;  // pages per thread held in registers
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int P = a.page_size;
-  const int L = clamp_len(a.seq_lens[b], a.max_pages, P, a.status);
-  const int n_b = pages_of(L, P);
-  const size_t bh = (size_t)b * a.n_q_heads + h;
-  const float2* st = a.musd + bh * a.max_pages;
-  __shared__ float2 live[kTauHatLds];
-  __shared__ double redd[16];
-  __shared__ int redi[17];
-  if (n_b == 0) {
-    if (tid == 0) {
-      a.tau_hat[bh] = 0.0;
-      if (a.tau_hat_out) a.tau_hat_out[bh] = 0.f;
-    }
+__device__ __forceinline__ void gauss_mass(float mu, float sd, float tf, bool quad, float& e, float& de) {
+  const float kInvSqrt2 = 0.70710678118654752440f, kInvSqrt2Pi = 0.39894228040143267794f;
+  const float am = mu - tf;
+  if (sd <= 0.f) {
+    const float pos = fmaxf(am, 0.f);
+    e = quad ? pos * pos : pos;
+    de = quad ? -2.f * pos : (am > 0.f ? -1.f : 0.f);
     return;
   }
-  const float last_n = (float)(L - (n_b - 1) * P);  // tokens of the last page
-  const bool in_regs = n_b <= kTauHatLds;
-  // thread t owns pages [PPT t, PPT t + PPT): one round of loads
-  float2 ms[PPT];
-  const int p0 = PPT * tid;
-  float mu_max = -INFINITY;
-  if (in_regs) {
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      ms[i] = p0 + i < n_b ? st[p0 + i] : make_float2(-INFINITY, 0.f);
-      mu_max = fmaxf(mu_max, ms[i].x);
-    }
+  const float u = am / sd;
+  if (u < -7.f) {
+    e = 0.f;
+    de = 0.f;
+    return;
+  }
+  const float Phi = 0.5f * erfcf(-u * kInvSqrt2);
+  const float phi = expf(-0.5f * u * u) * kInvSqrt2Pi;
+  const float e1 = am * Phi + sd * phi;
+  if (quad) {
+    e = (am * am + sd * sd) * Phi + am * sd * phi;
+    de = -2.f * e1;
   } else {
-    for (int p = tid; p < n_b; p += blockDim.x) mu_max = fmaxf(mu_max, st[p].x);
-  }
-  mu_max = block_max(mu_max, reinterpret_cast<float*>(redd));
-  const double t0 = (double)mu_max - 1.0;
-  const float t0f = (float)t0;
-  // live pages at t0 (u > -7, or zero spread and above t0), compacted in
-  // page order so the summation order is fixed
-  int n_live = 0;
-  if (in_regs) {
-    int c = 0;
-#pragma unroll
-    for (int i = 0; i < PPT; ++i)
-      c += (p0 + i < n_b) && (ms[i].y > 0.f ? (ms[i].x - t0f) > -7.f * ms[i].y : ms[i].x > t0f);
-    int pos = block_exclusive_scan(c, redi, &n_live);
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const bool keep = (p0 + i < n_b) && (ms[i].y > 0.f ? (ms[i].x - t0f) > -7.f * ms[i].y : ms[i].x > t0f);
-      if (keep) {
-        float2 v = ms[i];
-        if (p0 + i == n_b - 1 && last_n != (float)P) v.y = -v.y - 1.f;  // mark the partial page
-        live[pos++] = v;
-      }
-    }
-  }
-  __syncthreads();
-  const bool quad = a.alpha == 1.5f;
-  const float kInvSqrt2 = 0.70710678118654752440f, kInvSqrt2Pi = 0.39894228040143267794f;
-  double t = t0;
-  for (int it = 0; it < 64; ++it) {
-    const float tf = (float)t;
-    double F = 0.0, dF = 0.0;
-    const int nloop = in_regs ? n_live : n_b;
-    for (int i = tid; i < nloop; i += blockDim.x) {
-      float mu, sd, n;
-      if (in_regs) {
-        const float2 v = live[i];
-        mu = v.x;
-        sd = v.y;
-        n = (float)P;
-        if (sd < 0.f) { sd = -sd - 1.f; n = last_n; }
-      } else {
-        const float2 v = st[i];
-        mu = v.x;
-        sd = v.y;
-        n = i == n_b - 1 ? last_n : (float)P;
-      }
-      const float am = mu - tf;
-      float e, de;
-      if (sd <= 0.f) {
-        const float pos = fmaxf(am, 0.f);
-        e = quad ? pos * pos : pos;
-        de = quad ? -2.f * pos : (am > 0.f ? -1.f : 0.f);
-      } else {
-        const float u = am / sd;
-        if (u < -7.f) continue;
-        const float Phi = 0.5f * erfcf(-u * kInvSqrt2);
-        const float phi = expf(-0.5f * u * u) * kInvSqrt2Pi;
-        const float e1 = am * Phi + sd * phi;  // E[(Y - t)_+]
-        if (quad) {
-          e = (am * am + sd * sd) * Phi + am * sd * phi;
-          de = -2.f * e1;
-        } else {
-          e = e1;
-          de = -Phi;
-        }
-      }
-      F += (double)n * (double)e;
-      dF += (double)n * (double)de;
-    }
-    F = block_sum(F, redd);
-    dF = block_sum(dF, redd);
-    const double step = (F - 1.0) / (-dF);
-    if (!(step > 0.0)) break;
-    t += step;
-    if (step <= 2e-7 * fmax(1.0, fabs(t))) break;
-  }
-  if (tid == 0) {
-    a.tau_hat[bh] = t;
-    if (a.tau_hat_out) a.tau_hat_out[bh] = (float)t;
+    e = e1;
+    de = -Phi;
   }
 }
 
-// ---------------------------------------------------------------------------
-// Keep pages whose estimated maximum beats tau_hat - delta for some head of
-// the group; ordered compaction; at least one page (the best margin, lowest
-// id on ties).  Thread t owns a contiguous run of pages whose estimates are
-// all read in one round; one block scan places the kept pages.
-// ---------------------------------------------------------------------------
+// live-list entries carry the partial last page as sd -> -sd - 1
+__device__ __forceinline__ void live_term(float2 v, float P, float last_n, float tf, bool quad, double& F,
+                                          double& dF) {
+  float n = P, sd = v.y;
+  if (sd < 0.f) { sd = -sd - 1.f; n = last_n; }
+  float e, de;
+  gauss_mass(v.x, sd, tf, quad, e, de);
+  F += (double)n * (double)e;
+  dF += (double)n * (double)de;
+}
+
 template <int G>
-__global__ __launch_bounds__(kSelThreads) void gauss_keep_kernel(SelectArgs a) {
-  constexpr int PPT = 8;  // pages per thread held in registers (n_b <= 8192)
-  const int g = blockIdx.x, b = blockIdx.y;
+__device__ void gauss_keep_unit(const SelectArgs& a, int b, int g) {
+  constexpr int PPT = G >= 8 ? 4 : 8;  // pages per thread held in registers
   const int unit = b * a.n_kv_heads + g;
   const int tid = threadIdx.x;
   const int P = a.page_size;
@@ -584,7 +513,7 @@ __global__ __launch_bounds__(kSelThreads) void gauss_keep_kernel(SelectArgs a) {
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const size_t bh = (size_t)b * a.n_q_heads + (size_t)g * G + h;
-    tau[h] = a.tau_hat[bh];
+    tau[h] = __hip_atomic_load(a.tau_hat + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     eh[h] = a.ehat + bh * a.max_pages;
   }
   const double ndelta = -(double)a.delta;
@@ -651,6 +580,134 @@ __global__ __launch_bounds__(kSelThreads) void gauss_keep_kernel(SelectArgs a) {
   }
 }
 
+template <int G>
+__global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
+  constexpr int PPT = kTauHatPPT;
+  constexpr int NW = kTauHatThreads / kWave;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int g = h / G, unit = b * a.n_kv_heads + g;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int P = a.page_size;
+  const int L = clamp_len(a.seq_lens[b], a.max_pages, P, a.status);
+  const int n_b = pages_of(L, P);
+  const size_t bh = (size_t)b * a.n_q_heads + h;
+  const float2* st = a.musd + bh * a.max_pages;
+  __shared__ float2 live[kTauHatLive];
+  __shared__ double part[2][NW][2];
+  __shared__ double redd[16];
+  __shared__ int redi[17];
+  __shared__ int s_last;
+  double t = 0.0;
+  if (n_b > 0) {
+    const bool quad = a.alpha == 1.5f;
+    const float Pf = (float)P;
+    const float last_n = (float)(L - (n_b - 1) * P);  // tokens of the last page
+    const bool in_regs = n_b <= PPT * kTauHatThreads;
+    // thread t owns pages t, t + 1024, ...: one round of coalesced loads
+    float2 ms[PPT];
+    double lb = -INFINITY;
+    auto bound = [&](float2 v, int p) {
+      const double n = p == n_b - 1 ? (double)last_n : (double)P;
+      return (double)v.x - (quad ? 1.0 / sqrt(n) : 1.0 / n);
+    };
+    if (in_regs) {
+#pragma unroll
+      for (int i = 0; i < PPT; ++i) {
+        const int p = i * kTauHatThreads + tid;
+        ms[i] = p < n_b ? st[p] : make_float2(-INFINITY, 0.f);
+        if (p < n_b) lb = fmax(lb, bound(ms[i], p));
+      }
+    } else {
+      for (int p = tid; p < n_b; p += kTauHatThreads) lb = fmax(lb, bound(st[p], p));
+    }
+    const double t0 = block_max(lb, redd);
+    const float t0f = (float)t0;
+    auto alive = [&](float2 v) { return v.y > 0.f ? (v.x - t0f) > -7.f * v.y : v.x > t0f; };
+    // live pages at t0, compacted (thread-major order, fixed for given inputs)
+    int n_live = 0;
+    bool use_live = false;
+    if (in_regs) {
+      int c = 0;
+#pragma unroll
+      for (int i = 0; i < PPT; ++i) c += (i * kTauHatThreads + tid < n_b) && alive(ms[i]);
+      int pos = block_exclusive_scan(c, redi, &n_live);
+      use_live = n_live <= kTauHatLive;
+      if (use_live) {
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+          const int p = i * kTauHatThreads + tid;
+          if (p < n_b && alive(ms[i])) {
+            float2 v = ms[i];
+            if (p == n_b - 1 && last_n != Pf) v.y = -v.y - 1.f;
+            live[pos++] = v;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    double lo = -INFINITY, hi = INFINITY;
+    t = t0;
+    for (int it = 0; it < 200; ++it) {
+      const float tf = (float)t;
+      double F = 0.0, dF = 0.0;
+      if (use_live) {
+        for (int i = tid; i < n_live; i += kTauHatThreads) live_term(live[i], Pf, last_n, tf, quad, F, dF);
+      } else {
+        for (int p = tid; p < n_b; p += kTauHatThreads) {
+          const float2 v = st[p];
+          float e, de;
+          gauss_mass(v.x, v.y, tf, quad, e, de);
+          const double n = p == n_b - 1 ? (double)last_n : (double)P;
+          F += n * (double)e;
+          dF += n * (double)de;
+        }
+      }
+      // one barrier per iteration: partials alternate between two buffers
+      F = wave_sum(F);
+      dF = wave_sum(dF);
+      if (lane == 0) {
+        part[it & 1][w][0] = F;
+        part[it & 1][w][1] = dF;
+      }
+      __syncthreads();
+      F = 0.0;
+      dF = 0.0;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        F += part[it & 1][i][0];
+        dF += part[it & 1][i][1];
+      }
+      if (F == 1.0) break;
+      if (F > 1.0) lo = t; else hi = t;
+      const double tol = 2e-7 * fmax(1.0, fabs(t));
+      const bool newton = F > 0.0 && dF < 0.0;
+      double cand = newton ? t - F * log(F) / dF : t;
+      if (newton && fabs(cand - t) <= tol) {
+        t = cand;
+        break;
+      }
+      if (!(cand > lo && cand < hi)) {
+        if (lo > -INFINITY && hi < INFINITY) cand = 0.5 * (lo + hi);
+        else if (hi < INFINITY) cand = hi - fmax(1.0, fabs(hi));
+        else cand = lo + fmax(1.0, fabs(lo));
+      }
+      t = cand;
+      if (hi - lo <= tol) break;
+    }
+  }
+  if (tid == 0) {
+    a.tau_hat[bh] = t;
+    if (a.tau_hat_out) a.tau_hat_out[bh] = (float)t;
+    __threadfence();
+    s_last = atomicAdd(a.done + unit, 1u) == (uint32_t)(G - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  if (tid == 0) a.done[unit] = 0u;  // ready for the next call
+  gauss_keep_unit<G>(a, b, g);
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -714,17 +771,12 @@ hipError_t launch_score_gauss(const SelectArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_tau_hat(const SelectArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(tau_hat_kernel, dim3(a.n_q_heads, a.batch), dim3(kTauHatThreads), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_gauss_keep(const SelectArgs& a, hipStream_t s) {
-  dim3 grid(a.n_kv_heads, a.batch), block(kSelThreads);
+  const dim3 grid(a.n_q_heads, a.batch), block(kTauHatThreads);
   switch (a.group) {
-    case 1: hipLaunchKernelGGL(gauss_keep_kernel<1>, grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL(gauss_keep_kernel<2>, grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL(gauss_keep_kernel<4>, grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL(gauss_keep_kernel<8>, grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL(tau_hat_kernel<1>, grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL(tau_hat_kernel<2>, grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL(tau_hat_kernel<4>, grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL(tau_hat_kernel<8>, grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

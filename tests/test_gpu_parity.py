@@ -110,6 +110,24 @@ def test_c3_reduced_gauss_alpha2():
     check_step(spec, run_step(sess, spec, q, sparse=False), q, all_units(spec), sparse=False, kv_cache=cache)
 
 
+@pytest.mark.parametrize("hkv", [8, 4, 1])
+def test_gauss_group_sizes(hkv):
+    """Gaussian selection and decode with query groups of 1, 2 and 8 heads."""
+    spec = W.make_spec("c3", batch=2, context=2048 + 5, n_q_heads=8, n_kv_heads=hkv)
+    sess, _ = _session(spec)
+    q = W.queries(spec)
+    check_step(spec, run_step(sess, spec, q), q, all_units(spec))
+
+
+def test_gauss_more_pages_than_register_tiles():
+    """8199 pages of 16 tokens: the threshold estimate streams the page
+    statistics from memory and the keep step takes its looped path."""
+    spec = W.make_spec("c3", batch=1, context=8198 * 16 + 7, page_size=16, n_q_heads=4, n_kv_heads=1)
+    sess, _ = _session(spec)
+    q = W.queries(spec)
+    check_step(spec, run_step(sess, spec, q), q, all_units(spec))
+
+
 def test_c4_reduced():
     spec = W.make_spec("c4", context=65536 + 33, n_q_heads=8, n_kv_heads=2, n_needles=64, top_k=21)
     sess, _ = _session(spec)
