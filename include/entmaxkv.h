@@ -196,7 +196,8 @@ ekv_status ekv_select_pages(const ekv_cache* cache, const ekv_seqs* seqs, const 
  *   alpha      > 1 (exact threshold for 1.5 and 2, Newton-converged otherwise)
  *   sel, sel_count, cap  as produced by ekv_select_pages (sel_count entries
  *              are clamped to [0, cap] and to the sequence's page count)
- *   out        [batch][n_q_heads][head_dim] float32: sum_j p_j v_j
+ *   out        [batch][n_q_heads][head_dim] float32, 16-byte aligned:
+ *              sum_j p_j v_j
  *   tau        optional [batch][n_q_heads] float32: the threshold (x domain)
  *   support_count optional [batch][n_q_heads] int32: tokens with p_j > 0
  *   psum       optional [batch][n_q_heads] float32: sum_j p_j

@@ -222,7 +222,7 @@ ekv_status ekv_entmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const
   if ((st = check_seqs(cache, seqs)) != EKV_OK) return st;
   if ((st = check_heads(cache, n_q_heads, &G)) != EKV_OK) return st;
   if (!q || !aligned16(q)) return fail(EKV_ERR_INVALID_ARG, "q is NULL or not 16-byte aligned");
-  if (!out) return fail(EKV_ERR_INVALID_ARG, "out is NULL");
+  if (!out || !aligned16(out)) return fail(EKV_ERR_INVALID_ARG, "out is NULL or not 16-byte aligned");
   if (!(alpha > 1.f) || !isfinite(alpha)) return fail(EKV_ERR_INVALID_ARG, "alpha must be finite and > 1");
   if (!(scale > 0.f) || !isfinite(scale)) return fail(EKV_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (sel && (!sel_count || cap < 1)) return fail(EKV_ERR_INVALID_ARG, "sel needs sel_count and cap >= 1");

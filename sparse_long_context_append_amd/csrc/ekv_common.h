@@ -21,7 +21,6 @@ constexpr int kItemTokens = 64;  // tokens of one decode work item
 struct Layout {
   size_t status;    // u32 device status bits
   size_t sel_done;  // u32 [B*Hkv] per-unit arrival counters of the selection stage (zero between calls)
-  size_t dec_done;  // u32 [B*Hkv] per-unit arrival counters of the decode stage (zero between calls)
   size_t scores;    // f32 [B*Hkv][score_stride] bounding-box page scores
   size_t musd;      // float2 [B*Hq*max_pages] Gaussian page score (mean_Y, sd_Y)
   size_t ehat;      // f32 [B*Hq*max_pages] estimated page maximum
@@ -50,7 +49,6 @@ inline Layout make_layout(int B, int Hkv, int Hq, int max_pages, int P) {
   const size_t tok = L.max_items * kItemTokens;
   L.status = off;   off = align256(off + 4);
   L.sel_done = off; off = align256(off + 4 * size_t(B) * Hkv);
-  L.dec_done = off; off = align256(off + 4 * size_t(B) * Hkv);
   L.scores = off;   off = align256(off + 4 * size_t(B) * Hkv * score_stride(max_pages));
   L.musd = off;     off = align256(off + 8 * bh * max_pages);
   L.ehat = off;     off = align256(off + 4 * bh * max_pages);
@@ -210,6 +208,15 @@ template <typename T> __device__ __forceinline__ T wave_min(T v) {
   for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m, kWave));
   return v;
 }
+
+// Store that is visible to every block of the device once it completes
+// (device-scope relaxed atomic store; written through the L2).
+template <typename T> __device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory access this wave issued has completed.  After
+// st_dev stores, a later atomic by the same block orders after them.
+__device__ __forceinline__ void wait_mem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Block-wide reductions for blockDim.x a multiple of 64 (<= 1024).  `red`
 // is shared scratch of >= 16 elements; every thread gets the result.

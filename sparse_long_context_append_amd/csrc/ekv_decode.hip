@@ -13,9 +13,10 @@
 //               tau >= (head max) - 1 >= (item max) - 1 (the top token's
 //               weight is at most 1).
 // tau_v         one block per (sequence, query head): collects the
-//               candidates above (head max) - 1, finds the exact threshold
-//               and support in float64, and accumulates sum_j p_j v_j over
-//               the support rows (rows split across the block, fixed-order
+//               candidates above (head max) - 1 (skipping items whose
+//               maximum is not above it), finds the exact threshold and
+//               support in float64, and accumulates sum_j p_j v_j over the
+//               support rows (rows split across the block, fixed-order
 //               combine, so results are bitwise reproducible).
 #include "ekv_kernels.h"
 
@@ -495,6 +496,7 @@ struct TauSmem {
   int lt[kLdsCands];
   int lr[kLdsCands];
   int s_pre[kTauItemChunk + 1];
+  int s_item[kTauItemChunk];
   float vpart[2048];  // row-group partial outputs (RPB x D <= 2048)
   double redd[16];
   int redi[17];
@@ -541,14 +543,15 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
   const int tid_w = tid >> 6;
   const bool few_items = n_items <= IPT * kTauThreads;
   int loc[IPT], lsum = 0;
+  float lmx[IPT];
   float lmax = -INFINITY;
   if (few_items) {
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
       const int jj = IPT * tid + i;
       loc[i] = jj < n_items ? icnt[jj] : 0;
-      lmax = fmaxf(lmax, jj < n_items ? imax[jj] : -INFINITY);
-      lsum += loc[i];
+      lmx[i] = jj < n_items ? imax[jj] : -INFINITY;
+      lmax = fmaxf(lmax, lmx[i]);
     }
   } else {
     for (int j = tid; j < n_items; j += blockDim.x) lmax = fmaxf(lmax, imax[j]);
@@ -566,32 +569,49 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
   const double m = mf;
   const double thr = m - 1.0;
 
-  // ---- collect candidates above m - 1, in item order ----
+  // ---- collect candidates above m - 1, in item order (an item whose
+  // maximum is at most m - 1 holds none) ----
   int N = 0;
   bool in_lds = true, done = false;
   if (few_items) {
-    int raw_tot;
-    int base = block_exclusive_scan(lsum, redi, &raw_tot);
+    int nz = 0;
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
-      if (IPT * tid + i < n_items) s_pre[IPT * tid + i] = base;
+      if (!((double)lmx[i] > thr)) loc[i] = 0;
+      lsum += loc[i];
+      nz += loc[i] > 0;
+    }
+    // the non-empty items, listed with their first candidate's rank: one
+    // scan of (items << 17 | candidates), at most 1024 items and 65536
+    // candidates, so the fields cannot carry into each other
+    int packed_tot;
+    const int packed = block_exclusive_scan((nz << 17) | lsum, redi, &packed_tot);
+    const int raw_tot = packed_tot & 0x1ffff, n_ne = packed_tot >> 17;
+    int base = packed & 0x1ffff, rank = packed >> 17;
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      if (loc[i] > 0) {
+        s_pre[rank] = base;
+        sm.s_item[rank] = IPT * tid + i;
+        ++rank;
+      }
       base += loc[i];
     }
-    if (tid == 0) s_pre[n_items] = raw_tot;
+    if (tid == 0) s_pre[n_ne] = raw_tot;
     __syncthreads();
     if (raw_tot <= RPT * kTauThreads) {
       // thread t reads raw candidates [RPT t, RPT t + RPT): one round of loads
       float xv[RPT];
       int tv[RPT], rv[RPT];
       const int i0 = RPT * tid;
-      int item = 0;
+      int k = 0;  // index into the non-empty items
       if (i0 < raw_tot) {
-        int lo = 0, hi = n_items;  // s_pre[lo] <= i0 < s_pre[hi]
+        int lo = 0, hi = n_ne;  // s_pre[lo] <= i0 < s_pre[hi]
         while (hi - lo > 1) {
           const int mid = (lo + hi) >> 1;
           if (s_pre[mid] <= i0) lo = mid; else hi = mid;
         }
-        item = lo;
+        k = lo;
       }
 #pragma unroll
       for (int c = 0; c < RPT; ++c) {
@@ -599,8 +619,8 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
         xv[c] = -INFINITY;
         tv[c] = rv[c] = 0;
         if (i < raw_tot) {
-          while (s_pre[item + 1] <= i) ++item;
-          const size_t at = (size_t)item * kItemTokens + (i - s_pre[item]);
+          while (s_pre[k + 1] <= i) ++k;
+          const size_t at = (size_t)sm.s_item[k] * kItemTokens + (i - s_pre[k]);
           xv[c] = cx[at];
           tv[c] = ct[at];
           rv[c] = cr[at];
@@ -627,7 +647,7 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int jj = 4 * tid + i;
-          lc[i] = jj < nc ? icnt[c0 + jj] : 0;
+          lc[i] = jj < nc && (double)imax[c0 + jj] > thr ? icnt[c0 + jj] : 0;
           sum += lc[i];
         }
         int raw_tot;
@@ -760,21 +780,14 @@ __global__ __launch_bounds__(kTauThreads) void tau_v_kernel(DecodeArgs a) {
 }
 
 template <int DT, int D>
-static hipError_t decode_dispatch(const DecodeArgs& a, int slots, int sub, hipStream_t s) {
+static hipError_t decode_dispatch(const DecodeArgs& a, int slots, hipStream_t s) {
   const dim3 g1(slots, a.batch * a.n_kv_heads), b1(kDecThreads);
-  if (DT == EKV_BF16 && a.group <= 4) {
-    if (sub == 4) {
-      switch (a.group) {
-        case 1: hipLaunchKernelGGL((gather_mfma_kernel<D, 1, 4>), g1, b1, 0, s, a, slots); break;
-        case 2: hipLaunchKernelGGL((gather_mfma_kernel<D, 2, 4>), g1, b1, 0, s, a, slots); break;
-        default: hipLaunchKernelGGL((gather_mfma_kernel<D, 4, 4>), g1, b1, 0, s, a, slots); break;
-      }
-    } else {
-      switch (a.group) {
-        case 1: hipLaunchKernelGGL((gather_mfma_kernel<D, 1, 1>), g1, b1, 0, s, a, slots); break;
-        case 2: hipLaunchKernelGGL((gather_mfma_kernel<D, 2, 1>), g1, b1, 0, s, a, slots); break;
-        default: hipLaunchKernelGGL((gather_mfma_kernel<D, 4, 1>), g1, b1, 0, s, a, slots); break;
-      }
+  const bool mfma = DT == EKV_BF16 && a.group <= 4;
+  if (mfma) {
+    switch (a.group) {
+      case 1: hipLaunchKernelGGL((gather_mfma_kernel<D, 1, 4>), g1, b1, 0, s, a, slots); break;
+      case 2: hipLaunchKernelGGL((gather_mfma_kernel<D, 2, 4>), g1, b1, 0, s, a, slots); break;
+      default: hipLaunchKernelGGL((gather_mfma_kernel<D, 4, 4>), g1, b1, 0, s, a, slots); break;
     }
   } else {
     switch (a.group) {
@@ -811,10 +824,10 @@ hipError_t launch_decode(const DecodeArgs& a, int target_blocks, hipStream_t s) 
   if (slots < 1) slots = 1;
   if (slots > 65535) slots = 65535;
   if (a.kv_dtype == EKV_BF16)
-    return a.head_dim == 128 ? decode_dispatch<EKV_BF16, 128>(a, (int)slots, sub, s)
-                             : decode_dispatch<EKV_BF16, 64>(a, (int)slots, sub, s);
-  return a.head_dim == 128 ? decode_dispatch<EKV_F32, 128>(a, (int)slots, sub, s)
-                           : decode_dispatch<EKV_F32, 64>(a, (int)slots, sub, s);
+    return a.head_dim == 128 ? decode_dispatch<EKV_BF16, 128>(a, (int)slots, s)
+                             : decode_dispatch<EKV_BF16, 64>(a, (int)slots, s);
+  return a.head_dim == 128 ? decode_dispatch<EKV_F32, 128>(a, (int)slots, s)
+                           : decode_dispatch<EKV_F32, 64>(a, (int)slots, s);
 }
 
 __global__ void fill_zero_kernel(uint4* p, size_t n16) {

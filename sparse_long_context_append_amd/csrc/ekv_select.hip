@@ -696,15 +696,15 @@ __global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
     }
   }
   if (tid == 0) {
-    a.tau_hat[bh] = t;
+    st_dev(a.tau_hat + bh, t);  // read by the unit's last block
     if (a.tau_hat_out) a.tau_hat_out[bh] = (float)t;
-    __threadfence();
+    wait_mem();
     s_last = atomicAdd(a.done + unit, 1u) == (uint32_t)(G - 1);
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
-  if (tid == 0) a.done[unit] = 0u;  // ready for the next call
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (tid == 0) st_dev(a.done + unit, 0u);  // ready for the next call
   gauss_keep_unit<G>(a, b, g);
 }
 

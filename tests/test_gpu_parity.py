@@ -160,7 +160,12 @@ def test_topk_covering_every_page_equals_dense():
     rs = run_step(sess, spec, q)
     rd = run_step(sess, spec, q, sparse=False)
     assert np.all(rs["cnt"] == 63)
-    np.testing.assert_array_equal(rs["out"], rd["out"])  # same token set, same order
+    # the same tokens with the same scores: identical supports; the two paths
+    # solve and accumulate in different orders, so values agree to rounding
+    np.testing.assert_array_equal(rs["count"], rd["count"])
+    np.testing.assert_array_equal(rs["supp"], rd["supp"])
+    np.testing.assert_allclose(rs["tau"], rd["tau"], rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(rs["out"], rd["out"], rtol=0, atol=1e-6)
     check_step(spec, rs, q, all_units(spec))
 
 
