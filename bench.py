@@ -124,6 +124,37 @@ class Timer:
         return ms, wall
 
 
+def score_kernel_ms(sess, spec, q, pol, scores, torch, timer, reps, copies=8):
+    """Average duration of one launch of the page-scoring kernel on cold
+    data: `copies` copies of the page metadata are scored back to back
+    between two events (each copy was last read copies-1 launches earlier,
+    more bytes ago than the last-level cache holds), after an eviction.
+    Returns ms per launch, one value per repetition."""
+    import dataclasses
+    import sparse_long_context_append_amd as ekv
+    field = "k_box" if pol == ekv.EKV_SELECT_BBOX_TOPK else "k_moments"
+    caches = [dataclasses.replace(sess.cache, **{field: getattr(sess.cache, field).clone()}) for _ in range(copies)]
+
+    def launch(c):
+        ekv.score_pages(c, sess.seqs, q, spec.n_q_heads, policy=pol, alpha=spec.alpha, scale=spec.scale,
+                        scores=scores, ws=sess.ws)
+
+    for c in caches:
+        launch(c)
+    out = []
+    for _ in range(reps):
+        timer.evict()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for c in caches:
+            launch(c)
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / copies)
+    del caches
+    return out
+
+
 def pct(xs, q):
     xs = sorted(xs)
     return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
@@ -150,10 +181,6 @@ def measure(spec, steps, warmup, torch, timer, do_dense=True, do_graph=True):
     scores = torch.empty((spec.batch, spec.n_kv_heads if pol == 0 else spec.n_q_heads, sess.max_pages)
                          + (() if pol == 0 else (4,)), dtype=torch.float32, device="cuda")
 
-    def score_only():
-        ekv.score_pages(sess.cache, sess.seqs, q, spec.n_q_heads, policy=pol, alpha=spec.alpha, scale=spec.scale,
-                        scores=scores, ws=sess.ws)
-
     res = {}
     ms, wall = timer.run(sparse_step, steps, warmup)
     res["sparse_ms"] = ms
@@ -172,11 +199,11 @@ def measure(spec, steps, warmup, torch, timer, do_dense=True, do_graph=True):
     res["support_mean"] = float(sc.mean())
     res["psum_err"] = float(np.abs(sess.psum.cpu().numpy() - 1.0).max())
     sparse_out = sess.out.clone()
-    ms_s, _ = timer.run(score_only, steps, warmup)
-    res["score_ms"] = ms_s
+    res["score_ms"] = score_kernel_ms(sess, spec, q, pol, scores, torch, timer, reps=max(5, steps // 4))
     npages = res["pages_total"]
     rec = 2 * spec.head_dim * (spec.elem_bytes if pol == 0 else 4)
-    out_b = 4 if pol == 0 else 16 * spec.group  # one fp32 score / G float4 page stats per (page, KV head)
+    # one fp32 score per (page, KV head); Gaussian: (mean, sd) + estimate + float4 stats per (page, query head)
+    out_b = 4 if pol == 0 else 28 * spec.group
     res["score_bytes"] = float(npages * (rec + out_b))
     if do_graph:
         g = torch.cuda.CUDAGraph()
@@ -211,47 +238,63 @@ def measure(spec, steps, warmup, torch, timer, do_dense=True, do_graph=True):
 
 
 # ------------------------------------------------------------ CPU oracle ---
-def cpu_baseline(spec, units, reps=3):
-    """Time the oracle's sparse step (scoring from metadata, selection, exact
-    entmax over the kept pages) on `units` (b, g) of the workload; metadata
-    build is excluded.  Returns seconds per unit (median of reps)."""
+def cpu_baseline(spec, units, reps=3, dense_units=()):
+    """Time the float64 oracle on the host: its sparse step (page scoring from
+    prebuilt metadata, selection, exact entmax over the kept pages) on each
+    unit (b, g) in `units`, and its full-cache entmax on `dense_units`.
+    Inputs and metadata are prepared outside the timed region, one unit at a
+    time.  Returns (sparse seconds summed over units, dense seconds summed
+    over dense_units), each unit's time the median of `reps` runs."""
     from oracle import decode as odecode
     from oracle import entmax, metadata, scoring, select
 
     q = W.queries(spec).astype(np.float64)
-    prepared = []
-    for (b, g) in units:
+    G = spec.group
+    lens = W.seq_lens(spec)
+
+    def sparse_pass(b, g, k, v, L, md):
+        heads = range(g * G, (g + 1) * G)
+        if spec.policy == "bbox":
+            S = scoring.bbox_page_scores(q[b, heads], md["kmin"], md["kmax"], spec.scale)
+            pages = select.topk_pages(S, spec.top_k)
+        else:
+            eh, th = [], []
+            for h in heads:
+                mu, sd, e = scoring.gauss_page_stats(q[b, h], md["mean"], md["var"], md["count"],
+                                                     spec.alpha, spec.scale)
+                eh.append(e)
+                th.append(select.gauss_tau_hat(mu, sd, md["count"], spec.alpha))
+            pages = select.gauss_keep_pages(np.array(eh), np.array(th), spec.delta)
+        toks = odecode.pages_to_tokens(pages, L, spec.page_size)
+        for h in heads:
+            odecode.decode_head(q[b, h], k, v, toks, spec.alpha, spec.scale)
+
+    def dense_pass(b, g, k, v, L):
+        toks = np.arange(L)
+        for h in range(g * G, (g + 1) * G):
+            odecode.decode_head(q[b, h], k, v, toks, spec.alpha, spec.scale)
+
+    def timed(fn, n):
+        ts = []
+        for _ in range(n):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return statistics.median(ts)
+
+    sparse_s = dense_s = 0.0
+    for (b, g) in sorted(set(units) | set(dense_units)):
         k = entmax.stored_to_f64(W.keys(spec, b, g), spec.kv_dtype)
         v = entmax.stored_to_f64(W.values(spec, b, g), spec.kv_dtype)
-        L = int(W.seq_lens(spec)[b])
-        md = metadata.page_metadata(k, L, spec.page_size)
-        prepared.append((b, g, k, v, L, md))
-    G = spec.group
-
-    def one_pass():
-        for (b, g, k, v, L, md) in prepared:
-            heads = range(g * G, (g + 1) * G)
-            if spec.policy == "bbox":
-                S = scoring.bbox_page_scores(q[b, heads], md["kmin"], md["kmax"], spec.scale)
-                pages = select.topk_pages(S, spec.top_k)
-            else:
-                eh, th = [], []
-                for h in heads:
-                    mu, sd, e = scoring.gauss_page_stats(q[b, h], md["mean"], md["var"], md["count"],
-                                                         spec.alpha, spec.scale)
-                    eh.append(e)
-                    th.append(select.gauss_tau_hat(mu, sd, md["count"], spec.alpha))
-                pages = select.gauss_keep_pages(np.array(eh), np.array(th), spec.delta)
-            toks = odecode.pages_to_tokens(pages, L, spec.page_size)
-            for h in heads:
-                odecode.decode_head(q[b, h], k, v, toks, spec.alpha, spec.scale)
-
-    times = []
-    for _ in range(reps):
-        t0 = time.perf_counter()
-        one_pass()
-        times.append(time.perf_counter() - t0)
-    return statistics.median(times) / len(units)
+        L = int(lens[b])
+        if (b, g) in units:
+            md = metadata.page_metadata(k, L, spec.page_size)
+            sparse_s += timed(lambda: sparse_pass(b, g, k, v, L, md), reps)
+            del md
+        if (b, g) in dense_units:
+            dense_s += timed(lambda: dense_pass(b, g, k, v, L), 1)
+        del k, v
+    return sparse_s, dense_s
 
 
 # -------------------------------------------------------------------- main -
@@ -287,6 +330,43 @@ def summarize(spec, r):
     return out
 
 
+def copy_probe(mib):
+    """A plain copy kernel of known size: HBM read and write counters of its
+    dispatches calibrate the counters of the path's kernels."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "dispatches": 5}), flush=True)
+
+
+def traffic_from_profile(kernel, workload):
+    """HBM bytes per dispatch of `kernel` on `workload` from the committed
+    counter summary, if the kernel source it was taken on is unchanged."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        line = line.strip().lstrip("-").strip()
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in ("ekv_select.hip", "ekv_common.h", "ekv_kernels.h"):
+        h.update(open(os.path.join(ROOT, "sparse_long_context_append_amd", "csrc", f), "rb").read())
+    if vals.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_dispatch"]))
+    except (KeyError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -298,7 +378,13 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--context", type=int, default=0, help="override the workload's context (scaling sweeps)")
+    ap.add_argument("--cpu-units", type=int, default=2, help="(sequence, KV head) units the CPU oracle is timed on")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (counter calibration)")
     args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the decode path is a single-GPU path and no multi-GPU mode exists",
               file=sys.stderr)
@@ -318,19 +404,23 @@ def main():
         extra = summarize(spec2, r2)
     cpu = None
     if not args.no_cpu:
-        units = [(0, 0), (0, 1)]
-        per_unit = cpu_baseline(spec, units)
         n_units = spec.batch * spec.n_kv_heads
-        cpu_us = per_unit * n_units * 1e6
+        units = [(b, g) for b in range(spec.batch) for g in range(spec.n_kv_heads)][: args.cpu_units]
+        t0 = time.perf_counter()
+        sparse_s, dense_s = cpu_baseline(spec, units, dense_units=[units[0]])
+        log(f"cpu oracle: {time.perf_counter() - t0:.1f}s including input preparation")
+        cpu_us = sparse_s / len(units) * n_units * 1e6
         cpu = {
             "value": round(r["bytes"] / (cpu_us * 1e-6) / 1e9, 3),
             "unit": "GB/s",
             "us_per_step": round(cpu_us, 1),
+            "dense_us_per_step": round(dense_s * n_units * 1e6, 1),
             "cores": int(os.environ.get("OMP_NUM_THREADS", _NCPU)),
             "kind": "oracle",
-            "sample": (f"float64 numpy oracle sparse step (bbox scoring from prebuilt metadata, top-k, exact "
-                       f"entmax over the kept pages) on {len(units)} of {n_units} (sequence, KV head) units of "
-                       f"{spec.name}, median of 3, scaled to the whole step"),
+            "sample": (f"float64 numpy oracle on the host, inputs prepared outside the timing: sparse step "
+                       f"({spec.policy} scoring from prebuilt page metadata, selection, exact entmax over the "
+                       f"kept pages) on {len(units)} of {n_units} (sequence, KV head) units of {spec.name}, "
+                       f"median of 3 per unit, scaled to all units; full-cache entmax on 1 unit, scaled"),
         }
     med_us = main_sum["us_per_step"]
     sm_us = main_sum["score_kernel_us"]
@@ -362,8 +452,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(main_sum["score_kernel_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "launch_us": sm_us,
+            "traffic": traffic_from_profile("score_bbox" if spec.policy == "bbox" else "score_gauss", spec.name),
+            "kernel_us": sm_us,
+            "algorithmic_bytes": int(r["score_bytes"]),
         },
         "cpu_baseline": cpu,
     }
