@@ -630,10 +630,12 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
 #pragma unroll
       for (int c = 0; c < RPT; ++c) kc += (double)xv[c] > thr;
       int pos = block_exclusive_scan(kc, redi, &N);
+      if (N <= kLdsCands) {  // else the general path below lists them in the workspace
 #pragma unroll
-      for (int c = 0; c < RPT; ++c)
-        if ((double)xv[c] > thr) { lx[pos] = xv[c]; lt[pos] = tv[c]; lr[pos] = rv[c]; ++pos; }
-      done = true;
+        for (int c = 0; c < RPT; ++c)
+          if ((double)xv[c] > thr) { lx[pos] = xv[c]; lt[pos] = tv[c]; lr[pos] = rv[c]; ++pos; }
+        done = true;
+      }
     }
   }
   if (!done) {

@@ -169,31 +169,43 @@ def test_topk_covering_every_page_equals_dense():
     check_step(spec, rs, q, all_units(spec))
 
 
+@pytest.mark.parametrize("kv", ["f32", "bf16"])
+@pytest.mark.parametrize("L", [1500, 5000])
 @pytest.mark.parametrize("alpha", [1.5, 2.0])
-def test_all_keys_equal_large_support(alpha):
+def test_all_keys_equal_large_support(alpha, L, kv):
     """Every key identical: every page ties (lowest ids win) and every token
-    is in the support, which overflows the on-chip candidate list."""
+    is in the support.  1500 tokens overflow the on-chip candidate list from
+    the register path, 5000 from the chunked path; bf16 runs the matrix-core
+    gather, fp32 the vector one."""
     from sparse_long_context_append_amd.runtime import DecodeSession
     import sparse_long_context_append_amd as ekv
-    L, P, d = 5000, 16, 64
+    P, d = 16, 64
     npg = -(-L // P)
     table = np.arange(npg, dtype=np.int32)[None]
-    sess = DecodeSession(batch=1, n_kv_heads=1, n_q_heads=2, head_dim=d, page_size=P, kv_dtype=ekv.EKV_F32,
+    dt = ekv.EKV_F32 if kv == "f32" else ekv.EKV_BF16
+    tdt = torch.float32 if kv == "f32" else torch.bfloat16
+    sess = DecodeSession(batch=1, n_kv_heads=1, n_q_heads=2, head_dim=d, page_size=P, kv_dtype=dt,
                          n_phys_pages=npg, page_table=table, cap=npg)
     rng = np.random.default_rng(7)
     k = np.repeat(rng.standard_normal((1, d)).astype(np.float32), L, axis=0)
     v = rng.standard_normal((L, d)).astype(np.float32)
-    sess.append(torch.from_numpy(k[None, :, None]).cuda(), torch.from_numpy(v[None, :, None]).cuda())
+    kd = torch.from_numpy(k[None, :, None]).cuda().to(tdt)
+    vd = torch.from_numpy(v[None, :, None]).cuda().to(tdt)
+    sess.append(kd, vd)
     q = torch.from_numpy(rng.standard_normal((1, 2, d)).astype(np.float32)).cuda()
     sess.select(q, policy=ekv.EKV_SELECT_BBOX_TOPK, alpha=alpha, scale=0.125, top_k=5)
     torch.cuda.synchronize()
     assert sess.sel_count.item() == 5
     assert sess.sel[0, 0, :5].tolist() == [0, 1, 2, 3, 4]
-    sess.decode(q, alpha=alpha, scale=0.125, sparse=False)
-    torch.cuda.synchronize()
-    assert np.all(sess.support_count.cpu().numpy() == L)
-    np.testing.assert_allclose(sess.psum.cpu().numpy(), 1.0, atol=1e-5)
-    np.testing.assert_allclose(sess.out.cpu().numpy()[0], np.tile(v.mean(axis=0), (2, 1)), atol=2e-3)
+    v_stored = vd[0, :, 0].float().cpu().numpy().astype(np.float64)
+    for sparse, n in ((True, 5 * P), (False, L)):
+        sess.decode(q, alpha=alpha, scale=0.125, sparse=sparse)
+        torch.cuda.synchronize()
+        assert np.all(sess.support_count.cpu().numpy() == n)
+        np.testing.assert_allclose(sess.psum.cpu().numpy(), 1.0, atol=1e-5)
+        np.testing.assert_allclose(sess.out.cpu().numpy()[0], np.tile(v_stored[:n].mean(axis=0), (2, 1)),
+                                   atol=2e-3)
+    assert sess.device_status() == 0
 
 
 def test_empty_and_single_token_sequences():
