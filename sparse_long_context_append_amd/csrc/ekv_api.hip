@@ -166,6 +166,8 @@ static ekv_status prepare_select(const ekv_cache* cache, const ekv_seqs* seqs, c
   a->ehat = at<float>(workspace, L->ehat);
   a->stats_out = nullptr;
   a->tau_hat = at<double>(workspace, L->tau_hat);
+  a->keep_bits = at<uint64_t>(workspace, L->keep_bits);
+  a->keep_words = ekv::keep_words(seqs->max_pages);
   a->done = at<uint32_t>(workspace, L->sel_done);
   a->status = at<uint32_t>(workspace, L->status);
   return EKV_OK;
@@ -249,8 +251,8 @@ ekv_status ekv_entmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const
   a.ovf_t = at<int32_t>(workspace, L.ovf_t);
   a.ovf_r = at<int32_t>(workspace, L.ovf_r);
   a.status = at<uint32_t>(workspace, L.status);
-  // about 16 gather blocks per compute unit
-  return hip_status(ekv::launch_decode(a, 16 * device_cus(), (hipStream_t)stream), "entmax_decode launch");
+  // about 4 gather blocks per compute unit (one resident wave of blocks)
+  return hip_status(ekv::launch_decode(a, 4 * device_cus(), (hipStream_t)stream), "entmax_decode launch");
 }
 
 ekv_status ekv_read_device_status(void* workspace, size_t ws_bytes, int32_t* host_flags) {

@@ -25,6 +25,7 @@ struct Layout {
   size_t musd;      // float2 [B*Hq*max_pages] Gaussian page score (mean_Y, sd_Y)
   size_t ehat;      // f32 [B*Hq*max_pages] estimated page maximum
   size_t tau_hat;   // f64 [B*Hq]
+  size_t keep_bits; // u64 [B*Hq][keep_words(max_pages)] Gaussian keep bitmaps
   size_t item_cnt;  // i32 [B*Hq*max_items] candidates kept by each decode work item
   size_t item_max;  // f32 [B*Hq*max_items] per item maximum score
   size_t cand_x;    // f32 [B*Hq*max_items*64] candidate scores, one region per item
@@ -38,6 +39,8 @@ struct Layout {
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+// 64-bit words of a per-page bitmap
+inline int keep_words(int max_pages) { return (max_pages + 63) / 64; }
 // row stride of the internal page-score buffer: 16-byte aligned rows
 inline int score_stride(int max_pages) { return (max_pages + 3) & ~3; }
 
@@ -53,6 +56,7 @@ inline Layout make_layout(int B, int Hkv, int Hq, int max_pages, int P) {
   L.musd = off;     off = align256(off + 8 * bh * max_pages);
   L.ehat = off;     off = align256(off + 4 * bh * max_pages);
   L.tau_hat = off;  off = align256(off + 8 * bh);
+  L.keep_bits = off; off = align256(off + 8 * bh * keep_words(max_pages));
   L.item_cnt = off; off = align256(off + 4 * bh * L.max_items);
   L.item_max = off; off = align256(off + 4 * bh * L.max_items);
   L.cand_x = off;   off = align256(off + 4 * bh * tok);
@@ -193,20 +197,59 @@ __device__ __forceinline__ void set_status(uint32_t* status, uint32_t bits) {
 // ---------------------------------------------------------------------------
 // Reductions.  Fixed butterfly order, so results do not depend on timing.
 // ---------------------------------------------------------------------------
-template <typename T> __device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+// Wave-wide reductions on the DPP row network (no LDS traffic): within each
+// 16-lane row, xor-1 and xor-2 quad permutes, then the half-row and row
+// mirrors (after the quad steps every lane of a quad holds the same value,
+// so a mirror adds the other quad / half-row); the four row results are read
+// with readlane and combined in a fixed order, so every lane gets the same,
+// reproducible value.  The whole wave must be active.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRowHalfMirror = 0x141, kDppRowMirror = 0x140;
+
+template <int CTRL> __device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL, typename T> __device__ __forceinline__ T dpp(T v) {
+  if constexpr (sizeof(T) == 8) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint64_t r = ((uint64_t)dpp32<CTRL>((uint32_t)(u >> 32)) << 32) | dpp32<CTRL>((uint32_t)u);
+    return __builtin_bit_cast(T, r);
+  } else {
+    return __builtin_bit_cast(T, dpp32<CTRL>(__builtin_bit_cast(uint32_t, v)));
+  }
+}
+template <typename T> __device__ __forceinline__ T lane_value(T v, int l) {
+  if constexpr (sizeof(T) == 8) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+  } else {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+  }
+}
+// Reduction over aligned groups of 4, 8 or 16 lanes (every lane of a group
+// gets the group's value).
+template <int N, typename T, typename Op> __device__ __forceinline__ T group_reduce(T v, Op op) {
+  static_assert(N == 4 || N == 8 || N == 16, "group size");
+  v = op(v, dpp<kDppXor1>(v));
+  v = op(v, dpp<kDppXor2>(v));
+  if constexpr (N >= 8) v = op(v, dpp<kDppRowHalfMirror>(v));
+  if constexpr (N >= 16) v = op(v, dpp<kDppRowMirror>(v));
   return v;
+}
+template <typename T, typename Op> __device__ __forceinline__ T wave_reduce(T v, Op op) {
+  v = group_reduce<16>(v, op);
+  const T r0 = lane_value(v, 0), r1 = lane_value(v, 16), r2 = lane_value(v, 32), r3 = lane_value(v, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
+template <typename T> __device__ __forceinline__ T wave_sum(T v) {
+  return wave_reduce(v, [](T x, T y) { return x + y; });
 }
 template <typename T> __device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m, kWave));
-  return v;
+  return wave_reduce(v, [](T x, T y) { return max(x, y); });
 }
 template <typename T> __device__ __forceinline__ T wave_min(T v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m, kWave));
-  return v;
+  return wave_reduce(v, [](T x, T y) { return min(x, y); });
 }
 
 // Store that is visible to every block of the device once it completes
@@ -229,6 +272,18 @@ template <typename T> __device__ T block_sum(T v, T* red) {
   T r = red[0];
   for (int i = 1; i < nw; ++i) r += red[i];
   return r;
+}
+// Three sums at once; `red` holds >= 3 * 16 doubles.
+__device__ inline void block_sum3(double& a, double& b, double& c, double* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  a = wave_sum(a);
+  b = wave_sum(b);
+  c = wave_sum(c);
+  __syncthreads();
+  if (lane == 0) { red[3 * w] = a; red[3 * w + 1] = b; red[3 * w + 2] = c; }
+  __syncthreads();
+  a = red[0]; b = red[1]; c = red[2];
+  for (int i = 1; i < nw; ++i) { a += red[3 * i]; b += red[3 * i + 1]; c += red[3 * i + 2]; }
 }
 template <typename T> __device__ T block_max(T v, T* red) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;

@@ -191,11 +191,7 @@ __global__ __launch_bounds__(kDecThreads) void gather_mfma_kernel(DecodeArgs a, 
       for (int kb = 0; kb < KB; ++kb) c = mfma_bf16(s_a[kb][lane], bv[s][kb], c);
       x[s] = tr[s].valid && grp < G ? (c[0] + c[1]) + c[2] : -INFINITY;
       // per-head item maximum (the 16 lanes of one head share grp)
-      float m = x[s];
-      m = fmaxf(m, __shfl_xor(m, 1, kWave));
-      m = fmaxf(m, __shfl_xor(m, 2, kWave));
-      m = fmaxf(m, __shfl_xor(m, 4, kWave));
-      m = fmaxf(m, __shfl_xor(m, 8, kWave));
+      const float m = group_reduce<16>(x[s], [](float u, float v) { return fmaxf(u, v); });
       if (col == 0) s_max[s][w][grp] = m;
     }
     __syncthreads();
@@ -446,22 +442,30 @@ __device__ double solve_pairwise(const float* xs, int N, double m, float alpha_f
   float xr[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) xr[r] = (lane + kWave * r < N) ? xs[lane + kWave * r] : 0.f;
+  // alpha 2 and 1.5: f in float32 (its rounding, about N 2^-24 f, only
+  // matters for scores that lie within that distance of tau); otherwise float64
   double f = 0.0;
+  float ff = 0.f;
+  const float xif = has ? xs[i] : 0.f;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int nr = min(kWave, N - kWave * r);
     for (int l = 0; l < nr; ++l) {
       const float xj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xr[r]), l));
-      const double d = (double)xj - xi;
-      if (d > 0.0) f += entmax_pow<AK>(d, beta);
+      if (AK == 2) {
+        const double d = (double)xj - xi;
+        if (d > 0.0) f += entmax_pow<AK>(d, beta);
+      } else {
+        const float d = fmaxf(xj - xif, 0.f);
+        ff += AK == 0 ? d : d * d;
+      }
     }
   }
+  if (AK != 2) f = ff;
   const bool in = has && f < 1.0;
   const double y = xi - m;
   double c = in ? 1.0 : 0.0, s1 = in ? y : 0.0, s2 = in ? y * y : 0.0;
-  c = block_sum(c, red);
-  s1 = block_sum(s1, red);
-  s2 = block_sum(s2, red);
+  block_sum3(c, s1, s2, red);
   if (sparsemax) return m + (s1 - 1.0) / c;
   if (ent15) {
     const double mu = s1 / c;
@@ -498,7 +502,7 @@ struct TauSmem {
   int s_pre[kTauItemChunk + 1];
   int s_item[kTauItemChunk];
   float vpart[2048];  // row-group partial outputs (RPB x D <= 2048)
-  double redd[16];
+  double redd[48];  // block reductions (up to three values per wave)
   int redi[17];
   double s_tau;
   uint32_t s_mkey[4];

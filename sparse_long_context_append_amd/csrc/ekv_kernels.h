@@ -42,6 +42,8 @@ struct SelectArgs {
   float* ehat;         // estimated page maximum [B*Hq*max_pages]
   float4* stats_out;   // optional (mean_Y, sd_Y, e_hat, n_p) copy for diagnostics
   double* tau_hat;     // [B*Hq]
+  uint64_t* keep_bits; // [B*Hq][keep_words] per-head page keep bitmaps
+  int keep_words;
   uint32_t* done;      // [B*Hkv] arrival counters, zero between calls
   uint32_t* status;
 };

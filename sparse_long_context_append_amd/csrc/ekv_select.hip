@@ -181,8 +181,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_bbox_valu_kernel(SelectAr
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    acc[h] += __shfl_xor(acc[h], 1, kWave);
-    acc[h] += __shfl_xor(acc[h], 2, kWave);
+    acc[h] = group_reduce<4>(acc[h], [](double u, double v) { return u + v; });
   }
   if (sub == 0 && p < a.max_pages) {
     double s = acc[0];
@@ -244,11 +243,8 @@ __device__ void topk_block(const SelectArgs& a, const float* s, int n_b, int k_e
   // bits shared by every key (AND and OR in one reduction) and cleared histograms
   uint32_t kand = 0xffffffffu, kor = 0u;
   EKV_FOR_KEYS(kand &= k; kor |= k;)
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    kand &= __shfl_xor(kand, m, kWave);
-    kor |= __shfl_xor(kor, m, kWave);
-  }
+  kand = wave_reduce(kand, [](uint32_t u, uint32_t v) { return u & v; });
+  kor = wave_reduce(kor, [](uint32_t u, uint32_t v) { return u | v; });
   for (int i = tid; i < 512; i += blockDim.x) (&hist[0][0])[i] = 0u;
   if (lane == 0) { red[0][w] = kand; red[1][w] = kor; }
   __syncthreads();
@@ -399,11 +395,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_gauss_kernel(SelectArgs a
     for (int h = 0; h < G; ++h) {
       A[h] = fa[h];
       Bv[h] = fb[h];
-#pragma unroll
-      for (int m = 1; m < 8; m <<= 1) {
-        A[h] += __shfl_xor(A[h], m, kWave);
-        Bv[h] += __shfl_xor(Bv[h], m, kWave);
-      }
+      A[h] = group_reduce<8>(A[h], [](double u, double v) { return u + v; });
+      Bv[h] = group_reduce<8>(Bv[h], [](double u, double v) { return u + v; });
     }
     const int p = pbase + 32 * n;
     if (sub < G && p < a.max_pages) {
@@ -454,19 +447,21 @@ __global__ __launch_bounds__(kScoreThreads) void score_gauss_kernel(SelectArgs a
 // the group, in ascending order, at least one page (the best margin, lowest
 // id on ties).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void gauss_mass(float mu, float sd, float tf, bool quad, float& e, float& de) {
+__device__ __forceinline__ void gauss_mass(float mu, float sd, float tf, bool quad, float& e, float& de,
+                                           float& dde) {
   const float kInvSqrt2 = 0.70710678118654752440f, kInvSqrt2Pi = 0.39894228040143267794f;
   const float am = mu - tf;
   if (sd <= 0.f) {
     const float pos = fmaxf(am, 0.f);
     e = quad ? pos * pos : pos;
     de = quad ? -2.f * pos : (am > 0.f ? -1.f : 0.f);
+    dde = quad && am > 0.f ? 2.f : 0.f;
     return;
   }
-  const float u = am / sd;
+  const float rsd = __builtin_amdgcn_rcpf(sd);
+  const float u = am * rsd;
   if (u < -7.f) {
-    e = 0.f;
-    de = 0.f;
+    e = de = dde = 0.f;
     return;
   }
   const float Phi = 0.5f * erfcf(-u * kInvSqrt2);
@@ -475,99 +470,51 @@ __device__ __forceinline__ void gauss_mass(float mu, float sd, float tf, bool qu
   if (quad) {
     e = (am * am + sd * sd) * Phi + am * sd * phi;
     de = -2.f * e1;
+    dde = 2.f * Phi;
   } else {
     e = e1;
     de = -Phi;
+    dde = phi * rsd;
   }
 }
 
 // live-list entries carry the partial last page as sd -> -sd - 1
 __device__ __forceinline__ void live_term(float2 v, float P, float last_n, float tf, bool quad, double& F,
-                                          double& dF) {
+                                          double& dF, double& ddF) {
   float n = P, sd = v.y;
   if (sd < 0.f) { sd = -sd - 1.f; n = last_n; }
-  float e, de;
-  gauss_mass(v.x, sd, tf, quad, e, de);
+  float e, de, dde;
+  gauss_mass(v.x, sd, tf, quad, e, de, dde);
   F += (double)n * (double)e;
   dF += (double)n * (double)de;
+  ddF += (double)n * (double)dde;
 }
 
+// The single page of the largest margin max_h (e_hat - tau_hat) (lowest id
+// on ties), for a group that keeps no page.
 template <int G>
-__device__ void gauss_keep_unit(const SelectArgs& a, int b, int g) {
-  constexpr int PPT = G >= 8 ? 4 : 8;  // pages per thread held in registers
-  const int unit = b * a.n_kv_heads + g;
-  const int tid = threadIdx.x;
-  const int P = a.page_size;
-  const int L = clamp_len(a.seq_lens[b], a.max_pages, P, a.status);
-  const int n_b = pages_of(L, P);
-  int32_t* out = a.sel + (size_t)unit * a.cap;
-  __shared__ int redi[17];
+__device__ void gauss_floor_unit(const SelectArgs& a, int b, int g, int n_b, int32_t* out, int unit) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
   __shared__ double redd[16];
   __shared__ int redp[16];
-  if (n_b == 0) {
-    if (tid == 0) a.sel_count[unit] = 0;
-    return;
-  }
   double tau[G];
   const float* eh[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const size_t bh = (size_t)b * a.n_q_heads + (size_t)g * G + h;
-    tau[h] = __hip_atomic_load(a.tau_hat + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    tau[h] = a.tau_hat[bh];
     eh[h] = a.ehat + bh * a.max_pages;
   }
-  const double ndelta = -(double)a.delta;
   double best = -INFINITY;
   int best_p = 0x7fffffff;
-  int run = 0;
-  const int per = (n_b + blockDim.x - 1) / blockDim.x;
-  if (per <= PPT) {
-    const int p0 = per * tid;
-    float e[G][PPT];
+  for (int p = tid; p < n_b; p += blockDim.x) {
+    double mg = -INFINITY;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int i = 0; i < PPT; ++i) e[h][i] = (i < per && p0 + i < n_b) ? eh[h][p0 + i] : -INFINITY;
-    bool keep[PPT];
-    int c = 0;
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      double mg = -INFINITY;
-#pragma unroll
-      for (int h = 0; h < G; ++h) mg = fmax(mg, (double)e[h][i] - tau[h]);
-      keep[i] = i < per && p0 + i < n_b && mg > ndelta;
-      c += keep[i];
-      if (i < per && p0 + i < n_b && mg > best) { best = mg; best_p = p0 + i; }
-    }
-    int pos = block_exclusive_scan(c, redi, &run);
-#pragma unroll
-    for (int i = 0; i < PPT; ++i)
-      if (keep[i]) out[pos++] = p0 + i;
-  } else {
-    for (int p0 = 0; p0 < n_b; p0 += blockDim.x) {
-      const int p = p0 + tid;
-      bool keep = false;
-      if (p < n_b) {
-        double mg = -INFINITY;
-#pragma unroll
-        for (int h = 0; h < G; ++h) mg = fmax(mg, (double)eh[h][p] - tau[h]);
-        keep = mg > ndelta;
-        if (mg > best) { best = mg; best_p = p; }
-      }
-      int tot;
-      const int pos = run + block_exclusive_scan(keep ? 1 : 0, redi, &tot);
-      if (keep) out[pos] = p;
-      run += tot;
-    }
+    for (int h = 0; h < G; ++h) mg = fmax(mg, (double)eh[h][p] - tau[h]);
+    if (mg > best) { best = mg; best_p = p; }
   }
-  if (run > 0) {
-    if (tid == 0) a.sel_count[unit] = run;
-    return;
-  }
-  // floor: the single best page
   const double bm = block_max(best, redd);
   int cand = (best == bm) ? best_p : 0x7fffffff;
-  const int lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
   cand = wave_min(cand);
   __syncthreads();
   if (lane == 0) redp[w] = cand;
@@ -592,17 +539,22 @@ __global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
   const int n_b = pages_of(L, P);
   const size_t bh = (size_t)b * a.n_q_heads + h;
   const float2* st = a.musd + bh * a.max_pages;
+  const float* eh = a.ehat + bh * a.max_pages;
+  uint64_t* kbits = a.keep_bits + bh * a.keep_words;
   __shared__ float2 live[kTauHatLive];
-  __shared__ double part[2][NW][2];
+  __shared__ double part[2][NW][3];
   __shared__ double redd[16];
   __shared__ int redi[17];
   __shared__ int s_last;
   double t = 0.0;
+  const bool in_regs = n_b <= PPT * kTauHatThreads;
+  float er[PPT];  // this thread's estimated maxima (pages tid + 1024 i)
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) er[i] = -INFINITY;
   if (n_b > 0) {
     const bool quad = a.alpha == 1.5f;
     const float Pf = (float)P;
     const float last_n = (float)(L - (n_b - 1) * P);  // tokens of the last page
-    const bool in_regs = n_b <= PPT * kTauHatThreads;
     // thread t owns pages t, t + 1024, ...: one round of coalesced loads
     float2 ms[PPT];
     double lb = -INFINITY;
@@ -615,6 +567,7 @@ __global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
       for (int i = 0; i < PPT; ++i) {
         const int p = i * kTauHatThreads + tid;
         ms[i] = p < n_b ? st[p] : make_float2(-INFINITY, 0.f);
+        er[i] = p < n_b ? eh[p] : -INFINITY;
         if (p < n_b) lb = fmax(lb, bound(ms[i], p));
       }
     } else {
@@ -649,63 +602,143 @@ __global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
     t = t0;
     for (int it = 0; it < 200; ++it) {
       const float tf = (float)t;
-      double F = 0.0, dF = 0.0;
+      double F = 0.0, dF = 0.0, ddF = 0.0;
       if (use_live) {
-        for (int i = tid; i < n_live; i += kTauHatThreads) live_term(live[i], Pf, last_n, tf, quad, F, dF);
+        for (int i = tid; i < n_live; i += kTauHatThreads) live_term(live[i], Pf, last_n, tf, quad, F, dF, ddF);
       } else {
         for (int p = tid; p < n_b; p += kTauHatThreads) {
-          const float2 v = st[p];
-          float e, de;
-          gauss_mass(v.x, v.y, tf, quad, e, de);
-          const double n = p == n_b - 1 ? (double)last_n : (double)P;
-          F += n * (double)e;
-          dF += n * (double)de;
+          float2 v = st[p];
+          if (p == n_b - 1 && last_n != Pf) v.y = -v.y - 1.f;
+          live_term(v, Pf, last_n, tf, quad, F, dF, ddF);
         }
       }
-      // one barrier per iteration: partials alternate between two buffers
+      // wave partials -> wave 0 computes the step -> every wave reads it
       F = wave_sum(F);
       dF = wave_sum(dF);
+      ddF = wave_sum(ddF);
       if (lane == 0) {
-        part[it & 1][w][0] = F;
-        part[it & 1][w][1] = dF;
+        part[0][w][0] = F;
+        part[0][w][1] = dF;
+        part[0][w][2] = ddF;
       }
       __syncthreads();
-      F = 0.0;
-      dF = 0.0;
+      if (w == 0) {
+        // lane i < NW takes wave i's partials; a fixed-order wave sum
+        double pf = lane < NW ? part[0][lane][0] : 0.0;
+        double pd = lane < NW ? part[0][lane][1] : 0.0;
+        double pdd = lane < NW ? part[0][lane][2] : 0.0;
+        static_assert(NW == 16, "one partial per lane of the first row");
+        auto add = [](double u, double v) { return u + v; };
+        pf = group_reduce<16>(pf, add);
+        pd = group_reduce<16>(pd, add);
+        pdd = group_reduce<16>(pdd, add);
+        F = pf; dF = pd; ddF = pdd;
+        int stop = 0;
+        if (F == 1.0) {
+          stop = 1;
+        } else {
+          if (F > 1.0) lo = t; else hi = t;
+          const double tol = 2e-7 * fmax(1.0, fabs(t));
+          // Halley's method on g = log F (cubic near the root), else Newton's
+          // on g, else bisection of the bracket.  Near the root g comes from
+          // its series in F - 1; farther away a float logarithm suffices.
+          double cand = t;
+          bool ok = false;
+          if (F > 0.0 && dF < 0.0) {
+            const double x = F - 1.0;
+            const double gl = fabs(x) < 1e-3 ? x * (1.0 - x * (0.5 - x * (1.0 / 3.0 - 0.25 * x)))
+                                             : (double)logf((float)F);
+            const double iF = 1.0 / F;
+            const double g1 = dF * iF, g2 = ddF * iF - g1 * g1;
+            const double cn = t - gl / g1;
+            const float r = (float)(gl * g2 / (g1 * g1));
+            const float den = 1.f - 0.5f * r;
+            const double ch = den > 0.f ? t + (cn - t) * (double)(1.f / den) : cn;  // Halley = Newton / (1 - r/2)
+            if (den > 0.f && ch > lo && ch < hi) { cand = ch; ok = true; }
+            else if (cn > lo && cn < hi) { cand = cn; ok = true; }
+            else if (fabs(cn - t) <= tol) { cand = cn; ok = true; }
+          }
+          if (ok && fabs(cand - t) <= tol) {
+            stop = 1;
+          } else if (!ok) {
+            if (lo > -INFINITY && hi < INFINITY) cand = 0.5 * (lo + hi);
+            else if (hi < INFINITY) cand = hi - fmax(1.0, fabs(hi));
+            else cand = lo + fmax(1.0, fabs(lo));
+          }
+          if (!stop && hi - lo <= tol) stop = 1;
+          t = cand;
+        }
+        if (lane == 0) {
+          part[1][0][0] = t;
+          part[1][0][1] = stop ? 1.0 : 0.0;
+        }
+      }
+      __syncthreads();
+      t = part[1][0][0];
+      const bool stop = part[1][0][1] != 0.0;
+      if (stop) break;
+    }
+  }
+  // this head's keep decisions as a bitmap (bit p: e_hat_p - tau_hat > -delta)
+  const double ndelta = -(double)a.delta;
+  const int nwords = (n_b + 63) / 64;
+  if (in_regs) {
 #pragma unroll
-      for (int i = 0; i < NW; ++i) {
-        F += part[it & 1][i][0];
-        dF += part[it & 1][i][1];
+    for (int i = 0; i < PPT; ++i) {
+      const int p0 = i * kTauHatThreads + w * kWave;  // this wave's 64 pages
+      if (p0 < n_b) {
+        const unsigned long long bal = __ballot(p0 + lane < n_b && (double)er[i] - t > ndelta);
+        if (lane == 0) st_dev(kbits + p0 / 64, (uint64_t)bal);
       }
-      if (F == 1.0) break;
-      if (F > 1.0) lo = t; else hi = t;
-      const double tol = 2e-7 * fmax(1.0, fabs(t));
-      const bool newton = F > 0.0 && dF < 0.0;
-      double cand = newton ? t - F * log(F) / dF : t;
-      if (newton && fabs(cand - t) <= tol) {
-        t = cand;
-        break;
-      }
-      if (!(cand > lo && cand < hi)) {
-        if (lo > -INFINITY && hi < INFINITY) cand = 0.5 * (lo + hi);
-        else if (hi < INFINITY) cand = hi - fmax(1.0, fabs(hi));
-        else cand = lo + fmax(1.0, fabs(lo));
-      }
-      t = cand;
-      if (hi - lo <= tol) break;
+    }
+  } else {
+    for (int p0 = w * kWave; p0 < n_b; p0 += kTauHatThreads) {
+      const int p = p0 + lane;
+      const unsigned long long bal = __ballot(p < n_b && (double)eh[p] - t > ndelta);
+      if (lane == 0) st_dev(kbits + p0 / 64, (uint64_t)bal);
     }
   }
   if (tid == 0) {
-    st_dev(a.tau_hat + bh, t);  // read by the unit's last block
+    st_dev(a.tau_hat + bh, t);  // read by the group's last block
     if (a.tau_hat_out) a.tau_hat_out[bh] = (float)t;
-    wait_mem();
-    s_last = atomicAdd(a.done + unit, 1u) == (uint32_t)(G - 1);
   }
+  wait_mem();  // every wave's device-scope stores have completed
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(a.done + unit, 1u) == (uint32_t)(G - 1);
   __syncthreads();
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (tid == 0) st_dev(a.done + unit, 0u);  // ready for the next call
-  gauss_keep_unit<G>(a, b, g);
+
+  // ---- the group's last block: union of the heads' bitmaps, ascending ids ----
+  int32_t* out = a.sel + (size_t)unit * a.cap;
+  if (n_b == 0) {
+    if (tid == 0) a.sel_count[unit] = 0;
+    return;
+  }
+  const uint64_t* kb0 = a.keep_bits + ((size_t)b * a.n_q_heads + (size_t)g * G) * a.keep_words;
+  int run = 0;
+  for (int w0 = 0; w0 < nwords; w0 += kTauHatThreads) {
+    const int wi = w0 + tid;
+    uint64_t word = 0;
+    if (wi < nwords) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) word |= kb0[(size_t)hh * a.keep_words + wi];
+    }
+    int tot;
+    int pos = run + block_exclusive_scan(__popcll(word), redi, &tot);
+    while (word) {
+      const int j = __ffsll((unsigned long long)word) - 1;
+      out[pos++] = wi * 64 + j;
+      word &= word - 1;
+    }
+    run += tot;
+  }
+  if (run > 0) {
+    if (tid == 0) a.sel_count[unit] = run;
+    return;
+  }
+  gauss_floor_unit<G>(a, b, g, n_b, out, unit);
 }
 
 // ---------------------------------------------------------------------------
