@@ -306,16 +306,24 @@ template <typename T> __device__ T block_min(T v, T* red) {
   return r;
 }
 
+// Inclusive prefix sum across the wave: row shifts by 1, 2, 4, 8 (lanes
+// without a source add 0), then lane 15 of rows 0 and 2 is added to rows 1
+// and 3 and lane 31 to rows 2 and 3 (row broadcasts).  Whole wave active.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
 // Exclusive prefix sum over the block (blockDim.x multiple of 64, <= 1024);
 // `red` holds >= 17 ints.  Returns the exclusive prefix, *total the sum.
 __device__ inline int block_exclusive_scan(int v, int* red, int* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += t;
-  }
+  const int inc = wave_incl_scan(v);
   __syncthreads();
   if (lane == 63) red[w] = inc;
   __syncthreads();

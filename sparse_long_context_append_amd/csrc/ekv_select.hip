@@ -270,14 +270,13 @@ __device__ void topk_block(const SelectArgs& a, const float* s, int n_b, int k_e
         const uint32_t c0 = hb[4 * lane], c1 = hb[4 * lane + 1], c2 = hb[4 * lane + 2], c3 = hb[4 * lane + 3];
         // this histogram is used again two passes later: clear it now
         hb[4 * lane] = 0u; hb[4 * lane + 1] = 0u; hb[4 * lane + 2] = 0u; hb[4 * lane + 3] = 0u;
-        uint32_t S = c0 + c1 + c2 + c3;  // suffix sum over lanes: bins >= 4 lane
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t t = __shfl_down(S, o, kWave);
-          if (lane + o < 64) S += t;
-        }
-        uint32_t Snext = __shfl_down(S, 1, kWave);
-        if (lane == 63) Snext = 0u;
+        // suffix sums over lanes (bins >= 4 lane, and >= 4 lane + 4) from
+        // the inclusive prefix and the total
+        const uint32_t c = c0 + c1 + c2 + c3;
+        const uint32_t inc = (uint32_t)wave_incl_scan((int)c);
+        const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+        const uint32_t Snext = total - inc;
+        const uint32_t S = Snext + c;
         if (S >= (uint32_t)rem && Snext < (uint32_t)rem) {
           uint32_t above = Snext;
           const uint32_t cs[4] = {c0, c1, c2, c3};
