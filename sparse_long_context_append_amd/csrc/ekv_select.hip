@@ -354,6 +354,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_gauss_kernel(SelectArgs a
   const int P = a.page_size, Hkv = a.n_kv_heads;
   // lane group (lane / 8) of wave w takes pages base + 32 n + 8 w + lane / 8
   const int pbase = blockIdx.x * kGaussPagesPerBlock + w * 8 + (lane >> 3);
+  // the group's queries, staged once per block in LDS (every lane reads
+  // its 16-float slice of each head from there, not through the L1)
+  __shared__ float4 s_q[G * D / 4];
+  float4 qload = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4* qg = reinterpret_cast<const float4*>(a.q + ((size_t)b * a.n_q_heads + (size_t)g * G) * D);
+  if (tid < G * D / 4) qload = qg[tid];
   int phys[NP];
   int n_b = 0;
 #pragma unroll
@@ -368,24 +374,24 @@ __global__ __launch_bounds__(kScoreThreads) void score_gauss_kernel(SelectArgs a
       for (int i = 0; i < NL; ++i) v[n][i] = rec[sub + 8 * i];
     }
   }
+  if (tid < G * D / 4) s_q[tid] = qload;
+  __syncthreads();
   const double a1s = ((double)a.alpha - 1.0) * (double)a.scale;
 #pragma unroll
   for (int n = 0; n < NP; ++n) {
     float fa[G], fb[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) { fa[h] = 0.f; fb[h] = 0.f; }
-    if (phys[n] >= 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float* qh = a.q + ((size_t)b * a.n_q_heads + (size_t)g * G + h) * D;
+    for (int h = 0; h < G; ++h) {
+      fa[h] = 0.f;
+      fb[h] = 0.f;
+      if (phys[n] >= 0) {
 #pragma unroll
         for (int i = 0; i < NLH; ++i) {
-          const float4 qv = *reinterpret_cast<const float4*>(qh + 4 * (sub + 8 * i));
-          const float4 mv = v[n][i], sv = v[n][i + NLH];
-          fa[h] = fmaf(qv.x, mv.x, fa[h]); fa[h] = fmaf(qv.y, mv.y, fa[h]);
-          fa[h] = fmaf(qv.z, mv.z, fa[h]); fa[h] = fmaf(qv.w, mv.w, fa[h]);
-          fb[h] = fmaf(qv.x * qv.x, sv.x, fb[h]); fb[h] = fmaf(qv.y * qv.y, sv.y, fb[h]);
-          fb[h] = fmaf(qv.z * qv.z, sv.z, fb[h]); fb[h] = fmaf(qv.w * qv.w, sv.w, fb[h]);
+          const float4 q4 = s_q[h * (D / 4) + sub + 8 * i], mv = v[n][i], sv = v[n][i + NLH];
+          fa[h] = fmaf(q4.x, mv.x, fa[h]); fa[h] = fmaf(q4.y, mv.y, fa[h]);
+          fa[h] = fmaf(q4.z, mv.z, fa[h]); fa[h] = fmaf(q4.w, mv.w, fa[h]);
+          fb[h] = fmaf(q4.x * q4.x, sv.x, fb[h]); fb[h] = fmaf(q4.y * q4.y, sv.y, fb[h]);
+          fb[h] = fmaf(q4.z * q4.z, sv.z, fb[h]); fb[h] = fmaf(q4.w * q4.w, sv.w, fb[h]);
         }
       }
     }
