@@ -330,6 +330,30 @@ def summarize(spec, r):
     return out
 
 
+def run_sweep(args, torch, timer):
+    """Sparse step and full-cache decode of one sequence (32/8 heads, d=128,
+    pages of 64) at contexts 32K..1M: top-k on the bounding-box bound with a
+    2% page budget (isotropic keys with needles), and the Gaussian selector
+    (clustered keys)."""
+    import math
+    rows = []
+    for name in ("c4", "c4g"):
+        for ctx in (1 << 15, 1 << 16, 1 << 17, 1 << 18, 1 << 19, 1 << 20):
+            over = {"context": ctx}
+            if name == "c4":
+                over["top_k"] = math.ceil(0.02 * ctx / 64)
+            spec = W.make_spec(name, **over)
+            r = measure(spec, args.steps, args.warmup, torch, timer, do_dense=True, do_graph=False)
+            s = summarize(spec, r)
+            rows.append({"selector": spec.policy, "context": ctx, "top_k": spec.top_k if spec.policy == "bbox" else None,
+                         **{k: s[k] for k in ("us_per_step", "us_p10", "us_p90", "bytes_per_step", "effective_gbs",
+                                              "pages_selected", "pages_total", "support_mean", "dense_us_per_step",
+                                              "speedup_vs_dense")}})
+            log(f"sweep {spec.policy} {ctx}: {s['us_per_step']} us, dense {s['dense_us_per_step']} us")
+    print(json.dumps({"metric": METRIC, "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "data": "synthetic", "sweep": rows}), flush=True)
+
+
 def copy_probe(mib):
     """A plain copy kernel of known size: HBM read and write counters of its
     dispatches calibrate the counters of the path's kernels."""
@@ -379,6 +403,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--context", type=int, default=0, help="override the workload's context (scaling sweeps)")
     ap.add_argument("--cpu-units", type=int, default=2, help="(sequence, KV head) units the CPU oracle is timed on")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the headline line: context sweep 32K..1M of the top-2%% and Gaussian "
+                         "million-token workloads (one JSON line with a 'sweep' list)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (counter calibration)")
     args = ap.parse_args()
@@ -392,6 +419,9 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     timer = Timer(torch)
+    if args.sweep:
+        run_sweep(args, torch, timer)
+        return
     over = {"context": args.context} if args.context else {}
     spec = W.make_spec(args.workload, **over)
     log(f"device {torch.cuda.get_device_name(0)}; workload {spec.name}")

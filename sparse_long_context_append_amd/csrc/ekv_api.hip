@@ -244,6 +244,7 @@ ekv_status ekv_entmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const
   a.max_items = (int)L.max_items;
   a.item_cnt = at<int32_t>(workspace, L.item_cnt);
   a.item_max = at<float>(workspace, L.item_max);
+  a.item_lb = at<float>(workspace, L.item_lb);
   a.cand_x = at<float>(workspace, L.cand_x);
   a.cand_t = at<int32_t>(workspace, L.cand_t);
   a.cand_r = at<int32_t>(workspace, L.cand_r);

@@ -28,6 +28,7 @@ struct Layout {
   size_t keep_bits; // u64 [B*Hq][keep_words(max_pages)] Gaussian keep bitmaps
   size_t item_cnt;  // i32 [B*Hq*max_items] candidates kept by each decode work item
   size_t item_max;  // f32 [B*Hq*max_items] per item maximum score
+  size_t item_lb;   // f32 [B*Hq*max_items] per item lower bound on the head's threshold
   size_t cand_x;    // f32 [B*Hq*max_items*64] candidate scores, one region per item
   size_t cand_t;    // i32 [...] candidate logical token ids
   size_t cand_r;    // i32 [...] candidate physical rows (page * P + slot)
@@ -59,6 +60,7 @@ inline Layout make_layout(int B, int Hkv, int Hq, int max_pages, int P) {
   L.keep_bits = off; off = align256(off + 8 * bh * keep_words(max_pages));
   L.item_cnt = off; off = align256(off + 4 * bh * L.max_items);
   L.item_max = off; off = align256(off + 4 * bh * L.max_items);
+  L.item_lb = off;  off = align256(off + 4 * bh * L.max_items);
   L.cand_x = off;   off = align256(off + 4 * bh * tok);
   L.cand_t = off;   off = align256(off + 4 * bh * tok);
   L.cand_r = off;   off = align256(off + 4 * bh * tok);
@@ -273,17 +275,28 @@ template <typename T> __device__ T block_sum(T v, T* red) {
   for (int i = 1; i < nw; ++i) r += red[i];
   return r;
 }
-// Three sums at once; `red` holds >= 3 * 16 doubles.
-__device__ inline void block_sum3(double& a, double& b, double& c, double* red) {
+// K sums at once; `red` holds >= K * (waves per block) doubles.
+template <int K> __device__ inline void block_sums(double (&v)[K], double* red) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  a = wave_sum(a);
-  b = wave_sum(b);
-  c = wave_sum(c);
+#pragma unroll
+  for (int k = 0; k < K; ++k) v[k] = wave_sum(v[k]);
   __syncthreads();
-  if (lane == 0) { red[3 * w] = a; red[3 * w + 1] = b; red[3 * w + 2] = c; }
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) red[K * w + k] = v[k];
+  }
   __syncthreads();
-  a = red[0]; b = red[1]; c = red[2];
-  for (int i = 1; i < nw; ++i) { a += red[3 * i]; b += red[3 * i + 1]; c += red[3 * i + 2]; }
+#pragma unroll
+  for (int k = 0; k < K; ++k) v[k] = red[k];
+  for (int i = 1; i < nw; ++i) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) v[k] += red[K * i + k];
+  }
+}
+__device__ inline void block_sum3(double& a, double& b, double& c, double* red) {
+  double v[3] = {a, b, c};
+  block_sums<3>(v, red);
+  a = v[0]; b = v[1]; c = v[2];
 }
 template <typename T> __device__ T block_max(T v, T* red) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;

@@ -135,6 +135,19 @@ __device__ __forceinline__ void resolve_refs(const DecodeArgs& a, int u, int b, 
 // 16 tokens of a wave; the fp32 accumulator runs over the D/32 k blocks.
 // Lane l ends with head l/16 of token l%16: x = (c0 + c1) + c2.
 // ---------------------------------------------------------------------------
+// n^-(alpha-1): the largest distance below a level shared by n scores at
+// which their weights alone reach 1.
+// Evaluated in float and rounded up by a relative 1e-5, so the bound
+// stays below the exact one.
+__device__ __forceinline__ double count_pow(int n, float alpha) {
+  const float nf = (float)n;
+  float v;
+  if (alpha == 2.0f) v = 1.f / nf;
+  else if (alpha == 1.5f) v = 1.f / sqrtf(nf);
+  else v = exp2f(-(alpha - 1.f) * log2f(nf));
+  return (double)v * (1.0 + 1e-5);
+}
+
 template <int D, int G, int SUB>
 __global__ __launch_bounds__(kDecThreads) void gather_mfma_kernel(DecodeArgs a, int slots) {
   constexpr int KB = D / 32;
@@ -195,18 +208,36 @@ __global__ __launch_bounds__(kDecThreads) void gather_mfma_kernel(DecodeArgs a, 
       if (col == 0) s_max[s][w][grp] = m;
     }
     __syncthreads();
-    // candidates: above (super-item maximum) - 1, a lower bound on tau
+    // candidates: above a lower bound on tau (tokens at or below it have
+    // weight 0).  The super-item maximum gives msup - 1 (the top token alone
+    // has weight at most 1).  More generally, if n tokens lie at or above a
+    // level l, tau >= l - n^-(alpha-1) (a subset's threshold never exceeds
+    // the full set's); this wave's tokens of the head are counted at
+    // l = msup - 1/8, - 1/4, - 1/2.
     float m[SUB], msup = -INFINITY;
 #pragma unroll
     for (int s = 0; s < SUB; ++s) {
       m[s] = fmaxf(fmaxf(s_max[s][0][grp], s_max[s][1][grp]), fmaxf(s_max[s][2][grp], s_max[s][3][grp]));
       msup = fmaxf(msup, m[s]);
     }
+    double lb = (double)msup - 1.0;
+#pragma unroll
+    for (int ci = 0; ci < 3; ++ci) {
+      const float lvl = msup - 0.125f * (float)(1 << ci);
+      int n = 0;
+#pragma unroll
+      for (int s = 0; s < SUB; ++s) {
+        const unsigned long long bal = __ballot(grp < G && x[s] >= lvl);
+        n += __popc((uint32_t)(bal >> (16 * grp)) & 0xffffu);
+      }
+      if (n > 0) lb = fmax(lb, (double)lvl - count_pow(n, a.alpha));
+    }
+    lb -= 1e-6 * fmax(1.0, fabs((double)msup));  // margin for the rounding of x
     bool keep[SUB];
     uint32_t bits[SUB];
 #pragma unroll
     for (int s = 0; s < SUB; ++s) {
-      keep[s] = grp < G && msup > -INFINITY && (double)x[s] > (double)msup - 1.0;
+      keep[s] = grp < G && msup > -INFINITY && (double)x[s] > lb;
       const unsigned long long bal = __ballot(keep[s]);
       bits[s] = (uint32_t)(bal >> (16 * grp)) & 0xffffu;
       if (col == 0) s_cnt[s][w][grp] = __popc(bits[s]);
@@ -234,6 +265,7 @@ __global__ __launch_bounds__(kDecThreads) void gather_mfma_kernel(DecodeArgs a, 
         if (w == 0 && col == 0) {
           a.item_cnt[bh * a.max_items + j] = tot;
           a.item_max[bh * a.max_items + j] = m[s];
+          a.item_lb[bh * a.max_items + j] = msup > -INFINITY ? __double2float_rd(lb) : -INFINITY;
         }
       }
     }
@@ -334,6 +366,7 @@ __global__ __launch_bounds__(kDecThreads) void gather_valu_kernel(DecodeArgs a, 
       if (lane == 0) {
         a.item_cnt[bh * a.max_items + j] = __popcll(bal);
         a.item_max[bh * a.max_items + j] = m;
+        a.item_lb[bh * a.max_items + j] = m > -INFINITY ? __double2float_rd((double)m - 1.0) : -INFINITY;
       }
     }
     __syncthreads();
@@ -537,6 +570,7 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
   float* out = a.out + bh * D;
   const int32_t* icnt = a.item_cnt + bh * a.max_items;
   const float* imax = a.item_max + bh * a.max_items;
+  const float* ilb = a.item_lb + bh * a.max_items;
   const float* cx = a.cand_x + bh * tok_per_bh;
   const int32_t* ct = a.cand_t + bh * tok_per_bh;
   const int32_t* cr = a.cand_r + bh * tok_per_bh;
@@ -548,19 +582,35 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
   const bool few_items = n_items <= IPT * kTauThreads;
   int loc[IPT], lsum = 0;
   float lmx[IPT];
-  float lmax = -INFINITY;
+  float lmax = -INFINITY, llb = -INFINITY;
   if (few_items) {
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
       const int jj = IPT * tid + i;
       loc[i] = jj < n_items ? icnt[jj] : 0;
       lmx[i] = jj < n_items ? imax[jj] : -INFINITY;
+      llb = fmaxf(llb, jj < n_items ? ilb[jj] : -INFINITY);
       lmax = fmaxf(lmax, lmx[i]);
     }
   } else {
-    for (int j = tid; j < n_items; j += blockDim.x) lmax = fmaxf(lmax, imax[j]);
+    // eight loads in flight per thread per round
+    for (int j0 = tid; j0 < n_items; j0 += 8 * kTauThreads) {
+      float vm[8], vl[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u * kTauThreads;
+        vm[u] = j < n_items ? imax[j] : -INFINITY;
+        vl[u] = j < n_items ? ilb[j] : -INFINITY;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        lmax = fmaxf(lmax, vm[u]);
+        llb = fmaxf(llb, vl[u]);
+      }
+    }
   }
   const float mf = block_max(lmax, reinterpret_cast<float*>(redd));
+  const float lbf = block_max(llb, reinterpret_cast<float*>(redd));
   if (!(mf > -INFINITY)) {  // no pages, or every page invalid (flagged): empty result
     for (int e = tid; e < D; e += blockDim.x) out[e] = 0.f;
     if (tid == 0) {
@@ -571,7 +621,45 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
     return;
   }
   const double m = mf;
-  const double thr = m - 1.0;
+  // Lower bound on tau: the largest of the items' own bounds (each at least
+  // its item's maximum - 1, so this is at least m - 1), and the count bound
+  // on the item maxima: n items with maximum at or above a level l hold n
+  // scores there, so tau >= l - n^-(alpha-1); levels m - 1/32 .. m - 1/4.
+  double thr = fmax(m - 1.0, (double)lbf);
+  {
+    float lvl[4];
+    double nk[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      lvl[k] = mf - 0.03125f * (float)(1 << k);
+      nk[k] = 0.0;
+    }
+    if (few_items) {
+#pragma unroll
+      for (int i = 0; i < IPT; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) nk[k] += lmx[i] >= lvl[k] ? 1.0 : 0.0;
+    } else {
+      for (int j0 = tid; j0 < n_items; j0 += 8 * kTauThreads) {
+        float vm[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int j = j0 + u * kTauThreads;
+          vm[u] = j < n_items ? imax[j] : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) nk[k] += vm[u] >= lvl[k] ? 1.0 : 0.0;
+      }
+    }
+    block_sums<4>(nk, redd);
+    double cb = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (nk[k] > 0.0) cb = fmax(cb, (double)lvl[k] - count_pow((int)nk[k], a.alpha));
+    thr = fmax(thr, cb - 1e-6 * fmax(1.0, fabs(m)));
+  }
 
   // ---- collect candidates above m - 1, in item order (an item whose
   // maximum is at most m - 1 holds none) ----
@@ -643,60 +731,82 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
     }
   }
   if (!done) {
-    // general case: chunks of items; pass 0 counts, pass 1 writes (to LDS
-    // when the kept candidates fit, else to the workspace list)
-    for (int pass = 0; pass < 2; ++pass) {
-      int run = 0;
-      for (int c0 = 0; c0 < n_items; c0 += kTauItemChunk) {
-        const int nc = min(kTauItemChunk, n_items - c0);
-        int lc[4], sum = 0;
+    // general case: chunks of up to 1024 items.  Per chunk the non-empty
+    // items are listed with their first candidate's rank (one scan); the raw
+    // candidates are then read RPT per thread per round (one round of loads,
+    // one scan), and the kept ones appended to the workspace list, which is
+    // copied on chip afterwards when it fits.
+    float* ox = a.ovf_x + bh * tok_per_bh;
+    int32_t* ot = a.ovf_t + bh * tok_per_bh;
+    int32_t* orow = a.ovf_r + bh * tok_per_bh;
+    int run = 0;
+    for (int c0 = 0; c0 < n_items; c0 += kTauItemChunk) {
+      const int nc = min(kTauItemChunk, n_items - c0);
+      int lc[4], sum = 0, nz = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int jj = 4 * tid + i;
-          lc[i] = jj < nc && (double)imax[c0 + jj] > thr ? icnt[c0 + jj] : 0;
-          sum += lc[i];
-        }
-        int raw_tot;
-        int base = block_exclusive_scan(sum, redi, &raw_tot);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (4 * tid + i < nc) s_pre[4 * tid + i] = base;
-          base += lc[i];
-        }
-        if (tid == 0) s_pre[nc] = raw_tot;
-        __syncthreads();
-        for (int i0 = 0; i0 < raw_tot; i0 += blockDim.x) {
-          const int i = i0 + tid;
-          float x = -INFINITY;
-          size_t at = 0;
-          if (i < raw_tot) {
-            int lo = 0, hi = nc;  // s_pre[lo] <= i < s_pre[hi]
-            while (hi - lo > 1) {
-              const int mid = (lo + hi) >> 1;
-              if (s_pre[mid] <= i) lo = mid; else hi = mid;
-            }
-            at = (size_t)(c0 + lo) * kItemTokens + (i - s_pre[lo]);
-            x = cx[at];
-          }
-          const bool keep = (double)x > thr;
-          int tot;
-          const int pos = run + block_exclusive_scan(keep ? 1 : 0, redi, &tot);
-          if (pass == 1 && keep) {
-            if (in_lds) {
-              lx[pos] = x; lt[pos] = ct[at]; lr[pos] = cr[at];
-            } else {
-              a.ovf_x[bh * tok_per_bh + pos] = x;
-              a.ovf_t[bh * tok_per_bh + pos] = ct[at];
-              a.ovf_r[bh * tok_per_bh + pos] = cr[at];
-            }
-          }
-          run += tot;
-        }
-        __syncthreads();
+      for (int i = 0; i < 4; ++i) {
+        const int jj = 4 * tid + i;
+        lc[i] = jj < nc && (double)imax[c0 + jj] > thr ? icnt[c0 + jj] : 0;
+        sum += lc[i];
+        nz += lc[i] > 0;
       }
-      N = run;
-      if (pass == 0) in_lds = N <= kLdsCands;
+      int packed_tot;
+      const int packed = block_exclusive_scan((nz << 17) | sum, redi, &packed_tot);
+      const int raw_tot = packed_tot & 0x1ffff, n_ne = packed_tot >> 17;
+      int base = packed & 0x1ffff, rank = packed >> 17;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (lc[i] > 0) {
+          s_pre[rank] = base;
+          sm.s_item[rank] = c0 + 4 * tid + i;
+          ++rank;
+        }
+        base += lc[i];
+      }
+      if (tid == 0) s_pre[n_ne] = raw_tot;
+      __syncthreads();
+      for (int r0 = 0; r0 < raw_tot; r0 += RPT * kTauThreads) {
+        float xv[RPT];
+        size_t av[RPT];
+        const int i0 = r0 + RPT * tid;
+        int k = 0;
+        if (i0 < raw_tot) {
+          int lo = 0, hi = n_ne;  // s_pre[lo] <= i0 < s_pre[hi]
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_pre[mid] <= i0) lo = mid; else hi = mid;
+          }
+          k = lo;
+        }
+#pragma unroll
+        for (int c = 0; c < RPT; ++c) {
+          const int i = i0 + c;
+          xv[c] = -INFINITY;
+          av[c] = 0;
+          if (i < raw_tot) {
+            while (s_pre[k + 1] <= i) ++k;
+            av[c] = (size_t)sm.s_item[k] * kItemTokens + (i - s_pre[k]);
+            xv[c] = cx[av[c]];
+          }
+        }
+        int kc = 0;
+#pragma unroll
+        for (int c = 0; c < RPT; ++c) kc += (double)xv[c] > thr;
+        int tot;
+        int pos = run + block_exclusive_scan(kc, redi, &tot);
+#pragma unroll
+        for (int c = 0; c < RPT; ++c)
+          if ((double)xv[c] > thr) { ox[pos] = xv[c]; ot[pos] = ct[av[c]]; orow[pos] = cr[av[c]]; ++pos; }
+        run += tot;
+      }
+      __syncthreads();  // s_pre / s_item are rewritten by the next chunk
     }
+    N = run;
+    in_lds = N <= kLdsCands;
+    wait_mem();  // this thread's list entries are written before others read them
+    __syncthreads();
+    if (in_lds)
+      for (int i = tid; i < N; i += kTauThreads) { lx[i] = ox[i]; lt[i] = ot[i]; lr[i] = orow[i]; }
   }
   __syncthreads();
   float* xs = in_lds ? lx : a.ovf_x + bh * tok_per_bh;
@@ -744,6 +854,7 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
       if (a.support_idx && pos < a.support_cap) a.support_idx[bh * a.support_cap + pos] = tok;
     }
     nsup += tot;
+    if (!in_lds) wait_mem();  // workspace list entries are read by other threads next
     __syncthreads();
   }
   ps = block_sum(ps, redd);

@@ -8,7 +8,7 @@ namespace ekv {
 // Limits the kernels are compiled for (checked on the host before launch).
 constexpr int kMaxGroup = 8;         // query heads per KV head
 constexpr int kMaxUnits = 4096;      // batch * n_kv_heads
-constexpr int kLdsCands = 1024;      // candidates kept in LDS by the threshold solve
+constexpr int kLdsCands = 4096;      // candidates kept in LDS by the threshold solve
 
 struct AppendArgs {
   int batch, n_kv_heads, page_size, head_dim, kv_dtype, max_pages, n_phys, n_new;
@@ -68,6 +68,7 @@ struct DecodeArgs {
   int max_items;  // per (sequence, query head)
   int32_t* item_cnt;
   float* item_max;
+  float* item_lb;
   float* cand_x;
   int32_t* cand_t;
   int32_t* cand_r;

@@ -24,8 +24,8 @@ constexpr int kBboxPagesPerBlock = 64;   // 16 pages per wave
 constexpr int kGaussPagesPerBlock = 64;  // 8 lane groups per wave, 2 pages each
 constexpr int kSelThreads = 1024;
 constexpr int kTauHatThreads = 1024;
-constexpr int kTauHatPPT = 8;            // pages per thread held in registers (n_b <= 8192)
-constexpr int kTauHatLive = 4096;        // pages alive at the start point kept in LDS
+constexpr int kTauHatPPT = 16;           // pages per thread held in registers (n_b <= 16384)
+constexpr int kTauHatLive = 8192;        // pages alive at the start point kept in LDS
 
 __device__ __forceinline__ int clamp_len(int L, int max_pages, int P, uint32_t* status) {
   if (L < 0 || (long long)L > (long long)max_pages * P) {

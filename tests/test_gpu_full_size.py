@@ -60,6 +60,17 @@ def test_c3_full_gaussian_128k():
     assert sess.device_status() == 0
 
 
+def test_c4g_full_gaussian_million_tokens():
+    """The million-token shape with clustered keys and the Gaussian selector."""
+    spec = W.make_spec("c4g")
+    sess, _ = _session(spec)
+    q = W.queries(spec)
+    res = run_step(sess, spec, q)
+    _all_units_sane(res)
+    check_step(spec, res, q, [(0, 3)])
+    assert sess.device_status() == 0
+
+
 def test_c5_full_batched_appends():
     """16 sequences of 16K-64K tokens on permuted pages, one token appended
     per sequence per step for 64 steps; sampled units checked at the first,

@@ -120,9 +120,9 @@ def test_gauss_group_sizes(hkv):
 
 
 def test_gauss_more_pages_than_register_tiles():
-    """8199 pages of 16 tokens: the threshold estimate streams the page
-    statistics from memory and the keep step takes its looped path."""
-    spec = W.make_spec("c3", batch=1, context=8198 * 16 + 7, page_size=16, n_q_heads=4, n_kv_heads=1)
+    """16392 pages of 16 tokens: the threshold estimate streams the page
+    statistics from memory instead of holding them in registers."""
+    spec = W.make_spec("c3", batch=1, context=16391 * 16 + 7, page_size=16, n_q_heads=4, n_kv_heads=1)
     sess, _ = _session(spec)
     q = W.queries(spec)
     check_step(spec, run_step(sess, spec, q), q, all_units(spec))

@@ -125,3 +125,21 @@ def test_bf16_upcast_exact():
     assert v[0] == 1.0 and v[1] == -1.0 and v[3] == 0.0
     assert v[2] == 3.140625  # 0x4049 = 1.5703125 * 2
     assert v[5] == pytest.approx(3.3895313892515355e38)
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0, 1.3])
+def test_count_bound_on_threshold(alpha):
+    """If n scores lie at or above a level l, tau >= l - n^-(alpha-1): those
+    scores alone (a subset) already have a threshold at least that high.  The
+    decode path filters candidates with this bound."""
+    rng = np.random.default_rng(11)
+    for trial in range(300):
+        n_tok = int(rng.integers(1, 400))
+        spread = [0.05, 0.5, 3.0][trial % 3]
+        x = rng.standard_normal(n_tok) * spread
+        tau = entmax.threshold_sort(x, alpha) if alpha in (1.5, 2.0) else entmax.threshold_bisect(x, alpha)
+        m = x.max()
+        for c in (0.0, 0.125, 0.25, 0.5, 1.0):
+            lvl = m - c
+            n = int((x >= lvl).sum())
+            assert tau >= lvl - n ** (-(alpha - 1.0)) - 1e-12

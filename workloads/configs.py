@@ -21,6 +21,10 @@ these synthetic inputs stand in for them):
   c5  B=16, 32/8, d=128, L_b ~ U{16384..65536}, P=16, randomly permuted
       physical pages, clustered keys as c3, alpha=1.5, Gaussian selector,
       64 decode steps each appending one token per sequence.
+  c4g the million-token shape of c4 with c3's clustered keys and the
+      Gaussian selector (margin 0.5), alpha=1.5: the selector the pages
+      report their million-token speedups for, on keys it can separate
+      (on isotropic keys it keeps almost nothing).
 """
 from __future__ import annotations
 
@@ -30,7 +34,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-CONFIG_NAMES = ("c1", "c2", "c3", "c4", "c5")
+CONFIG_NAMES = ("c1", "c2", "c3", "c4", "c5", "c4g")
 
 # stream tags
 _T_Q, _T_K, _T_V, _T_NEEDLE_POS, _T_NEEDLE_NOISE, _T_CENTRES, _T_RUNS, _T_LENS, _T_PERM = range(9)
@@ -92,6 +96,8 @@ _BASE = {
     "c5": WorkloadSpec("c5", 16, 32, 8, 128, 16, "bf16", 1.5, "gauss", delta=0.5,
                        key_kind="clusters", ctx_lo=16384, ctx_hi=65536,
                        permute_pages=True, steps=64, seed=1004),
+    "c4g": WorkloadSpec("c4g", 1, 32, 8, 128, 64, "bf16", 1.5, "gauss", delta=0.5,
+                        key_kind="clusters", context=1 << 20, seed=1005),
 }
 
 
