@@ -13,6 +13,7 @@ Modules:
   scoring   bounding-box upper bound and Gaussian page score model
   select    fixed-budget top-k and the Gaussian-aware threshold selector
   decode    exact entmax attention over a token set, dropped mass, error bound
+  softmax   softmax attention over a token set and its dropped mass (comparison)
 
 Where the pages are silent (the bound's formula, the Gaussian expectation,
 the estimated maximum, GQA sharing, tie rules) each function states the
@@ -20,4 +21,4 @@ reading it implements.  Parity status: every function is pinned by tests in
 tests/test_oracle_*.py except the ones whose docstring says
 "parity unpinned".
 """
-from . import entmax, metadata, scoring, select, decode  # noqa: F401
+from . import entmax, metadata, scoring, select, decode, softmax  # noqa: F401

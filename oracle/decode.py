@@ -65,3 +65,11 @@ def dropped_mass(full: dict, kept_tokens: np.ndarray) -> float:
 def value_norm_bound(v: np.ndarray) -> float:
     """B = max_j ||v_j||_2."""
     return float(np.sqrt((np.asarray(v, dtype=np.float64) ** 2).sum(axis=1)).max())
+
+
+def support_retention(full: dict, kept_tokens: np.ndarray) -> float:
+    """Fraction of the full-cache support that lies in the kept set."""
+    sup = full["support"]
+    if sup.size == 0:
+        return 1.0
+    return float(np.isin(sup, np.asarray(kept_tokens, dtype=np.int64)).mean())
