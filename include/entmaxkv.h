@@ -203,13 +203,34 @@ ekv_status ekv_select_pages(const ekv_cache* cache, const ekv_seqs* seqs, const 
  *   psum       optional [batch][n_q_heads] float32: sum_j p_j
  *   support_idx optional [batch][n_q_heads][support_cap] int32: ascending
  *              logical token ids of the support (first support_cap of them)
+ *   support_p  optional [batch][n_q_heads][support_cap] float32: their
+ *              weights p_j, in the same order (needs support_cap >= 1)
  * Scores are accumulated in float32; the threshold is finalised in float64.
  */
 ekv_status ekv_entmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const float* q,
                              int32_t n_q_heads, float alpha, float scale, const int32_t* sel,
                              const int32_t* sel_count, int32_t cap, float* out, float* tau,
                              int32_t* support_count, float* psum, int32_t* support_idx,
-                             int32_t support_cap, void* workspace, size_t ws_bytes, void* stream);
+                             float* support_p, int32_t support_cap, void* workspace, size_t ws_bytes,
+                             void* stream);
+
+/*
+ * Softmax attention decode over the same page list, the baseline the
+ * EntmaxKV summary compares against (sec. 1 and 3: softmax gives every
+ * token a positive weight, so a dropped page always leaves some error):
+ * z_j = scale q.k_j over the selected pages' tokens (sel != NULL) or the
+ * whole cache (sel == NULL), p = softmax(z) over that set, out = sum_j p_j v_j.
+ *   lse   optional [batch][n_q_heads] float32: log sum_j exp(z_j) over the
+ *         set (-inf when it is empty); the full-cache mass outside a kept
+ *         set J is 1 - exp(lse_J - lse_full)
+ * Other arguments as for ekv_entmax_decode.  Needs bf16 K/V and query
+ * groups of at most 4 heads (else EKV_ERR_UNSUPPORTED).  Accumulates in
+ * float32 with a running maximum per block, merged in a fixed order.
+ */
+ekv_status ekv_softmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const float* q,
+                              int32_t n_q_heads, float scale, const int32_t* sel,
+                              const int32_t* sel_count, int32_t cap, float* out, float* lse,
+                              void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Page scores only (diagnostics and parity checks).

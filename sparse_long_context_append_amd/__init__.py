@@ -9,6 +9,6 @@ from .binding import (  # noqa: F401
     EKV_OK, EKV_ERR_INVALID_ARG, EKV_ERR_UNSUPPORTED, EKV_ERR_WORKSPACE, EKV_ERR_CAPACITY, EKV_ERR_HIP,
     EKV_F32, EKV_BF16, EKV_SELECT_BBOX_TOPK, EKV_SELECT_GAUSS,
     EntmaxKVError, PagedCache, Sequences, lib, lib_path,
-    workspace_size, workspace_init, append_kv, select_pages, entmax_decode, score_pages,
+    workspace_size, workspace_init, append_kv, select_pages, entmax_decode, softmax_decode, score_pages,
     read_device_status, status_string, last_error,
 )

@@ -61,7 +61,9 @@ _SIGS = {
     "ekv_append_kv": (_i32, [_PC, _PS, _vp, _vp, _i32, _vp, _sz, _vp]),
     "ekv_select_pages": (_i32, [_PC, _PS, _vp, _i32, _PP, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
     "ekv_entmax_decode": (_i32, [_PC, _PS, _vp, _i32, ctypes.c_float, ctypes.c_float, _vp, _vp, _i32,
-                                 _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
+    "ekv_softmax_decode": (_i32, [_PC, _PS, _vp, _i32, ctypes.c_float, _vp, _vp, _i32, _vp, _vp, _vp, _sz,
+                                  _vp]),
     "ekv_score_pages": (_i32, [_PC, _PS, _vp, _i32, _PP, _vp, _vp, _sz, _vp]),
     "ekv_read_device_status": (_i32, [_vp, _sz, ctypes.POINTER(_i32)]),
     "ekv_status_string": (ctypes.c_char_p, [_i32]),
@@ -188,11 +190,19 @@ def score_pages(cache: PagedCache, seqs: Sequences, q, n_q_heads: int, *, policy
 
 def entmax_decode(cache: PagedCache, seqs: Sequences, q, n_q_heads: int, *, alpha: float, scale: float,
                   sel=None, sel_count=None, cap: int = 0, out, tau=None, support_count=None, psum=None,
-                  support_idx=None, support_cap: int = 0, ws, stream=None):
+                  support_idx=None, support_p=None, support_cap: int = 0, ws, stream=None):
     _check(lib().ekv_entmax_decode(ctypes.byref(cache.c()), ctypes.byref(seqs.c()), _ptr(q), n_q_heads,
                                    float(alpha), float(scale), _ptr(sel), _ptr(sel_count), cap, _ptr(out),
-                                   _ptr(tau), _ptr(support_count), _ptr(psum), _ptr(support_idx), support_cap,
-                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "entmax_decode")
+                                   _ptr(tau), _ptr(support_count), _ptr(psum), _ptr(support_idx),
+                                   _ptr(support_p), support_cap, _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)), "entmax_decode")
+
+
+def softmax_decode(cache: PagedCache, seqs: Sequences, q, n_q_heads: int, *, scale: float, sel=None,
+                   sel_count=None, cap: int = 0, out, lse=None, ws, stream=None):
+    _check(lib().ekv_softmax_decode(ctypes.byref(cache.c()), ctypes.byref(seqs.c()), _ptr(q), n_q_heads,
+                                    float(scale), _ptr(sel), _ptr(sel_count), cap, _ptr(out), _ptr(lse),
+                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "softmax_decode")
 
 
 def read_device_status(ws) -> int:

@@ -60,7 +60,7 @@ ekv_status check_heads(const ekv_cache* c, int32_t n_q_heads, int* group) {
 
 ekv_status check_ws(const ekv_cache* c, const ekv_seqs* s, int32_t n_q_heads, void* ws, size_t ws_bytes,
                     ekv::Layout* L) {
-  *L = ekv::make_layout(s->batch, c->n_kv_heads, n_q_heads, s->max_pages, c->page_size);
+  *L = ekv::make_layout(s->batch, c->n_kv_heads, n_q_heads, s->max_pages, c->page_size, c->head_dim);
   if (!ws) return fail(EKV_ERR_WORKSPACE, "workspace is NULL");
   if (!aligned16(ws)) return fail(EKV_ERR_WORKSPACE, "workspace must be 16-byte aligned");
   if (ws_bytes < L->total)
@@ -94,7 +94,8 @@ size_t ekv_workspace_size(const ekv_cache* cache, const ekv_seqs* seqs, int32_t 
   if (check_cache(cache) != EKV_OK || check_seqs(cache, seqs) != EKV_OK ||
       check_heads(cache, n_q_heads, &G) != EKV_OK)
     return 0;
-  return ekv::make_layout(seqs->batch, cache->n_kv_heads, n_q_heads, seqs->max_pages, cache->page_size).total;
+  return ekv::make_layout(seqs->batch, cache->n_kv_heads, n_q_heads, seqs->max_pages, cache->page_size,
+                          cache->head_dim).total;
 }
 
 ekv_status ekv_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
@@ -214,10 +215,10 @@ ekv_status ekv_score_pages(const ekv_cache* cache, const ekv_seqs* seqs, const f
   return hip_status(ekv::launch_score_gauss(a, s), "score_gauss launch");
 }
 
-ekv_status ekv_entmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const float* q, int32_t n_q_heads,
-                             float alpha, float scale, const int32_t* sel, const int32_t* sel_count, int32_t cap,
-                             float* out, float* tau, int32_t* support_count, float* psum, int32_t* support_idx,
-                             int32_t support_cap, void* workspace, size_t ws_bytes, void* stream) {
+// Validation and argument packing shared by the two decode entry points.
+ekv_status prepare_decode(const ekv_cache* cache, const ekv_seqs* seqs, const float* q, int32_t n_q_heads,
+                          float alpha, float scale, const int32_t* sel, const int32_t* sel_count, int32_t cap,
+                          float* out, void* workspace, size_t ws_bytes, ekv::DecodeArgs* a, ekv::Layout* L) {
   ekv_status st;
   int G = 0;
   if ((st = check_cache(cache)) != EKV_OK) return st;
@@ -228,20 +229,34 @@ ekv_status ekv_entmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const
   if (!(alpha > 1.f) || !isfinite(alpha)) return fail(EKV_ERR_INVALID_ARG, "alpha must be finite and > 1");
   if (!(scale > 0.f) || !isfinite(scale)) return fail(EKV_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (sel && (!sel_count || cap < 1)) return fail(EKV_ERR_INVALID_ARG, "sel needs sel_count and cap >= 1");
-  if (support_idx && support_cap < 1) return fail(EKV_ERR_INVALID_ARG, "support_idx needs support_cap >= 1");
+  if ((st = check_ws(cache, seqs, n_q_heads, workspace, ws_bytes, L)) != EKV_OK) return st;
+  *a = ekv::DecodeArgs{};
+  a->batch = seqs->batch; a->n_kv_heads = cache->n_kv_heads; a->n_q_heads = n_q_heads; a->group = G;
+  a->page_size = cache->page_size; a->head_dim = cache->head_dim; a->kv_dtype = cache->kv_dtype;
+  a->max_pages = seqs->max_pages; a->n_phys = cache->n_phys_pages;
+  a->page_table = seqs->page_table; a->seq_lens = seqs->seq_lens;
+  a->k = cache->k; a->v = cache->v; a->q = q; a->alpha = alpha; a->scale = scale;
+  a->sel = sel; a->sel_count = sel_count; a->cap = sel ? cap : 0;
+  a->out = out;
+  a->max_items = (int)L->max_items;
+  a->status = at<uint32_t>(workspace, L->status);
+  return EKV_OK;
+}
+
+ekv_status ekv_entmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const float* q, int32_t n_q_heads,
+                             float alpha, float scale, const int32_t* sel, const int32_t* sel_count, int32_t cap,
+                             float* out, float* tau, int32_t* support_count, float* psum, int32_t* support_idx,
+                             float* support_p, int32_t support_cap, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  ekv::DecodeArgs a;
   ekv::Layout L;
-  if ((st = check_ws(cache, seqs, n_q_heads, workspace, ws_bytes, &L)) != EKV_OK) return st;
-  const int P = cache->page_size;
-  ekv::DecodeArgs a{};
-  a.batch = seqs->batch; a.n_kv_heads = cache->n_kv_heads; a.n_q_heads = n_q_heads; a.group = G;
-  a.page_size = P; a.head_dim = cache->head_dim; a.kv_dtype = cache->kv_dtype;
-  a.max_pages = seqs->max_pages; a.n_phys = cache->n_phys_pages;
-  a.page_table = seqs->page_table; a.seq_lens = seqs->seq_lens;
-  a.k = cache->k; a.v = cache->v; a.q = q; a.alpha = alpha; a.scale = scale;
-  a.sel = sel; a.sel_count = sel_count; a.cap = sel ? cap : 0;
-  a.out = out; a.tau = tau; a.support_count = support_count; a.psum = psum;
-  a.support_idx = support_idx; a.support_cap = support_cap;
-  a.max_items = (int)L.max_items;
+  ekv_status st = prepare_decode(cache, seqs, q, n_q_heads, alpha, scale, sel, sel_count, cap, out, workspace,
+                                 ws_bytes, &a, &L);
+  if (st != EKV_OK) return st;
+  if ((support_idx || support_p) && support_cap < 1)
+    return fail(EKV_ERR_INVALID_ARG, "support_idx/support_p need support_cap >= 1");
+  a.tau = tau; a.support_count = support_count; a.psum = psum;
+  a.support_idx = support_idx; a.support_p = support_p; a.support_cap = support_cap;
   a.item_cnt = at<int32_t>(workspace, L.item_cnt);
   a.item_max = at<float>(workspace, L.item_max);
   a.item_lb = at<float>(workspace, L.item_lb);
@@ -251,9 +266,23 @@ ekv_status ekv_entmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const
   a.ovf_x = at<float>(workspace, L.ovf_x);
   a.ovf_t = at<int32_t>(workspace, L.ovf_t);
   a.ovf_r = at<int32_t>(workspace, L.ovf_r);
-  a.status = at<uint32_t>(workspace, L.status);
   // about 4 gather blocks per compute unit (one resident wave of blocks)
   return hip_status(ekv::launch_decode(a, 4 * device_cus(), (hipStream_t)stream), "entmax_decode launch");
+}
+
+ekv_status ekv_softmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const float* q, int32_t n_q_heads,
+                              float scale, const int32_t* sel, const int32_t* sel_count, int32_t cap, float* out,
+                              float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  ekv::DecodeArgs a;
+  ekv::Layout L;
+  ekv_status st = prepare_decode(cache, seqs, q, n_q_heads, 2.0f, scale, sel, sel_count, cap, out, workspace,
+                                 ws_bytes, &a, &L);
+  if (st != EKV_OK) return st;
+  if (cache->kv_dtype != EKV_BF16 || a.group > 4)
+    return fail(EKV_ERR_UNSUPPORTED, "softmax decode needs bf16 keys/values and at most 4 query heads per KV head");
+  float* part = at<float>(workspace, L.smx_part);
+  return hip_status(ekv::launch_softmax(a, 4 * device_cus(), part, ekv::kSmxMaxSlots, lse, (hipStream_t)stream),
+                    "softmax_decode launch");
 }
 
 ekv_status ekv_read_device_status(void* workspace, size_t ws_bytes, int32_t* host_flags) {

@@ -35,6 +35,7 @@ struct Layout {
   size_t ovf_x;     // f32 [B*Hq*max_items*64] compacted candidates (large sets)
   size_t ovf_t;     // i32 [...]
   size_t ovf_r;     // i32 [...]
+  size_t smx_part;  // f32 [B*Hq][kSmxMaxSlots][head_dim + 2] softmax block partials
   size_t total;
   size_t max_items; // per (sequence, query head)
 };
@@ -45,7 +46,9 @@ inline int keep_words(int max_pages) { return (max_pages + 63) / 64; }
 // row stride of the internal page-score buffer: 16-byte aligned rows
 inline int score_stride(int max_pages) { return (max_pages + 3) & ~3; }
 
-inline Layout make_layout(int B, int Hkv, int Hq, int max_pages, int P) {
+constexpr int kSmxMaxSlots = 256;  // softmax decode blocks per (sequence, KV head), at most
+
+inline Layout make_layout(int B, int Hkv, int Hq, int max_pages, int P, int D = 128) {
   Layout L{};
   size_t off = 0;
   const size_t bh = size_t(B) * Hq;
@@ -67,6 +70,7 @@ inline Layout make_layout(int B, int Hkv, int Hq, int max_pages, int P) {
   L.ovf_x = off;    off = align256(off + 4 * bh * tok);
   L.ovf_t = off;    off = align256(off + 4 * bh * tok);
   L.ovf_r = off;    off = align256(off + 4 * bh * tok);
+  L.smx_part = off; off = align256(off + 4 * bh * kSmxMaxSlots * size_t(D + 2));
   L.total = off;
   return L;
 }

@@ -852,6 +852,7 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
       ts[pos] = tok;
       rs[pos] = row;
       if (a.support_idx && pos < a.support_cap) a.support_idx[bh * a.support_cap + pos] = tok;
+      if (a.support_p && pos < a.support_cap) a.support_p[bh * a.support_cap + pos] = (float)p;
     }
     nsup += tot;
     if (!in_lds) wait_mem();  // workspace list entries are read by other threads next
@@ -945,6 +946,209 @@ hipError_t launch_decode(const DecodeArgs& a, int target_blocks, hipStream_t s) 
                              : decode_dispatch<EKV_BF16, 64>(a, (int)slots, s);
   return a.head_dim == 128 ? decode_dispatch<EKV_F32, 128>(a, (int)slots, s)
                            : decode_dispatch<EKV_F32, 64>(a, (int)slots, s);
+}
+
+// ---------------------------------------------------------------------------
+// Softmax attention decode, the comparison the EntmaxKV summary draws
+// (sec. 1 and 3): z = scale q.k over the same page list (selected pages, or
+// the whole cache), p = softmax(z) renormalised over that set, o = sum p v.
+// Flash-decode split over the page list: block (slot, unit) scores its
+// super-items on the matrix cores (as the gather does, coefficient scale q),
+// keeps a running maximum M and sum l of exp(z - M) per head, stages the
+// super-item's V rows in LDS and accumulates sum exp(z - M) v; a combine
+// kernel merges the blocks' (M, l, acc) per head in a fixed order.
+// ---------------------------------------------------------------------------
+constexpr int kSmxSub = 2;  // items (of 64 tokens) per softmax super-item
+
+template <int D, int G>
+__global__ __launch_bounds__(kDecThreads) void softmax_part_kernel(DecodeArgs a, int slots, float* part) {
+  constexpr int SUB = kSmxSub;
+  constexpr int KB = D / 32;
+  constexpr int CH = D / 8;                   // 16-byte chunks per V row
+  constexpr int QT = kDecThreads / (4 * CH);  // token groups of the accumulation
+  constexpr int TT = SUB * kItemTokens;       // tokens per super-item
+  static_assert(4 * CH * QT == kDecThreads, "thread layout");
+  __shared__ u32x4_t s_a[KB][kWave];
+  __shared__ float s_max[SUB][4][4];
+  __shared__ float s_sum[4][4];
+  __shared__ float s_e[4][TT];
+  // the V tile; after the last tile it holds the token groups' sums
+  __shared__ uint4 s_v[TT][CH];
+  static_assert(sizeof(float) * QT * 4 * D <= sizeof(uint4) * TT * CH, "accumulator alias");
+  float (*s_acc)[4][D] = reinterpret_cast<float (*)[4][D]>(&s_v[0][0]);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int u = blockIdx.y, Hkv = a.n_kv_heads, P = a.page_size;
+  const int b = u / Hkv, g = u - b * Hkv;
+  const int r = 16 * w + col;  // this lane's token within an item
+  // accumulation layout: thread = (token group tq, head ha, 16-byte chunk ca)
+  const int ca = tid % CH, ha = (tid / CH) % 4, tq = tid / (4 * CH);
+
+  const float* qg = a.q + ((size_t)b * a.n_q_heads + (size_t)g * G) * D;
+  LimbChunks<KB> lc;
+  limb_fetch<KB, G>(lc, [&](int h, int k0, float* v) {
+    const float4* qv = reinterpret_cast<const float4*>(qg + (size_t)h * D + k0);
+    const float4 q0 = qv[0], q1 = qv[1];
+    v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w; v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
+  });
+  UnitCtx ctx;
+  TokenRef tr[SUB];
+  resolve_refs<SUB>(a, u, b, blockIdx.x * SUB, r, true, &ctx, tr);
+  const float sc = a.scale;
+  limb_build<KB, G>(s_a, lc, [sc](int, float qv) { return qv * sc; });
+  __syncthreads();
+
+  // running maximum of head grp (score lanes) and of head ha (accumulating
+  // threads): the same recurrence over the same values, so equal per head
+  float Mg = -INFINITY, M = -INFINITY, l = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  const int n_super = (ctx.n_items + SUB - 1) / SUB;
+  for (int sj = blockIdx.x; sj < n_super; sj += slots) {
+    if (sj != (int)blockIdx.x) resolve_refs<SUB>(a, u, b, sj * SUB, r, false, &ctx, tr);
+    // K and V rows of the lane's tokens: 4 x 16 bytes each per item
+    u32x4_t bv[SUB][KB];
+    uint4 vv[SUB][KB];
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      if (tr[s].phys >= 0) {
+        const size_t rowi = (((size_t)tr[s].phys * Hkv + g) * P + tr[s].slot) * D + 8 * grp;
+        const uint16_t* krow = reinterpret_cast<const uint16_t*>(a.k) + rowi;
+        const uint16_t* vrow = reinterpret_cast<const uint16_t*>(a.v) + rowi;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) bv[s][kb] = *reinterpret_cast<const u32x4_t*>(krow + 32 * kb);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) vv[s][kb] = tr[s].valid ? ldg16(vrow + 32 * kb) : make_uint4(0u, 0u, 0u, 0u);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          bv[s][kb] = u32x4_t{0u, 0u, 0u, 0u};
+          vv[s][kb] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+    }
+    float z[SUB];
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) c = mfma_bf16(s_a[kb][lane], bv[s][kb], c);
+      z[s] = tr[s].valid && grp < G ? (c[0] + c[1]) + c[2] : -INFINITY;
+      const float m = group_reduce<16>(z[s], [](float x, float y) { return fmaxf(x, y); });
+      if (col == 0) s_max[s][w][grp] = m;
+      // V chunk kb of this lane's token covers columns 8 grp + 32 kb .. + 8
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) s_v[s * kItemTokens + r][grp + 4 * kb] = vv[s][kb];
+    }
+    __syncthreads();
+    auto new_max = [&](int h, float mold) {
+      float mm = mold;
+#pragma unroll
+      for (int s = 0; s < SUB; ++s)
+        mm = fmaxf(mm, fmaxf(fmaxf(s_max[s][0][h], s_max[s][1][h]), fmaxf(s_max[s][2][h], s_max[s][3][h])));
+      return mm;
+    };
+    const float mg = new_max(grp, Mg);
+    float esum = 0.f;
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      const float e = (grp < G && mg > -INFINITY) ? __expf(z[s] - mg) : 0.f;
+      esum += e;
+      s_e[grp][s * kItemTokens + r] = e;
+    }
+    Mg = mg;
+    esum = group_reduce<16>(esum, [](float x, float y) { return x + y; });
+    if (col == 0) s_sum[w][grp] = esum;
+    __syncthreads();
+    // head ha: rescale the running sums to the new maximum, add this tile
+    const float mn = new_max(ha, M);
+    const float cs = M > -INFINITY ? __expf(M - mn) : 0.f;
+    l = l * cs + ((s_sum[0][ha] + s_sum[1][ha]) + (s_sum[2][ha] + s_sum[3][ha]));
+    M = mn;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= cs;
+    if (ha < G) {
+      for (int tok = tq; tok < TT; tok += QT) {
+        const float e = s_e[ha][tok];
+        float f[8];
+        Elem<EKV_BF16>::unpack(s_v[tok][ca], f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(e, f[j], acc[j]);
+      }
+    }
+    __syncthreads();  // s_max, s_e, s_v and s_sum are rewritten next
+  }
+  // combine the token groups; write this block's (M, l, acc) per head
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s_acc[tq][ha][ca * 8 + j] = acc[j];
+  __syncthreads();
+  for (int i = tid; i < G * D; i += kDecThreads) {
+    const int h = i / D, d = i - h * D;
+    float sum = 0.f;
+#pragma unroll
+    for (int t = 0; t < QT; ++t) sum += s_acc[t][h][d];
+    const size_t bh = (size_t)b * a.n_q_heads + (size_t)g * G + h;
+    part[(bh * slots + blockIdx.x) * (D + 2) + 2 + d] = sum;
+  }
+  if (tq == 0 && ca == 0 && ha < G) {
+    const size_t bh = (size_t)b * a.n_q_heads + (size_t)g * G + ha;
+    float* pp = part + (bh * slots + blockIdx.x) * (D + 2);
+    pp[0] = M;
+    pp[1] = l;
+  }
+}
+
+// One block per (sequence, query head): o = sum_i e^{M_i - M} acc_i / L,
+// L = sum_i e^{M_i - M} l_i, lse = M + log L, in slot order.
+template <int D>
+__global__ __launch_bounds__(D) void softmax_combine_kernel(DecodeArgs a, int slots, const float* part, float* lse) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const size_t bh = (size_t)b * a.n_q_heads + h;
+  const float* pp = part + bh * slots * (D + 2);
+  float M = -INFINITY;
+  for (int i = 0; i < slots; ++i) M = fmaxf(M, pp[(size_t)i * (D + 2)]);
+  float L = 0.f, o = 0.f;
+  if (M > -INFINITY) {
+    for (int i = 0; i < slots; ++i) {
+      const float mi = pp[(size_t)i * (D + 2)];
+      if (!(mi > -INFINITY)) continue;
+      const float c = __expf(mi - M);
+      L = fmaf(c, pp[(size_t)i * (D + 2) + 1], L);
+      o = fmaf(c, pp[(size_t)i * (D + 2) + 2 + d], o);
+    }
+  }
+  a.out[bh * D + d] = L > 0.f ? o / L : 0.f;
+  if (d == 0 && lse) lse[bh] = L > 0.f ? M + logf(L) : -INFINITY;
+}
+
+hipError_t launch_softmax(const DecodeArgs& a, int target_blocks, float* part, int max_slots, float* lse,
+                          hipStream_t s) {
+  const long long pages = a.sel ? (a.cap < a.max_pages ? a.cap : a.max_pages) : a.max_pages;
+  const long long items = (pages * a.page_size + kItemTokens - 1) / kItemTokens;
+  const long long supers = (items + kSmxSub - 1) / kSmxSub;
+  const int units = a.batch * a.n_kv_heads;
+  long long slots = (target_blocks + units - 1) / units;
+  if (slots > supers) slots = supers;
+  if (slots > max_slots) slots = max_slots;
+  if (slots < 1) slots = 1;
+  const dim3 g1((unsigned)slots, units), b1(kDecThreads);
+#define EKV_SMX(DD, GG) hipLaunchKernelGGL((softmax_part_kernel<DD, GG>), g1, b1, 0, s, a, (int)slots, part)
+  if (a.head_dim == 128) {
+    if (a.group == 1) EKV_SMX(128, 1); else if (a.group == 2) EKV_SMX(128, 2); else EKV_SMX(128, 4);
+  } else {
+    if (a.group == 1) EKV_SMX(64, 1); else if (a.group == 2) EKV_SMX(64, 2); else EKV_SMX(64, 4);
+  }
+#undef EKV_SMX
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 g2(a.n_q_heads, a.batch);
+  if (a.head_dim == 128)
+    hipLaunchKernelGGL((softmax_combine_kernel<128>), g2, dim3(128), 0, s, a, (int)slots, part, lse);
+  else
+    hipLaunchKernelGGL((softmax_combine_kernel<64>), g2, dim3(64), 0, s, a, (int)slots, part, lse);
+  return hipGetLastError();
 }
 
 __global__ void fill_zero_kernel(uint4* p, size_t n16) {

@@ -64,6 +64,7 @@ struct DecodeArgs {
   int32_t* support_count;  // optional
   float* psum;           // optional
   int32_t* support_idx;  // optional
+  float* support_p;      // optional
   int support_cap;
   int max_items;  // per (sequence, query head)
   int32_t* item_cnt;
@@ -85,5 +86,9 @@ hipError_t launch_topk(const SelectArgs& a, hipStream_t s);
 hipError_t launch_score_gauss(const SelectArgs& a, hipStream_t s);
 hipError_t launch_tau_hat(const SelectArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int target_blocks, hipStream_t s);
+// softmax decode over the same page list; `part` holds max_slots * (D + 2)
+// floats per query head
+hipError_t launch_softmax(const DecodeArgs& a, int target_blocks, float* part, int max_slots, float* lse,
+                          hipStream_t s);
 
 }  // namespace ekv

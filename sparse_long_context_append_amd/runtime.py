@@ -81,12 +81,19 @@ class DecodeSession:
                        scale=scale, delta=delta, sel=self.sel, sel_count=self.sel_count, cap=self.cap,
                        tau_hat=self.tau_hat, ws=self.ws)
 
-    def decode(self, q, *, alpha, scale, sparse=True, support_idx=None, support_cap=0):
+    def decode(self, q, *, alpha, scale, sparse=True, support_idx=None, support_p=None, support_cap=0):
         B.entmax_decode(self.cache, self.seqs, q, self.n_q_heads, alpha=alpha, scale=scale,
                         sel=self.sel if sparse else None, sel_count=self.sel_count if sparse else None,
                         cap=self.cap if sparse else 0, out=self.out, tau=self.tau,
                         support_count=self.support_count, psum=self.psum, support_idx=support_idx,
-                        support_cap=support_cap, ws=self.ws)
+                        support_p=support_p, support_cap=support_cap, ws=self.ws)
+
+    def decode_softmax(self, q, *, scale, sparse=True, out=None, lse=None):
+        """Softmax attention over the selected pages (or the whole cache);
+        writes `out` (default: the session's output buffer)."""
+        B.softmax_decode(self.cache, self.seqs, q, self.n_q_heads, scale=scale,
+                         sel=self.sel if sparse else None, sel_count=self.sel_count if sparse else None,
+                         cap=self.cap if sparse else 0, out=self.out if out is None else out, lse=lse, ws=self.ws)
 
     def scores(self, q, *, policy, alpha, scale):
         torch = self.torch

@@ -93,7 +93,7 @@ def test_select_validation(L):
 def call_decode(L, q=FAKE, alpha=1.5, scale=0.125, sel=FAKE, cnt=FAKE, cap=64, out=FAKE, sidx=None, scap=0,
                 ws=FAKE, wsb=1 << 40, c=None):
     return L.ekv_entmax_decode(ctypes.byref(c or cache()), ctypes.byref(seqs()), q, 32, alpha, scale, sel, cnt,
-                               cap, out, None, None, None, sidx, scap, ws, wsb, None)
+                               cap, out, None, None, None, sidx, None, scap, ws, wsb, None)
 
 
 def test_decode_validation(L):
@@ -107,6 +107,17 @@ def test_decode_validation(L):
     assert call_decode(L, wsb=100) == B.EKV_ERR_WORKSPACE
     assert call_decode(L, c=cache(k=None)) == B.EKV_ERR_INVALID_ARG
     assert call_decode(L, c=cache(kv_dtype=5)) == B.EKV_ERR_INVALID_ARG
+
+
+def test_softmax_validation(L):
+    f = L.ekv_softmax_decode
+    call = lambda c=None, sel=FAKE, cnt=FAKE, cap=64, out=FAKE, scale=0.125, wsb=1 << 40: f(
+        ctypes.byref(c or cache()), ctypes.byref(seqs()), FAKE, 32, scale, sel, cnt, cap, out, None, FAKE, wsb, None)
+    assert call(out=None) == B.EKV_ERR_INVALID_ARG
+    assert call(scale=0.0) == B.EKV_ERR_INVALID_ARG
+    assert call(cnt=None) == B.EKV_ERR_INVALID_ARG
+    assert call(wsb=100) == B.EKV_ERR_WORKSPACE
+    assert call(c=cache(kv_dtype=B.EKV_F32)) == B.EKV_ERR_UNSUPPORTED
 
 
 def test_append_validation(L):
