@@ -354,6 +354,88 @@ def run_sweep(args, torch, timer):
                       "data": "synthetic", "sweep": rows}), flush=True)
 
 
+def compare_one(spec, args, torch, timer):
+    """Entmax and softmax decode over the same selected pages and over the
+    whole cache: per query head, the full-cache mass outside the selection
+    (entmax: from the full-cache support weights; softmax: 1 - exp(lse_J -
+    lse_full)), the share of the entmax support the selection keeps, and the
+    relative output error of the selection against the full cache."""
+    import sparse_long_context_append_amd as ekv
+    from workloads.upload import build_session, queries_device
+    sess, _ = build_session(spec)
+    q = queries_device(spec)
+    pol = ekv.EKV_SELECT_BBOX_TOPK if spec.policy == "bbox" else ekv.EKV_SELECT_GAUSS
+    B, Hq, d = spec.batch, spec.n_q_heads, spec.head_dim
+    f32 = dict(dtype=torch.float32, device="cuda")
+    SC = 1 << 14
+    sidx = torch.full((B, Hq, SC), -1, dtype=torch.int32, device="cuda")
+    sp = torch.zeros((B, Hq, SC), **f32)
+    o_soft_s, o_soft_f = torch.zeros((B, Hq, d), **f32), torch.zeros((B, Hq, d), **f32)
+    lse_s, lse_f = torch.zeros((B, Hq), **f32), torch.zeros((B, Hq), **f32)
+
+    def select():
+        sess.select(q, policy=pol, alpha=spec.alpha, scale=spec.scale, top_k=spec.top_k, delta=spec.delta)
+
+    select()
+    t = {}
+    t["entmax_sparse_us"] = statistics.median(timer.run(
+        lambda: sess.decode(q, alpha=spec.alpha, scale=spec.scale, sparse=True), args.steps, args.warmup)[0]) * 1e3
+    t["entmax_full_us"] = statistics.median(timer.run(
+        lambda: sess.decode(q, alpha=spec.alpha, scale=spec.scale, sparse=False), max(3, args.steps // 3), 1)[0]) * 1e3
+    t["softmax_sparse_us"] = statistics.median(timer.run(
+        lambda: sess.decode_softmax(q, scale=spec.scale, sparse=True, out=o_soft_s, lse=lse_s), args.steps,
+        args.warmup)[0]) * 1e3
+    t["softmax_full_us"] = statistics.median(timer.run(
+        lambda: sess.decode_softmax(q, scale=spec.scale, sparse=False, out=o_soft_f, lse=lse_f),
+        max(3, args.steps // 3), 1)[0]) * 1e3
+    sess.decode(q, alpha=spec.alpha, scale=spec.scale, sparse=True)
+    o_ent_s = sess.out.clone()
+    sess.decode(q, alpha=spec.alpha, scale=spec.scale, sparse=False, support_idx=sidx, support_p=sp, support_cap=SC)
+    o_ent_f = sess.out.clone()
+    torch.cuda.synchronize()
+    cnt = sess.support_count.cpu().numpy()
+    ids, ps = sidx.cpu().numpy(), sp.cpu().numpy()
+    sel, scnt, lens = sess.sel.cpu().numpy(), sess.sel_count.cpu().numpy(), sess.seq_lens.cpu().numpy()
+    rel = lambda a, b: (torch.linalg.vector_norm(a - b, dim=-1) / torch.linalg.vector_norm(b, dim=-1)).cpu().numpy()
+    err_e, err_s = rel(o_ent_s, o_ent_f), rel(o_soft_s, o_soft_f)
+    d_soft = 1.0 - np.exp(lse_s.cpu().numpy().astype(np.float64) - lse_f.cpu().numpy().astype(np.float64))
+    d_ent, keep = [], []
+    P = spec.page_size
+    for b in range(B):
+        for g in range(spec.n_kv_heads):
+            pages = sel[b, g, : scnt[b, g]].astype(np.int64)
+            for h in range(g * spec.group, (g + 1) * spec.group):
+                n = min(int(cnt[b, h]), SC)
+                tok = ids[b, h, :n].astype(np.int64)
+                kept = np.isin(tok // P, pages)
+                d_ent.append(float(ps[b, h, :n][~kept].sum()))
+                keep.append(float(kept.mean()) if n else 1.0)
+    d_ent, keep = np.array(d_ent), np.array(keep)
+    pages_frac = float(scnt.sum()) / float(sum(-(-int(L) // P) for L in lens) * spec.n_kv_heads)
+    row = {"workload": spec.name, "selector": spec.policy, "alpha": spec.alpha, "pages_kept_frac": round(pages_frac, 4),
+           "entmax": {"dropped_mass_mean": float(d_ent.mean()), "dropped_mass_max": float(d_ent.max()),
+                      "support_retention_mean": float(keep.mean()),
+                      "heads_with_full_support": int((keep == 1.0).sum()), "heads": int(keep.size),
+                      "rel_out_err_mean": float(err_e.mean()), "rel_out_err_max": float(err_e.max())},
+           "softmax": {"dropped_mass_mean": float(d_soft.mean()), "dropped_mass_max": float(d_soft.max()),
+                       "rel_out_err_mean": float(err_s.mean()), "rel_out_err_max": float(err_s.max())},
+           **{k: round(v, 2) for k, v in t.items()}}
+    del sess
+    torch.cuda.empty_cache()
+    return row
+
+
+def run_compare(args, torch, timer):
+    rows = []
+    for name in ("c2", "c3", "c4"):
+        spec = W.make_spec(name)
+        rows.append(compare_one(spec, args, torch, timer))
+        log(f"compare {name}: entmax dropped {rows[-1]['entmax']['dropped_mass_mean']:.4f}, softmax dropped "
+            f"{rows[-1]['softmax']['dropped_mass_mean']:.4f}")
+    print(json.dumps({"metric": "entmax vs softmax at the same selected pages", "n_gpus": 1, "data": "synthetic",
+                      "steps": args.steps, "warmup": args.warmup, "compare": rows}), flush=True)
+
+
 def copy_probe(mib):
     """A plain copy kernel of known size: HBM read and write counters of its
     dispatches calibrate the counters of the path's kernels."""
@@ -406,6 +488,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline line: context sweep 32K..1M of the top-2%% and Gaussian "
                          "million-token workloads (one JSON line with a 'sweep' list)")
+    ap.add_argument("--compare", action="store_true",
+                    help="instead of the headline line: entmax vs softmax at the same selected pages (dropped "
+                         "mass, support retention, output error, decode times) on c2, c3, c4")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (counter calibration)")
     args = ap.parse_args()
@@ -421,6 +506,9 @@ def main():
     timer = Timer(torch)
     if args.sweep:
         run_sweep(args, torch, timer)
+        return
+    if args.compare:
+        run_compare(args, torch, timer)
         return
     over = {"context": args.context} if args.context else {}
     spec = W.make_spec(args.workload, **over)

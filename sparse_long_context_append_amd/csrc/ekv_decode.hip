@@ -1101,26 +1101,50 @@ __global__ __launch_bounds__(kDecThreads) void softmax_part_kernel(DecodeArgs a,
 }
 
 // One block per (sequence, query head): o = sum_i e^{M_i - M} acc_i / L,
-// L = sum_i e^{M_i - M} l_i, lse = M + log L, in slot order.
+// L = sum_i e^{M_i - M} l_i, lse = M + log L.  The blocks' maxima and sums
+// are read in one round; then thread (column d, slot group sg) sums its
+// slots sixteen loads at a time, and the groups are added in order.
+constexpr int kSmxCombineThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(D) void softmax_combine_kernel(DecodeArgs a, int slots, const float* part, float* lse) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+__global__ __launch_bounds__(kSmxCombineThreads) void softmax_combine_kernel(DecodeArgs a, int slots,
+                                                                             const float* part, float* lse) {
+  constexpr int NG = kSmxCombineThreads / D;
+  __shared__ float s_c[kSmxMaxSlots];
+  __shared__ float s_o[NG][D];
+  __shared__ float red[16];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int d = tid % D, sg = tid / D;
   const size_t bh = (size_t)b * a.n_q_heads + h;
   const float* pp = part + bh * slots * (D + 2);
-  float M = -INFINITY;
-  for (int i = 0; i < slots; ++i) M = fmaxf(M, pp[(size_t)i * (D + 2)]);
-  float L = 0.f, o = 0.f;
-  if (M > -INFINITY) {
-    for (int i = 0; i < slots; ++i) {
-      const float mi = pp[(size_t)i * (D + 2)];
-      if (!(mi > -INFINITY)) continue;
-      const float c = __expf(mi - M);
-      L = fmaf(c, pp[(size_t)i * (D + 2) + 1], L);
-      o = fmaf(c, pp[(size_t)i * (D + 2) + 2 + d], o);
+  const bool has = tid < slots;
+  const float mi = has ? pp[(size_t)tid * (D + 2)] : -INFINITY;
+  const float li = has ? pp[(size_t)tid * (D + 2) + 1] : 0.f;
+  const float M = block_max(mi, red);
+  const float c = (M > -INFINITY && mi > -INFINITY) ? __expf(mi - M) : 0.f;
+  if (has) s_c[tid] = c;
+  const float L = block_sum(c * li, red);  // block_sum's barriers also publish s_c
+  float o = 0.f;
+  for (int i0 = sg; i0 < slots; i0 += 16 * NG) {
+    float v[16], w[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = i0 + u * NG;
+      v[u] = i < slots ? pp[(size_t)i * (D + 2) + 2 + d] : 0.f;
+      w[u] = i < slots ? s_c[i] : 0.f;
     }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) o = fmaf(w[u], v[u], o);
   }
-  a.out[bh * D + d] = L > 0.f ? o / L : 0.f;
-  if (d == 0 && lse) lse[bh] = L > 0.f ? M + logf(L) : -INFINITY;
+  s_o[sg][d] = o;
+  __syncthreads();
+  if (sg == 0) {
+    float t = s_o[0][d];
+#pragma unroll
+    for (int j = 1; j < NG; ++j) t += s_o[j][d];
+    a.out[bh * D + d] = L > 0.f ? t / L : 0.f;
+    if (d == 0 && lse) lse[bh] = L > 0.f ? M + logf(L) : -INFINITY;
+  }
 }
 
 hipError_t launch_softmax(const DecodeArgs& a, int target_blocks, float* part, int max_slots, float* lse,
@@ -1144,10 +1168,11 @@ hipError_t launch_softmax(const DecodeArgs& a, int target_blocks, float* part, i
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 g2(a.n_q_heads, a.batch);
+  static_assert(kSmxMaxSlots <= kSmxCombineThreads, "one block maximum per combine thread");
   if (a.head_dim == 128)
-    hipLaunchKernelGGL((softmax_combine_kernel<128>), g2, dim3(128), 0, s, a, (int)slots, part, lse);
+    hipLaunchKernelGGL((softmax_combine_kernel<128>), g2, dim3(kSmxCombineThreads), 0, s, a, (int)slots, part, lse);
   else
-    hipLaunchKernelGGL((softmax_combine_kernel<64>), g2, dim3(64), 0, s, a, (int)slots, part, lse);
+    hipLaunchKernelGGL((softmax_combine_kernel<64>), g2, dim3(kSmxCombineThreads), 0, s, a, (int)slots, part, lse);
   return hipGetLastError();
 }
 
