@@ -128,6 +128,28 @@ def test_gauss_more_pages_than_register_tiles():
     check_step(spec, run_step(sess, spec, q), q, all_units(spec))
 
 
+@pytest.mark.parametrize("alpha,hkv", [(1.3, 2), (1.8, 2), (1.3, 1)])
+def test_general_alpha_decode(alpha, hkv):
+    """alpha outside {1.5, 2}: the threshold comes from Newton's method on the
+    support instead of a closed form (bf16 matrix-core gather for groups of
+    4, vector gather for the group of 8)."""
+    spec = W.make_spec("c2", context=3001, page_size=16, top_k=50, n_q_heads=8, n_kv_heads=hkv, n_needles=16,
+                       alpha=alpha)
+    sess, _ = _session(spec)
+    q = W.queries(spec)
+    cache = {}
+    check_step(spec, run_step(sess, spec, q), q, all_units(spec), kv_cache=cache)
+    check_step(spec, run_step(sess, spec, q, sparse=False), q, all_units(spec), sparse=False, kv_cache=cache)
+
+
+def test_c1_general_alpha_fp32():
+    spec = W.make_spec("c1", alpha=1.25)
+    sess, _ = _session(spec)
+    q = W.queries(spec)
+    check_step(spec, run_step(sess, spec, q), q, all_units(spec))
+    check_step(spec, run_step(sess, spec, q, sparse=False), q, all_units(spec), sparse=False)
+
+
 def test_c4_reduced():
     spec = W.make_spec("c4", context=65536 + 33, n_q_heads=8, n_kv_heads=2, n_needles=64, top_k=21)
     sess, _ = _session(spec)
