@@ -122,6 +122,11 @@ typedef struct {
  *   scale      score scale, normally 1/sqrt(head_dim)
  *   delta      EKV_SELECT_GAUSS safety margin, in the scaled score domain
  *              x = (alpha-1) scale q.k where the threshold lives
+ *   per_head   0: one page set per (sequence, KV head), shared by the KV
+ *              head's query-head group (the group-level rule below);
+ *              1: one page set per (sequence, query head), each head scored
+ *              and selected on its own.  The summary does not say how
+ *              grouped-query heads share a selection; both are offered.
  */
 typedef struct {
   int32_t policy;
@@ -129,7 +134,7 @@ typedef struct {
   float alpha;
   float scale;
   float delta;
-  int32_t reserved;
+  int32_t per_head;
 } ekv_select_params;
 
 /*
@@ -164,11 +169,15 @@ ekv_status ekv_append_kv(const ekv_cache* cache, const ekv_seqs* seqs, const voi
 
 /*
  * Score pages and select candidates for every (sequence, KV head); the
- * selection is shared by the KV head's query-head group.
+ * selection is shared by the KV head's query-head group.  With
+ * params->per_head = 1 every query head gets its own selection: the rules
+ * below then apply with a group of one head (its own bound, its own
+ * threshold estimate), and sel/sel_count have n_q_heads rows per sequence.
  *   q          [batch][n_q_heads][head_dim] float32, 16-byte aligned;
  *              n_q_heads = G * n_kv_heads with G in {1, 2, 4, 8}
- *   sel        [batch][n_kv_heads][cap] int32: ascending logical page ids
- *   sel_count  [batch][n_kv_heads] int32: number of valid entries in sel
+ *   sel        [batch][H][cap] int32: ascending logical page ids, with
+ *              H = n_kv_heads (shared) or n_q_heads (per_head = 1)
+ *   sel_count  [batch][H] int32: number of valid entries in sel
  *   tau_hat    optional [batch][n_q_heads] float32 (EKV_SELECT_GAUSS only):
  *              the estimated threshold per query head
  * BBOX_TOPK: page score = max over the group's heads of
@@ -196,6 +205,10 @@ ekv_status ekv_select_pages(const ekv_cache* cache, const ekv_seqs* seqs, const 
  *   alpha      > 1 (exact threshold for 1.5 and 2, Newton-converged otherwise)
  *   sel, sel_count, cap  as produced by ekv_select_pages (sel_count entries
  *              are clamped to [0, cap] and to the sequence's page count)
+ *   sel_heads  rows of sel per sequence: n_kv_heads (query head h reads the
+ *              list of KV head h / G) or n_q_heads (query head h reads its
+ *              own list, from per_head selection); any other value is
+ *              EKV_ERR_INVALID_ARG when sel != NULL, ignored otherwise
  *   out        [batch][n_q_heads][head_dim] float32, 16-byte aligned:
  *              sum_j p_j v_j
  *   tau        optional [batch][n_q_heads] float32: the threshold (x domain)
@@ -209,7 +222,7 @@ ekv_status ekv_select_pages(const ekv_cache* cache, const ekv_seqs* seqs, const 
  */
 ekv_status ekv_entmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const float* q,
                              int32_t n_q_heads, float alpha, float scale, const int32_t* sel,
-                             const int32_t* sel_count, int32_t cap, float* out, float* tau,
+                             const int32_t* sel_count, int32_t cap, int32_t sel_heads, float* out, float* tau,
                              int32_t* support_count, float* psum, int32_t* support_idx,
                              float* support_p, int32_t support_cap, void* workspace, size_t ws_bytes,
                              void* stream);
@@ -229,13 +242,14 @@ ekv_status ekv_entmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const
  */
 ekv_status ekv_softmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const float* q,
                               int32_t n_q_heads, float scale, const int32_t* sel,
-                              const int32_t* sel_count, int32_t cap, float* out, float* lse,
+                              const int32_t* sel_count, int32_t cap, int32_t sel_heads, float* out, float* lse,
                               void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Page scores only (diagnostics and parity checks).
- *   BBOX_TOPK: scores [batch][n_kv_heads][max_pages] float32, the page score
- *              used by the selector (-inf for pages past the sequence end).
+ *   BBOX_TOPK: scores [batch][H][max_pages] float32, the page score used by
+ *              the selector (-inf for pages past the sequence end); H as in
+ *              ekv_select_pages.
  *   GAUSS:     scores [batch][n_q_heads][max_pages][4] float32:
  *              (mean_Y, sd_Y, estimated max, n_p) per page.
  */

@@ -48,7 +48,7 @@ class _SelectParams(ctypes.Structure):
     _fields_ = [
         ("policy", ctypes.c_int32), ("top_k", ctypes.c_int32),
         ("alpha", ctypes.c_float), ("scale", ctypes.c_float),
-        ("delta", ctypes.c_float), ("reserved", ctypes.c_int32),
+        ("delta", ctypes.c_float), ("per_head", ctypes.c_int32),
     ]
 
 
@@ -60,10 +60,10 @@ _SIGS = {
     "ekv_workspace_init": (_i32, [_vp, _sz, _vp]),
     "ekv_append_kv": (_i32, [_PC, _PS, _vp, _vp, _i32, _vp, _sz, _vp]),
     "ekv_select_pages": (_i32, [_PC, _PS, _vp, _i32, _PP, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
-    "ekv_entmax_decode": (_i32, [_PC, _PS, _vp, _i32, ctypes.c_float, ctypes.c_float, _vp, _vp, _i32,
+    "ekv_entmax_decode": (_i32, [_PC, _PS, _vp, _i32, ctypes.c_float, ctypes.c_float, _vp, _vp, _i32, _i32,
                                  _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
-    "ekv_softmax_decode": (_i32, [_PC, _PS, _vp, _i32, ctypes.c_float, _vp, _vp, _i32, _vp, _vp, _vp, _sz,
-                                  _vp]),
+    "ekv_softmax_decode": (_i32, [_PC, _PS, _vp, _i32, ctypes.c_float, _vp, _vp, _i32, _i32, _vp, _vp, _vp,
+                                  _sz, _vp]),
     "ekv_score_pages": (_i32, [_PC, _PS, _vp, _i32, _PP, _vp, _vp, _sz, _vp]),
     "ekv_read_device_status": (_i32, [_vp, _sz, ctypes.POINTER(_i32)]),
     "ekv_status_string": (ctypes.c_char_p, [_i32]),
@@ -167,41 +167,52 @@ def append_kv(cache: PagedCache, seqs: Sequences, k_new, v_new, n_new: int, ws, 
                                n_new, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "append_kv")
 
 
-def _params(policy, top_k, alpha, scale, delta) -> _SelectParams:
-    return _SelectParams(int(policy), int(top_k), float(alpha), float(scale), float(delta), 0)
+def _params(policy, top_k, alpha, scale, delta, per_head=False) -> _SelectParams:
+    return _SelectParams(int(policy), int(top_k), float(alpha), float(scale), float(delta), int(bool(per_head)))
+
+
+def _sel_heads(cache: PagedCache, sel, sel_heads):
+    """Rows of `sel` per sequence: given, else read from a [B][H][cap] tensor."""
+    if sel_heads is not None:
+        return int(sel_heads)
+    if sel is not None and hasattr(sel, "shape") and len(sel.shape) == 3:
+        return int(sel.shape[1])
+    return cache.n_kv_heads
 
 
 def select_pages(cache: PagedCache, seqs: Sequences, q, n_q_heads: int, *, policy: int, top_k: int = 0,
-                 alpha: float, scale: float, delta: float = 0.0, sel, sel_count, cap: int, tau_hat=None,
-                 ws, stream=None):
-    p = _params(policy, top_k, alpha, scale, delta)
+                 alpha: float, scale: float, delta: float = 0.0, per_head: bool = False, sel, sel_count,
+                 cap: int, tau_hat=None, ws, stream=None):
+    p = _params(policy, top_k, alpha, scale, delta, per_head)
     _check(lib().ekv_select_pages(ctypes.byref(cache.c()), ctypes.byref(seqs.c()), _ptr(q), n_q_heads,
                                   ctypes.byref(p), _ptr(sel), _ptr(sel_count), cap, _ptr(tau_hat), _ptr(ws),
                                   ws.numel() * ws.element_size(), _stream(stream)), "select_pages")
 
 
 def score_pages(cache: PagedCache, seqs: Sequences, q, n_q_heads: int, *, policy: int, alpha: float,
-                scale: float, scores, ws, stream=None):
-    p = _params(policy, 1, alpha, scale, 0.0)
+                scale: float, per_head: bool = False, scores, ws, stream=None):
+    p = _params(policy, 1, alpha, scale, 0.0, per_head)
     _check(lib().ekv_score_pages(ctypes.byref(cache.c()), ctypes.byref(seqs.c()), _ptr(q), n_q_heads,
                                  ctypes.byref(p), _ptr(scores), _ptr(ws), ws.numel() * ws.element_size(),
                                  _stream(stream)), "score_pages")
 
 
 def entmax_decode(cache: PagedCache, seqs: Sequences, q, n_q_heads: int, *, alpha: float, scale: float,
-                  sel=None, sel_count=None, cap: int = 0, out, tau=None, support_count=None, psum=None,
-                  support_idx=None, support_p=None, support_cap: int = 0, ws, stream=None):
+                  sel=None, sel_count=None, cap: int = 0, sel_heads=None, out, tau=None, support_count=None,
+                  psum=None, support_idx=None, support_p=None, support_cap: int = 0, ws, stream=None):
     _check(lib().ekv_entmax_decode(ctypes.byref(cache.c()), ctypes.byref(seqs.c()), _ptr(q), n_q_heads,
-                                   float(alpha), float(scale), _ptr(sel), _ptr(sel_count), cap, _ptr(out),
+                                   float(alpha), float(scale), _ptr(sel), _ptr(sel_count), cap,
+                                   _sel_heads(cache, sel, sel_heads), _ptr(out),
                                    _ptr(tau), _ptr(support_count), _ptr(psum), _ptr(support_idx),
                                    _ptr(support_p), support_cap, _ptr(ws), ws.numel() * ws.element_size(),
                                    _stream(stream)), "entmax_decode")
 
 
 def softmax_decode(cache: PagedCache, seqs: Sequences, q, n_q_heads: int, *, scale: float, sel=None,
-                   sel_count=None, cap: int = 0, out, lse=None, ws, stream=None):
+                   sel_count=None, cap: int = 0, sel_heads=None, out, lse=None, ws, stream=None):
     _check(lib().ekv_softmax_decode(ctypes.byref(cache.c()), ctypes.byref(seqs.c()), _ptr(q), n_q_heads,
-                                    float(scale), _ptr(sel), _ptr(sel_count), cap, _ptr(out), _ptr(lse),
+                                    float(scale), _ptr(sel), _ptr(sel_count), cap,
+                                    _sel_heads(cache, sel, sel_heads), _ptr(out), _ptr(lse),
                                     _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "softmax_decode")
 
 

@@ -85,6 +85,18 @@ int device_cus() {
   return cus;
 }
 
+// The same arguments seen as one selection unit per (sequence, query head):
+// group 1, unit head h reads the cache records of KV head h / G.
+template <typename Args> Args per_query_head_view(const Args& a) {
+  Args u = a;
+  int shift = 0;
+  while ((1 << shift) < a.group) ++shift;
+  u.n_kv_heads = a.n_q_heads;
+  u.group = 1;
+  u.kv_shift = shift;
+  return u;
+}
+
 }  // namespace
 
 extern "C" {
@@ -153,9 +165,13 @@ static ekv_status prepare_select(const ekv_cache* cache, const ekv_seqs* seqs, c
     return fail(EKV_ERR_INVALID_ARG, "unknown selection policy");
   }
   if (!(p->alpha > 1.f) || !isfinite(p->alpha)) return fail(EKV_ERR_INVALID_ARG, "alpha must be finite and > 1");
+  if (p->per_head != 0 && p->per_head != 1) return fail(EKV_ERR_INVALID_ARG, "per_head must be 0 or 1");
+  if (p->per_head && (long long)seqs->batch * n_q_heads > ekv::kMaxUnits)
+    return fail(EKV_ERR_UNSUPPORTED, "per-query-head selection needs batch * n_q_heads <= 4096");
   if ((st = check_ws(cache, seqs, n_q_heads, workspace, ws_bytes, L)) != EKV_OK) return st;
   *a = ekv::SelectArgs{};
   a->batch = seqs->batch; a->n_kv_heads = cache->n_kv_heads; a->n_q_heads = n_q_heads; a->group = G;
+  a->hkv_mem = cache->n_kv_heads; a->kv_shift = 0; a->per_head_scores = 0;
   a->page_size = cache->page_size; a->head_dim = cache->head_dim; a->kv_dtype = cache->kv_dtype;
   a->max_pages = seqs->max_pages; a->n_phys = cache->n_phys_pages;
   a->page_table = seqs->page_table; a->seq_lens = seqs->seq_lens;
@@ -189,12 +205,18 @@ ekv_status ekv_select_pages(const ekv_cache* cache, const ekv_seqs* seqs, const 
     return fail(EKV_ERR_CAPACITY, "Gaussian selection needs cap >= max_pages");
   a.sel = sel; a.sel_count = sel_count; a.cap = cap; a.tau_hat_out = tau_hat;
   hipStream_t s = (hipStream_t)stream;
+  // Scoring reads each page record once per KV head in both modes; per
+  // query head, the bound is written per head and the top-k, threshold
+  // estimate and keep test run on (sequence, query head) units.
+  const bool per_head = params->per_head && a.group > 1;
+  const ekv::SelectArgs u = per_head ? per_query_head_view(a) : a;
   if (params->policy == EKV_SELECT_BBOX_TOPK) {
+    a.per_head_scores = per_head;
     if ((st = hip_status(ekv::launch_score_bbox(a, s), "score_bbox launch")) != EKV_OK) return st;
-    return hip_status(ekv::launch_topk(a, s), "topk launch");
+    return hip_status(ekv::launch_topk(u, s), "topk launch");
   }
   if ((st = hip_status(ekv::launch_score_gauss(a, s), "score_gauss launch")) != EKV_OK) return st;
-  return hip_status(ekv::launch_tau_hat(a, s), "tau_hat launch");
+  return hip_status(ekv::launch_tau_hat(u, s), "tau_hat launch");
 }
 
 ekv_status ekv_score_pages(const ekv_cache* cache, const ekv_seqs* seqs, const float* q, int32_t n_q_heads,
@@ -209,6 +231,7 @@ ekv_status ekv_score_pages(const ekv_cache* cache, const ekv_seqs* seqs, const f
   if (params->policy == EKV_SELECT_BBOX_TOPK) {
     a.scores = scores;
     a.score_stride = seqs->max_pages;
+    a.per_head_scores = params->per_head && a.group > 1;
     return hip_status(ekv::launch_score_bbox(a, s), "score_bbox launch");
   }
   a.stats_out = reinterpret_cast<float4*>(scores);
@@ -218,7 +241,8 @@ ekv_status ekv_score_pages(const ekv_cache* cache, const ekv_seqs* seqs, const f
 // Validation and argument packing shared by the two decode entry points.
 ekv_status prepare_decode(const ekv_cache* cache, const ekv_seqs* seqs, const float* q, int32_t n_q_heads,
                           float alpha, float scale, const int32_t* sel, const int32_t* sel_count, int32_t cap,
-                          float* out, void* workspace, size_t ws_bytes, ekv::DecodeArgs* a, ekv::Layout* L) {
+                          int32_t sel_heads, float* out, void* workspace, size_t ws_bytes, ekv::DecodeArgs* a,
+                          ekv::Layout* L) {
   ekv_status st;
   int G = 0;
   if ((st = check_cache(cache)) != EKV_OK) return st;
@@ -229,9 +253,15 @@ ekv_status prepare_decode(const ekv_cache* cache, const ekv_seqs* seqs, const fl
   if (!(alpha > 1.f) || !isfinite(alpha)) return fail(EKV_ERR_INVALID_ARG, "alpha must be finite and > 1");
   if (!(scale > 0.f) || !isfinite(scale)) return fail(EKV_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (sel && (!sel_count || cap < 1)) return fail(EKV_ERR_INVALID_ARG, "sel needs sel_count and cap >= 1");
+  if (sel && sel_heads != cache->n_kv_heads && sel_heads != n_q_heads)
+    return fail(EKV_ERR_INVALID_ARG, "sel_heads must be n_kv_heads or n_q_heads");
+  const bool per_head = sel && sel_heads == n_q_heads && G > 1;
+  if (per_head && (long long)seqs->batch * n_q_heads > ekv::kMaxUnits)
+    return fail(EKV_ERR_UNSUPPORTED, "per-query-head page lists need batch * n_q_heads <= 4096");
   if ((st = check_ws(cache, seqs, n_q_heads, workspace, ws_bytes, L)) != EKV_OK) return st;
   *a = ekv::DecodeArgs{};
   a->batch = seqs->batch; a->n_kv_heads = cache->n_kv_heads; a->n_q_heads = n_q_heads; a->group = G;
+  a->hkv_mem = cache->n_kv_heads; a->kv_shift = 0;
   a->page_size = cache->page_size; a->head_dim = cache->head_dim; a->kv_dtype = cache->kv_dtype;
   a->max_pages = seqs->max_pages; a->n_phys = cache->n_phys_pages;
   a->page_table = seqs->page_table; a->seq_lens = seqs->seq_lens;
@@ -240,18 +270,19 @@ ekv_status prepare_decode(const ekv_cache* cache, const ekv_seqs* seqs, const fl
   a->out = out;
   a->max_items = (int)L->max_items;
   a->status = at<uint32_t>(workspace, L->status);
+  if (per_head) *a = per_query_head_view(*a);
   return EKV_OK;
 }
 
 ekv_status ekv_entmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const float* q, int32_t n_q_heads,
                              float alpha, float scale, const int32_t* sel, const int32_t* sel_count, int32_t cap,
-                             float* out, float* tau, int32_t* support_count, float* psum, int32_t* support_idx,
-                             float* support_p, int32_t support_cap, void* workspace, size_t ws_bytes,
-                             void* stream) {
+                             int32_t sel_heads, float* out, float* tau, int32_t* support_count, float* psum,
+                             int32_t* support_idx, float* support_p, int32_t support_cap, void* workspace,
+                             size_t ws_bytes, void* stream) {
   ekv::DecodeArgs a;
   ekv::Layout L;
-  ekv_status st = prepare_decode(cache, seqs, q, n_q_heads, alpha, scale, sel, sel_count, cap, out, workspace,
-                                 ws_bytes, &a, &L);
+  ekv_status st = prepare_decode(cache, seqs, q, n_q_heads, alpha, scale, sel, sel_count, cap, sel_heads, out,
+                                 workspace, ws_bytes, &a, &L);
   if (st != EKV_OK) return st;
   if ((support_idx || support_p) && support_cap < 1)
     return fail(EKV_ERR_INVALID_ARG, "support_idx/support_p need support_cap >= 1");
@@ -271,12 +302,13 @@ ekv_status ekv_entmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const
 }
 
 ekv_status ekv_softmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const float* q, int32_t n_q_heads,
-                              float scale, const int32_t* sel, const int32_t* sel_count, int32_t cap, float* out,
-                              float* lse, void* workspace, size_t ws_bytes, void* stream) {
+                              float scale, const int32_t* sel, const int32_t* sel_count, int32_t cap,
+                              int32_t sel_heads, float* out, float* lse, void* workspace, size_t ws_bytes,
+                              void* stream) {
   ekv::DecodeArgs a;
   ekv::Layout L;
-  ekv_status st = prepare_decode(cache, seqs, q, n_q_heads, 2.0f, scale, sel, sel_count, cap, out, workspace,
-                                 ws_bytes, &a, &L);
+  ekv_status st = prepare_decode(cache, seqs, q, n_q_heads, 2.0f, scale, sel, sel_count, cap, sel_heads, out,
+                                 workspace, ws_bytes, &a, &L);
   if (st != EKV_OK) return st;
   if (cache->kv_dtype != EKV_BF16 || a.group > 4)
     return fail(EKV_ERR_UNSUPPORTED, "softmax decode needs bf16 keys/values and at most 4 query heads per KV head");

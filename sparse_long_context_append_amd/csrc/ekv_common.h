@@ -20,8 +20,8 @@ constexpr int kItemTokens = 64;  // tokens of one decode work item
 
 struct Layout {
   size_t status;    // u32 device status bits
-  size_t sel_done;  // u32 [B*Hkv] per-unit arrival counters of the selection stage (zero between calls)
-  size_t scores;    // f32 [B*Hkv][score_stride] bounding-box page scores
+  size_t sel_done;  // u32 [B*Hq] per-unit arrival counters of the selection stage (zero between calls)
+  size_t scores;    // f32 [B*Hq][score_stride] bounding-box page scores (unit rows)
   size_t musd;      // float2 [B*Hq*max_pages] Gaussian page score (mean_Y, sd_Y)
   size_t ehat;      // f32 [B*Hq*max_pages] estimated page maximum
   size_t tau_hat;   // f64 [B*Hq]
@@ -49,14 +49,17 @@ inline int score_stride(int max_pages) { return (max_pages + 3) & ~3; }
 constexpr int kSmxMaxSlots = 256;  // softmax decode blocks per (sequence, KV head), at most
 
 inline Layout make_layout(int B, int Hkv, int Hq, int max_pages, int P, int D = 128) {
+  (void)Hkv;  // every per-unit array is sized for B * Hq units
   Layout L{};
   size_t off = 0;
   const size_t bh = size_t(B) * Hq;
   L.max_items = (size_t(max_pages) * P + kItemTokens - 1) / kItemTokens;
   const size_t tok = L.max_items * kItemTokens;
   L.status = off;   off = align256(off + 4);
-  L.sel_done = off; off = align256(off + 4 * size_t(B) * Hkv);
-  L.scores = off;   off = align256(off + 4 * size_t(B) * Hkv * score_stride(max_pages));
+  // selection units are (sequence, KV head), or (sequence, query head) in
+  // per-query-head mode: size the per-unit arrays for the larger count
+  L.sel_done = off; off = align256(off + 4 * bh);
+  L.scores = off;   off = align256(off + 4 * bh * score_stride(max_pages));
   L.musd = off;     off = align256(off + 8 * bh * max_pages);
   L.ehat = off;     off = align256(off + 4 * bh * max_pages);
   L.tau_hat = off;  off = align256(off + 8 * bh);

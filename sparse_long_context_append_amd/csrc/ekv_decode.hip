@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kDecThreads) void gather_mfma_kernel(DecodeArgs a, 
     for (int s = 0; s < SUB; ++s) {
       if (tr[s].phys >= 0) {
         const uint16_t* row = reinterpret_cast<const uint16_t*>(a.k) +
-                              (((size_t)tr[s].phys * Hkv + g) * a.page_size + tr[s].slot) * D + 8 * grp;
+                              (((size_t)tr[s].phys * a.hkv_mem + (g >> a.kv_shift)) * a.page_size + tr[s].slot) * D + 8 * grp;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) bv[s][kb] = *reinterpret_cast<const u32x4_t*>(row + 32 * kb);
       } else {
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(kDecThreads) void gather_valu_kernel(DecodeArgs a, 
       const int r = it * RPI + w * RPW + rloc;
       if (tr[it].phys >= 0)
         v[it] = ldg16(reinterpret_cast<const char*>(a.k) +
-                      ((((size_t)tr[it].phys * Hkv + g) * a.page_size + tr[it].slot) * D + dim0) * E::kBytes);
+                      ((((size_t)tr[it].phys * a.hkv_mem + (g >> a.kv_shift)) * a.page_size + tr[it].slot) * D + dim0) * E::kBytes);
       if (sub == 0) {
         s_t[r] = tr[it].logical;
         s_r[r] = tr[it].phys * a.page_size + tr[it].slot;
@@ -870,7 +870,7 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
     const float p = xs[s];
     const int phys = row / P, slot = row - phys * P;
     const char* vrow = reinterpret_cast<const char*>(a.v) +
-                       ((((size_t)phys * Hkv + g) * P + slot) * D + (size_t)sub * EPL) * E::kBytes;
+                       ((((size_t)phys * a.hkv_mem + (g >> a.kv_shift)) * P + slot) * D + (size_t)sub * EPL) * E::kBytes;
     float f[EPL];
     E::unpack(ldg16(vrow), f);
 #pragma unroll
@@ -1013,7 +1013,7 @@ __global__ __launch_bounds__(kDecThreads) void softmax_part_kernel(DecodeArgs a,
 #pragma unroll
     for (int s = 0; s < SUB; ++s) {
       if (tr[s].phys >= 0) {
-        const size_t rowi = (((size_t)tr[s].phys * Hkv + g) * P + tr[s].slot) * D + 8 * grp;
+        const size_t rowi = (((size_t)tr[s].phys * a.hkv_mem + (g >> a.kv_shift)) * P + tr[s].slot) * D + 8 * grp;
         const uint16_t* krow = reinterpret_cast<const uint16_t*>(a.k) + rowi;
         const uint16_t* vrow = reinterpret_cast<const uint16_t*>(a.v) + rowi;
 #pragma unroll

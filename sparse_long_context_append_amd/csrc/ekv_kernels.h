@@ -23,8 +23,14 @@ struct AppendArgs {
   uint32_t* status;
 };
 
+// n_kv_heads and group describe the selection units: a unit is (sequence,
+// KV head) with `group` query heads, or, in per-query-head mode, (sequence,
+// query head) with group 1.  Cache records of unit head g live at KV head
+// g >> kv_shift of the cache's hkv_mem heads.
 struct SelectArgs {
   int batch, n_kv_heads, n_q_heads, group, page_size, head_dim, kv_dtype, max_pages, n_phys;
+  int hkv_mem, kv_shift;
+  int per_head_scores;  // bbox scoring: one score row per query head instead of the group maximum
   const int32_t* page_table;
   const int32_t* seq_lens;
   const void* k_box;
@@ -50,6 +56,7 @@ struct SelectArgs {
 
 struct DecodeArgs {
   int batch, n_kv_heads, n_q_heads, group, page_size, head_dim, kv_dtype, max_pages, n_phys;
+  int hkv_mem, kv_shift;  // as in SelectArgs
   const int32_t* page_table;
   const int32_t* seq_lens;
   const void* k;

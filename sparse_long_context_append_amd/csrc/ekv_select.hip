@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_bbox_mfma_kernel(SelectAr
 #pragma unroll
   for (int ng = 0; ng < NG; ++ng) {
     if (phys[ng] >= 0) {
-      const uint16_t* rec = reinterpret_cast<const uint16_t*>(a.k_box) + ((size_t)phys[ng] * Hkv + g) * K + 8 * grp;
+      const uint16_t* rec = reinterpret_cast<const uint16_t*>(a.k_box) + ((size_t)phys[ng] * a.hkv_mem + (g >> a.kv_shift)) * K + 8 * grp;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) bv[ng][kb] = *reinterpret_cast<const u32x4_t*>(rec + 32 * kb);
     } else {
@@ -122,11 +122,18 @@ __global__ __launch_bounds__(kScoreThreads) void score_bbox_mfma_kernel(SelectAr
       const f32x4_t c = mfma_bf16(s_a[kb][lane], bv[ng][kb], f32x4_t{0.f, 0.f, 0.f, 0.f});
       U += ((double)c[0] + (double)c[1]) + (double)c[2];
     }
-    // lane holds head `grp` of page `col`; the page score is the group maximum
+    // lane holds head `grp` of page `col`; the shared page score is the
+    // group maximum, the per-head score the lane's own value
+    const int p = p0 + (ng * 4 + w) * 16;
+    if (a.per_head_scores) {
+      if (grp < G && p < a.max_pages)
+        a.scores[((size_t)b * a.n_q_heads + (size_t)g * G + grp) * a.score_stride + p] =
+            phys[ng] >= 0 ? float(U * (double)a.scale) : -INFINITY;
+      continue;
+    }
     double S = grp < G ? U : -INFINITY;
     S = fmax(S, __shfl_xor(S, 16, kWave));
     S = fmax(S, __shfl_xor(S, 32, kWave));
-    const int p = p0 + (ng * 4 + w) * 16;
     if (grp == 0 && p < a.max_pages)
       a.scores[((size_t)b * Hkv + g) * a.score_stride + p] = phys[ng] >= 0 ? float(S * (double)a.scale) : -INFINITY;
   }
@@ -153,7 +160,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_bbox_valu_kernel(SelectAr
   const int phys = page_phys_spec(a, b, p, &n_b);
   uint4 v[NL];
   if (phys >= 0) {
-    const char* rec = reinterpret_cast<const char*>(a.k_box) + ((size_t)phys * Hkv + g) * 2 * D * E::kBytes;
+    const char* rec = reinterpret_cast<const char*>(a.k_box) + ((size_t)phys * a.hkv_mem + (g >> a.kv_shift)) * 2 * D * E::kBytes;
 #pragma unroll
     for (int i = 0; i < NL; ++i) v[i] = ldg16(rec + 16 * (sub + 4 * i));
   }
@@ -183,7 +190,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_bbox_valu_kernel(SelectAr
   for (int h = 0; h < G; ++h) {
     acc[h] = group_reduce<4>(acc[h], [](double u, double v) { return u + v; });
   }
-  if (sub == 0 && p < a.max_pages) {
+  if (sub == 0 && p < a.max_pages && a.per_head_scores) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      a.scores[((size_t)b * a.n_q_heads + (size_t)g * G + h) * a.score_stride + p] =
+          phys >= 0 ? float(acc[h] * (double)a.scale) : -INFINITY;
+  } else if (sub == 0 && p < a.max_pages) {
     double s = acc[0];
 #pragma unroll
     for (int h = 1; h < G; ++h) s = fmax(s, acc[h]);
@@ -369,7 +381,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_gauss_kernel(SelectArgs a
 #pragma unroll
   for (int n = 0; n < NP; ++n) {
     if (phys[n] >= 0) {
-      const float4* rec = reinterpret_cast<const float4*>(a.k_moments + ((size_t)phys[n] * Hkv + g) * 2 * D);
+      const float4* rec = reinterpret_cast<const float4*>(a.k_moments + ((size_t)phys[n] * a.hkv_mem + (g >> a.kv_shift)) * 2 * D);
 #pragma unroll
       for (int i = 0; i < NL; ++i) v[n][i] = rec[sub + 8 * i];
     }

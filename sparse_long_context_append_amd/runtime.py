@@ -50,8 +50,11 @@ class DecodeSession:
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         B.workspace_init(self.ws)
         self.cap = int(cap if cap is not None else self.max_pages)
-        self.sel = torch.zeros((batch, n_kv_heads, self.cap), dtype=torch.int32, device=self.device)
-        self.sel_count = torch.zeros((batch, n_kv_heads), dtype=torch.int32, device=self.device)
+        # room for one page list per query head; the last selection decides
+        # whether the rows are KV heads (shared lists) or query heads
+        self._sel_buf = torch.zeros(batch * n_q_heads * self.cap, dtype=torch.int32, device=self.device)
+        self._cnt_buf = torch.zeros(batch * n_q_heads, dtype=torch.int32, device=self.device)
+        self.sel_heads = n_kv_heads
         self.out = torch.zeros((batch, n_q_heads, head_dim), dtype=torch.float32, device=self.device)
         self.tau = torch.zeros((batch, n_q_heads), dtype=torch.float32, device=self.device)
         self.support_count = torch.zeros((batch, n_q_heads), dtype=torch.int32, device=self.device)
@@ -76,15 +79,28 @@ class DecodeSession:
             self.seq_lens[seq] += n
 
     # -- decode step --------------------------------------------------------
-    def select(self, q, *, policy, alpha, scale, top_k=0, delta=0.0):
+    @property
+    def sel(self):
+        """[batch][sel_heads][cap] selected logical pages of the last selection."""
+        n = self.batch * self.sel_heads
+        return self._sel_buf[: n * self.cap].view(self.batch, self.sel_heads, self.cap)
+
+    @property
+    def sel_count(self):
+        return self._cnt_buf[: self.batch * self.sel_heads].view(self.batch, self.sel_heads)
+
+    def select(self, q, *, policy, alpha, scale, top_k=0, delta=0.0, per_head=False):
+        """Page selection shared by each KV head's query group, or one
+        selection per query head (per_head=True)."""
+        self.sel_heads = self.n_q_heads if per_head else self.n_kv_heads
         B.select_pages(self.cache, self.seqs, q, self.n_q_heads, policy=policy, top_k=top_k, alpha=alpha,
-                       scale=scale, delta=delta, sel=self.sel, sel_count=self.sel_count, cap=self.cap,
-                       tau_hat=self.tau_hat, ws=self.ws)
+                       scale=scale, delta=delta, per_head=per_head, sel=self.sel, sel_count=self.sel_count,
+                       cap=self.cap, tau_hat=self.tau_hat, ws=self.ws)
 
     def decode(self, q, *, alpha, scale, sparse=True, support_idx=None, support_p=None, support_cap=0):
         B.entmax_decode(self.cache, self.seqs, q, self.n_q_heads, alpha=alpha, scale=scale,
                         sel=self.sel if sparse else None, sel_count=self.sel_count if sparse else None,
-                        cap=self.cap if sparse else 0, out=self.out, tau=self.tau,
+                        cap=self.cap if sparse else 0, sel_heads=self.sel_heads, out=self.out, tau=self.tau,
                         support_count=self.support_count, psum=self.psum, support_idx=support_idx,
                         support_p=support_p, support_cap=support_cap, ws=self.ws)
 
@@ -93,16 +109,18 @@ class DecodeSession:
         writes `out` (default: the session's output buffer)."""
         B.softmax_decode(self.cache, self.seqs, q, self.n_q_heads, scale=scale,
                          sel=self.sel if sparse else None, sel_count=self.sel_count if sparse else None,
-                         cap=self.cap if sparse else 0, out=self.out if out is None else out, lse=lse, ws=self.ws)
+                         cap=self.cap if sparse else 0, sel_heads=self.sel_heads,
+                         out=self.out if out is None else out, lse=lse, ws=self.ws)
 
-    def scores(self, q, *, policy, alpha, scale):
+    def scores(self, q, *, policy, alpha, scale, per_head=False):
         torch = self.torch
         if policy == B.EKV_SELECT_BBOX_TOPK:
-            s = torch.empty((self.batch, self.n_kv_heads, self.max_pages), dtype=torch.float32, device=self.device)
+            rows = self.n_q_heads if per_head else self.n_kv_heads
+            s = torch.empty((self.batch, rows, self.max_pages), dtype=torch.float32, device=self.device)
         else:
             s = torch.empty((self.batch, self.n_q_heads, self.max_pages, 4), dtype=torch.float32, device=self.device)
         B.score_pages(self.cache, self.seqs, q, self.n_q_heads, policy=policy, alpha=alpha, scale=scale,
-                      scores=s, ws=self.ws)
+                      per_head=per_head, scores=s, ws=self.ws)
         return s
 
     def device_status(self) -> int:

@@ -16,14 +16,15 @@ def policy_of(spec):
     return ekv.EKV_SELECT_BBOX_TOPK if spec.policy == "bbox" else ekv.EKV_SELECT_GAUSS
 
 
-def run_step(sess, spec, q_np, sparse=True):
-    """select (when sparse) + decode on the device; returns host copies."""
+def run_step(sess, spec, q_np, sparse=True, per_head=False):
+    """select (when sparse) + decode on the device; returns host copies.
+    per_head: one selection per query head instead of per KV head."""
     import torch
     q = torch.from_numpy(np.ascontiguousarray(q_np, dtype=np.float32)).to(sess.device)
     supp = torch.full((spec.batch, spec.n_q_heads, SUPPORT_CAP), -1, dtype=torch.int32, device=sess.device)
     if sparse:
         sess.select(q, policy=policy_of(spec), alpha=spec.alpha, scale=spec.scale, top_k=spec.top_k,
-                    delta=spec.delta)
+                    delta=spec.delta, per_head=per_head)
     sess.decode(q, alpha=spec.alpha, scale=spec.scale, sparse=sparse, support_idx=supp, support_cap=SUPPORT_CAP)
     torch.cuda.synchronize()
     res = {
@@ -33,15 +34,19 @@ def run_step(sess, spec, q_np, sparse=True):
         "tau_hat": sess.tau_hat.cpu().numpy(), "lens": sess.seq_lens.cpu().numpy(),
     }
     if sparse and spec.policy == "bbox":
-        res["scores"] = sess.scores(q, policy=policy_of(spec), alpha=spec.alpha, scale=spec.scale).cpu().numpy()
+        res["scores"] = sess.scores(q, policy=policy_of(spec), alpha=spec.alpha, scale=spec.scale,
+                                    per_head=per_head).cpu().numpy()
     return res
 
 
-def check_step(spec, res, q_np, units, sparse=True, kv_cache=None, heads_per_unit=None):
-    """Compare a device step with the oracle on the given (b, g) units.
+def check_step(spec, res, q_np, units, sparse=True, kv_cache=None, heads_per_unit=None, per_head=False):
+    """Compare a device step with the oracle on the given units: (b, g)
+    KV-head units, or (b, h) query-head units when per_head (the selection
+    rows of res are then query heads).
     kv_cache: optional dict (b, g) -> (keys_f64, vals_f64) reused across calls."""
     worst = 0.0
-    for (b, g) in units:
+    for (b, u) in units:
+        g = u // spec.group if per_head else u
         key = (b, g)
         if kv_cache is not None and key in kv_cache:
             keys, vals = kv_cache[key]
@@ -51,12 +56,12 @@ def check_step(spec, res, q_np, units, sparse=True, kv_cache=None, heads_per_uni
             if kv_cache is not None:
                 kv_cache[key] = (keys, vals)
         L = int(res["lens"][b])
-        uo = UnitOracle(spec, q_np[b], keys, vals, L, g)
+        uo = UnitOracle(spec, q_np[b], keys, vals, L, g, head=u if per_head else None)
         if sparse:
-            gsel = res["sel"][b, g, : res["cnt"][b, g]]
+            gsel = res["sel"][b, u, : res["cnt"][b, u]]
             if spec.policy == "bbox":
                 S = uo.bbox()
-                check_bbox_scores(res["scores"][b, g, : uo.n_pages], S)
+                check_bbox_scores(res["scores"][b, u, : uo.n_pages], S)
                 check_topk(gsel, S, spec.top_k)
             else:
                 uo.gauss()

@@ -28,13 +28,16 @@ def kv_f64(arr, kv_dtype):
 
 
 class UnitOracle:
-    """Oracle view of one (sequence, KV head) at current length L."""
+    """Oracle view of one selection unit at current length L: a (sequence,
+    KV head) whose selection the group's query heads share, or, with
+    `head` given, one query head h of KV head g selecting on its own (the
+    group rules with a group of one head)."""
 
-    def __init__(self, spec, q_b, keys, vals, L, g, alpha=None):
+    def __init__(self, spec, q_b, keys, vals, L, g, alpha=None, head=None):
         self.spec, self.g, self.L = spec, g, int(L)
         self.alpha = spec.alpha if alpha is None else alpha
         self.G = spec.group
-        self.heads = list(range(g * self.G, (g + 1) * self.G))
+        self.heads = list(range(g * self.G, (g + 1) * self.G)) if head is None else [int(head)]
         self.q = np.asarray(q_b, dtype=np.float64)
         self.k = keys[: self.L]
         self.v = vals[: self.L]

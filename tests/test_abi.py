@@ -59,7 +59,7 @@ def test_workspace_size(L):
 
 
 def sp(**kw):
-    p = dict(policy=B.EKV_SELECT_BBOX_TOPK, top_k=8, alpha=1.5, scale=0.125, delta=0.5, reserved=0)
+    p = dict(policy=B.EKV_SELECT_BBOX_TOPK, top_k=8, alpha=1.5, scale=0.125, delta=0.5, per_head=0)
     p.update(kw)
     return B._SelectParams(**p)
 
@@ -88,12 +88,15 @@ def test_select_validation(L):
     assert call_select(L, s=seqs(batch=1024)) == B.EKV_ERR_UNSUPPORTED  # 8192 units
     assert call_select(L, hq=20) == B.EKV_ERR_INVALID_ARG
     assert call_select(L, sel=None) == B.EKV_ERR_INVALID_ARG
+    assert call_select(L, p=sp(per_head=2)) == B.EKV_ERR_INVALID_ARG
+    # per query head the units are batch * n_q_heads: 200 * 32 = 6400 > 4096
+    assert call_select(L, s=seqs(batch=200), p=sp(per_head=1)) == B.EKV_ERR_UNSUPPORTED
 
 
-def call_decode(L, q=FAKE, alpha=1.5, scale=0.125, sel=FAKE, cnt=FAKE, cap=64, out=FAKE, sidx=None, scap=0,
-                ws=FAKE, wsb=1 << 40, c=None):
-    return L.ekv_entmax_decode(ctypes.byref(c or cache()), ctypes.byref(seqs()), q, 32, alpha, scale, sel, cnt,
-                               cap, out, None, None, None, sidx, None, scap, ws, wsb, None)
+def call_decode(L, q=FAKE, alpha=1.5, scale=0.125, sel=FAKE, cnt=FAKE, cap=64, sel_heads=8, out=FAKE, sidx=None,
+                scap=0, ws=FAKE, wsb=1 << 40, c=None, s=None):
+    return L.ekv_entmax_decode(ctypes.byref(c or cache()), ctypes.byref(s or seqs()), q, 32, alpha, scale, sel, cnt,
+                               cap, sel_heads, out, None, None, None, sidx, None, scap, ws, wsb, None)
 
 
 def test_decode_validation(L):
@@ -107,17 +110,21 @@ def test_decode_validation(L):
     assert call_decode(L, wsb=100) == B.EKV_ERR_WORKSPACE
     assert call_decode(L, c=cache(k=None)) == B.EKV_ERR_INVALID_ARG
     assert call_decode(L, c=cache(kv_dtype=5)) == B.EKV_ERR_INVALID_ARG
+    assert call_decode(L, sel_heads=5) == B.EKV_ERR_INVALID_ARG  # neither n_kv_heads nor n_q_heads
+    assert call_decode(L, sel_heads=32, s=seqs(batch=200)) == B.EKV_ERR_UNSUPPORTED
 
 
 def test_softmax_validation(L):
     f = L.ekv_softmax_decode
-    call = lambda c=None, sel=FAKE, cnt=FAKE, cap=64, out=FAKE, scale=0.125, wsb=1 << 40: f(
-        ctypes.byref(c or cache()), ctypes.byref(seqs()), FAKE, 32, scale, sel, cnt, cap, out, None, FAKE, wsb, None)
+    call = lambda c=None, sel=FAKE, cnt=FAKE, cap=64, sh=8, out=FAKE, scale=0.125, wsb=1 << 40: f(
+        ctypes.byref(c or cache()), ctypes.byref(seqs()), FAKE, 32, scale, sel, cnt, cap, sh, out, None, FAKE, wsb,
+        None)
     assert call(out=None) == B.EKV_ERR_INVALID_ARG
     assert call(scale=0.0) == B.EKV_ERR_INVALID_ARG
     assert call(cnt=None) == B.EKV_ERR_INVALID_ARG
     assert call(wsb=100) == B.EKV_ERR_WORKSPACE
     assert call(c=cache(kv_dtype=B.EKV_F32)) == B.EKV_ERR_UNSUPPORTED
+    assert call(sh=7) == B.EKV_ERR_INVALID_ARG
 
 
 def test_append_validation(L):
