@@ -436,6 +436,87 @@ def run_compare(args, torch, timer):
                       "steps": args.steps, "warmup": args.warmup, "compare": rows}), flush=True)
 
 
+def _selection_quality(spec, sel, scnt, per_head, ids, ps, cnt, SC):
+    """Per query head: full-cache entmax mass outside the head's page list
+    and the share of the full-cache support inside it."""
+    P = spec.page_size
+    d_ent, keep = [], []
+    for b in range(spec.batch):
+        for h in range(spec.n_q_heads):
+            r = h if per_head else h // spec.group
+            pages = sel[b, r, : scnt[b, r]].astype(np.int64)
+            n = min(int(cnt[b, h]), SC)
+            tok = ids[b, h, :n].astype(np.int64)
+            kept = np.isin(tok // P, pages)
+            d_ent.append(float(ps[b, h, :n][~kept].sum()))
+            keep.append(float(kept.mean()) if n else 1.0)
+    return np.array(d_ent), np.array(keep)
+
+
+def gqa_one(spec, args, torch, timer):
+    """Shared (one page set per KV head, used by its query group) against
+    per-query-head selection, at the same per-head budget and, for top-k, at
+    the same pages read per KV head (k/G per query head)."""
+    import sparse_long_context_append_amd as ekv
+    from workloads.upload import build_session, queries_device
+    sess, _ = build_session(spec)
+    q = queries_device(spec)
+    pol = ekv.EKV_SELECT_BBOX_TOPK if spec.policy == "bbox" else ekv.EKV_SELECT_GAUSS
+    B, Hq, G = spec.batch, spec.n_q_heads, spec.group
+    SC = 1 << 14
+    sidx = torch.full((B, Hq, SC), -1, dtype=torch.int32, device="cuda")
+    sp = torch.zeros((B, Hq, SC), dtype=torch.float32, device="cuda")
+    sess.decode(q, alpha=spec.alpha, scale=spec.scale, sparse=False, support_idx=sidx, support_p=sp, support_cap=SC)
+    o_full = sess.out.clone()
+    torch.cuda.synchronize()
+    cnt, ids, ps = sess.support_count.cpu().numpy(), sidx.cpu().numpy(), sp.cpu().numpy()
+    variants = [("shared", False, spec.top_k), ("per_head", True, spec.top_k)]
+    if spec.policy == "bbox":
+        variants.append(("per_head_matched_bytes", True, max(1, spec.top_k // G)))
+    page_bytes = spec.page_size * spec.head_dim * (2 if spec.kv_dtype == "bf16" else 4)
+    rows = []
+    for label, per_head, k in variants:
+        def step():
+            sess.select(q, policy=pol, alpha=spec.alpha, scale=spec.scale, top_k=k, delta=spec.delta,
+                        per_head=per_head)
+            sess.decode(q, alpha=spec.alpha, scale=spec.scale, sparse=True)
+        ms, _ = timer.run(step, args.steps, args.warmup)
+        step()
+        torch.cuda.synchronize()
+        sel, scnt = sess.sel.cpu().numpy(), sess.sel_count.cpu().numpy()
+        d_ent, keep = _selection_quality(spec, sel, scnt, per_head, ids, ps, cnt, SC)
+        err = (torch.linalg.vector_norm(sess.out - o_full, dim=-1) / torch.linalg.vector_norm(o_full, dim=-1))
+        err = err.cpu().numpy()
+        # K pages the gather reads: once per KV head for a shared list, once per query head otherwise
+        pages_read = int(scnt.sum())
+        distinct = 0
+        for b in range(B):
+            for g in range(spec.n_kv_heads):
+                rr = range(g * G, (g + 1) * G) if per_head else [g]
+                distinct += len(set(np.concatenate([sel[b, r, : scnt[b, r]] for r in rr]).tolist()))
+        rows.append({"selection": label, "top_k": k if spec.policy == "bbox" else None,
+                     "pages_per_query_head_mean": round(float(scnt.mean()), 2),
+                     "k_pages_read": pages_read, "k_bytes_read": pages_read * page_bytes,
+                     "distinct_pages_per_kv_head_mean": round(distinct / (B * spec.n_kv_heads), 2),
+                     "dropped_mass_mean": float(d_ent.mean()), "dropped_mass_max": float(d_ent.max()),
+                     "support_retention_mean": float(keep.mean()),
+                     "heads_with_full_support": int((keep == 1.0).sum()), "heads": int(keep.size),
+                     "rel_out_err_mean": float(err.mean()), "rel_out_err_max": float(err.max()),
+                     "step_us": round(statistics.median(ms) * 1e3, 2)})
+        log(f"gqa {spec.name} {label}: dropped {rows[-1]['dropped_mass_mean']:.4f}, retention "
+            f"{rows[-1]['support_retention_mean']:.4f}, {rows[-1]['step_us']} us")
+    del sess
+    torch.cuda.empty_cache()
+    return {"workload": spec.name, "selector": spec.policy, "alpha": spec.alpha, "group": G, "rows": rows}
+
+
+def run_gqa(args, torch, timer):
+    out = [gqa_one(W.make_spec(name), args, torch, timer) for name in ("c2", "c3", "c4")]
+    print(json.dumps({"metric": "shared vs per-query-head page selection under grouped-query attention",
+                      "n_gpus": 1, "data": "synthetic", "steps": args.steps, "warmup": args.warmup,
+                      "gqa": out}), flush=True)
+
+
 def copy_probe(mib):
     """A plain copy kernel of known size: HBM read and write counters of its
     dispatches calibrate the counters of the path's kernels."""
@@ -484,6 +565,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--context", type=int, default=0, help="override the workload's context (scaling sweeps)")
+    ap.add_argument("--q-heads", type=int, default=0,
+                    help="override the workload's query-head count (query groups of other sizes)")
     ap.add_argument("--cpu-units", type=int, default=2, help="(sequence, KV head) units the CPU oracle is timed on")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline line: context sweep 32K..1M of the top-2%% and Gaussian "
@@ -491,6 +574,9 @@ def main():
     ap.add_argument("--compare", action="store_true",
                     help="instead of the headline line: entmax vs softmax at the same selected pages (dropped "
                          "mass, support retention, output error, decode times) on c2, c3, c4")
+    ap.add_argument("--gqa", action="store_true",
+                    help="instead of the headline line: shared vs per-query-head selection (dropped mass, "
+                         "support retention, output error, pages read, step time) on c2, c3, c4")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (counter calibration)")
     args = ap.parse_args()
@@ -510,7 +596,12 @@ def main():
     if args.compare:
         run_compare(args, torch, timer)
         return
+    if args.gqa:
+        run_gqa(args, torch, timer)
+        return
     over = {"context": args.context} if args.context else {}
+    if args.q_heads:
+        over["n_q_heads"] = args.q_heads
     spec = W.make_spec(args.workload, **over)
     log(f"device {torch.cuda.get_device_name(0)}; workload {spec.name}")
     r = measure(spec, args.steps, args.warmup, torch, timer, not args.no_dense, not args.no_graph)

@@ -111,33 +111,37 @@ __device__ __forceinline__ void split3_bf16(float c, uint32_t* l0, uint32_t* l1,
 
 // A operand of a 16-row limb product: chunk (kb, ln) holds, for row ln%16 =
 // 4h + l and k = 32 kb + 8 (ln/16) + j (j < 8), limb l of coefficient
-// coef(h, k); rows with h >= G or l = 3 are zero.  Thread t owns chunks
-// t, t + blockDim, ...; limb_fetch reads the raw values its chunks need
-// (issue it before other loads so it is not queued behind them) and
-// limb_build writes each chunk with one conflict-free 16-byte LDS store.
-template <int KB> struct LimbChunks {
-  static constexpr int kPerThread = (KB * kWave + 255) / 256;  // for 256-thread blocks
+// coef(h, k); rows with h >= G or l = 3 are zero.  Groups of more than 4
+// heads take NH = ceil(G/4) such operands, operand hh holding heads
+// 4 hh .. 4 hh + 3 in s_a[hh KB + kb].  Thread t owns chunks t, t +
+// blockDim, ...; limb_fetch reads the raw values its chunks need (issue it
+// before other loads so it is not queued behind them) and limb_build writes
+// each chunk with one conflict-free 16-byte LDS store.
+template <int KB, int NH = 1> struct LimbChunks {
+  static constexpr int kPerThread = (NH * KB * kWave + 255) / 256;  // for 256-thread blocks
   float v[kPerThread][8];
 };
 
-template <int KB, int G, typename Fetch8>
-__device__ __forceinline__ void limb_fetch(LimbChunks<KB>& lc, Fetch8 fetch8) {
+template <int KB, int G, int NH = 1, typename Fetch8>
+__device__ __forceinline__ void limb_fetch(LimbChunks<KB, NH>& lc, Fetch8 fetch8) {
 #pragma unroll
-  for (int i = 0; i < LimbChunks<KB>::kPerThread; ++i) {
+  for (int i = 0; i < LimbChunks<KB, NH>::kPerThread; ++i) {
     const int c = threadIdx.x + 256 * i;
-    const int kb = c >> 6, ln = c & 63, row = ln & 15, kg = ln >> 4, h = row >> 2;
-    if (c < KB * kWave && h < G && (row & 3) < 3) fetch8(h, 32 * kb + 8 * kg, lc.v[i]);
+    const int hh = c / (KB * kWave), cc = c - hh * (KB * kWave);
+    const int kb = cc >> 6, ln = cc & 63, row = ln & 15, kg = ln >> 4, h = 4 * hh + (row >> 2);
+    if (c < NH * KB * kWave && h < G && (row & 3) < 3) fetch8(h, 32 * kb + 8 * kg, lc.v[i]);
   }
 }
 
-template <int KB, int G, typename Coef>
-__device__ __forceinline__ void limb_build(u32x4_t (*s_a)[kWave], const LimbChunks<KB>& lc, Coef coef) {
+template <int KB, int G, int NH = 1, typename Coef>
+__device__ __forceinline__ void limb_build(u32x4_t (*s_a)[kWave], const LimbChunks<KB, NH>& lc, Coef coef) {
 #pragma unroll
-  for (int i = 0; i < LimbChunks<KB>::kPerThread; ++i) {
+  for (int i = 0; i < LimbChunks<KB, NH>::kPerThread; ++i) {
     const int c = threadIdx.x + 256 * i;
-    if (c >= KB * kWave) break;
-    const int kb = c >> 6, ln = c & 63, row = ln & 15, kg = ln >> 4;
-    const int h = row >> 2, limb = row & 3;
+    if (c >= NH * KB * kWave) break;
+    const int hh = c / (KB * kWave), cc = c - hh * (KB * kWave);
+    const int kb = cc >> 6, ln = cc & 63, row = ln & 15, kg = ln >> 4;
+    const int h = 4 * hh + (row >> 2), limb = row & 3;
     uint32_t wv[4] = {0u, 0u, 0u, 0u};
     if (h < G && limb < 3) {
 #pragma unroll
@@ -148,7 +152,7 @@ __device__ __forceinline__ void limb_build(u32x4_t (*s_a)[kWave], const LimbChun
         wv[j >> 1] |= (bits & 0xffffu) << (16 * (j & 1));
       }
     }
-    s_a[kb][ln] = u32x4_t{wv[0], wv[1], wv[2], wv[3]};
+    s_a[hh * KB + kb][ln] = u32x4_t{wv[0], wv[1], wv[2], wv[3]};
   }
 }
 

@@ -128,12 +128,13 @@ __device__ __forceinline__ void resolve_refs(const DecodeArgs& a, int u, int b, 
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core gather (bf16 keys, G <= 4).  Grid (slots, units): block
+// Matrix-core gather (bf16 keys).  Grid (slots, units): block
 // (s, u) takes super-items s, s + slots, ... of unit u, a super-item being
 // SUB consecutive 64-token items whose loads are all issued before any is
 // used.  A rows 4h + l hold limb l of q_h (alpha-1) scale; B columns are the
 // 16 tokens of a wave; the fp32 accumulator runs over the D/32 k blocks.
-// Lane l ends with head l/16 of token l%16: x = (c0 + c1) + c2.
+// Lane l ends with head l/16 of token l%16: x = (c0 + c1) + c2.  Groups of
+// 8 heads take a second operand (heads 4..7) against the same K fragment.
 // ---------------------------------------------------------------------------
 // n^-(alpha-1): the largest distance below a level shared by n scores at
 // which their weights alone reach 1.
@@ -151,9 +152,10 @@ __device__ __forceinline__ double count_pow(int n, float alpha) {
 template <int D, int G, int SUB>
 __global__ __launch_bounds__(kDecThreads) void gather_mfma_kernel(DecodeArgs a, int slots) {
   constexpr int KB = D / 32;
-  __shared__ u32x4_t s_a[KB][kWave];
-  __shared__ float s_max[SUB][4][4];
-  __shared__ int s_cnt[SUB][4][4];
+  constexpr int NH = (G + 3) / 4;  // 16-row operands (four heads each)
+  __shared__ u32x4_t s_a[NH * KB][kWave];
+  __shared__ float s_max[NH][SUB][4][4];
+  __shared__ int s_cnt[NH][SUB][4][4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int u = blockIdx.y, Hkv = a.n_kv_heads;
@@ -165,8 +167,8 @@ __global__ __launch_bounds__(kDecThreads) void gather_mfma_kernel(DecodeArgs a, 
   // references (resolved speculatively with the unit's size)
   const float qs = (a.alpha - 1.f) * a.scale;
   const float* qg = a.q + ((size_t)b * a.n_q_heads + (size_t)g * G) * D;
-  LimbChunks<KB> lc;
-  limb_fetch<KB, G>(lc, [&](int h, int k0, float* v) {
+  LimbChunks<KB, NH> lc;
+  limb_fetch<KB, G, NH>(lc, [&](int h, int k0, float* v) {
     const float4* qv = reinterpret_cast<const float4*>(qg + (size_t)h * D + k0);
     const float4 q0 = qv[0], q1 = qv[1];
     v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w; v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
@@ -192,20 +194,24 @@ __global__ __launch_bounds__(kDecThreads) void gather_mfma_kernel(DecodeArgs a, 
       }
     }
     if (!a_ready) {  // q limbs: coefficients q_h (alpha-1) scale (block-uniform)
-      limb_build<KB, G>(s_a, lc, [qs](int, float qv) { return qv * qs; });
+      limb_build<KB, G, NH>(s_a, lc, [qs](int, float qv) { return qv * qs; });
       __syncthreads();
       a_ready = true;
     }
-    float x[SUB];
+    // lane holds heads grp + 4 hh (hh < NH) of token col
+    float x[NH][SUB];
 #pragma unroll
     for (int s = 0; s < SUB; ++s) {
-      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) c = mfma_bf16(s_a[kb][lane], bv[s][kb], c);
-      x[s] = tr[s].valid && grp < G ? (c[0] + c[1]) + c[2] : -INFINITY;
-      // per-head item maximum (the 16 lanes of one head share grp)
-      const float m = group_reduce<16>(x[s], [](float u, float v) { return fmaxf(u, v); });
-      if (col == 0) s_max[s][w][grp] = m;
+      for (int hh = 0; hh < NH; ++hh) {
+        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) c = mfma_bf16(s_a[hh * KB + kb][lane], bv[s][kb], c);
+        x[hh][s] = tr[s].valid && 4 * hh + grp < G ? (c[0] + c[1]) + c[2] : -INFINITY;
+        // per-head item maximum (the 16 lanes of one head share grp)
+        const float m = group_reduce<16>(x[hh][s], [](float u, float v) { return fmaxf(u, v); });
+        if (col == 0) s_max[hh][s][w][grp] = m;
+      }
     }
     __syncthreads();
     // candidates: above a lower bound on tau (tokens at or below it have
@@ -214,37 +220,48 @@ __global__ __launch_bounds__(kDecThreads) void gather_mfma_kernel(DecodeArgs a, 
     // level l, tau >= l - n^-(alpha-1) (a subset's threshold never exceeds
     // the full set's); this wave's tokens of the head are counted at
     // l = msup - 1/8, - 1/4, - 1/2.
-    float m[SUB], msup = -INFINITY;
+    float m[NH][SUB];
+    double lb[NH];
+    float msup[NH];
+    bool keep[NH][SUB];
+    uint32_t bits[NH][SUB];
 #pragma unroll
-    for (int s = 0; s < SUB; ++s) {
-      m[s] = fmaxf(fmaxf(s_max[s][0][grp], s_max[s][1][grp]), fmaxf(s_max[s][2][grp], s_max[s][3][grp]));
-      msup = fmaxf(msup, m[s]);
-    }
-    double lb = (double)msup - 1.0;
-#pragma unroll
-    for (int ci = 0; ci < 3; ++ci) {
-      const float lvl = msup - 0.125f * (float)(1 << ci);
-      int n = 0;
+    for (int hh = 0; hh < NH; ++hh) {
+      const bool hv = 4 * hh + grp < G;
+      msup[hh] = -INFINITY;
 #pragma unroll
       for (int s = 0; s < SUB; ++s) {
-        const unsigned long long bal = __ballot(grp < G && x[s] >= lvl);
-        n += __popc((uint32_t)(bal >> (16 * grp)) & 0xffffu);
+        m[hh][s] = fmaxf(fmaxf(s_max[hh][s][0][grp], s_max[hh][s][1][grp]),
+                         fmaxf(s_max[hh][s][2][grp], s_max[hh][s][3][grp]));
+        msup[hh] = fmaxf(msup[hh], m[hh][s]);
       }
-      if (n > 0) lb = fmax(lb, (double)lvl - count_pow(n, a.alpha));
-    }
-    lb -= 1e-6 * fmax(1.0, fabs((double)msup));  // margin for the rounding of x
-    bool keep[SUB];
-    uint32_t bits[SUB];
+      lb[hh] = (double)msup[hh] - 1.0;
 #pragma unroll
-    for (int s = 0; s < SUB; ++s) {
-      keep[s] = grp < G && msup > -INFINITY && (double)x[s] > lb;
-      const unsigned long long bal = __ballot(keep[s]);
-      bits[s] = (uint32_t)(bal >> (16 * grp)) & 0xffffu;
-      if (col == 0) s_cnt[s][w][grp] = __popc(bits[s]);
+      for (int ci = 0; ci < 3; ++ci) {
+        const float lvl = msup[hh] - 0.125f * (float)(1 << ci);
+        int n = 0;
+#pragma unroll
+        for (int s = 0; s < SUB; ++s) {
+          const unsigned long long bal = __ballot(hv && x[hh][s] >= lvl);
+          n += __popc((uint32_t)(bal >> (16 * grp)) & 0xffffu);
+        }
+        if (n > 0) lb[hh] = fmax(lb[hh], (double)lvl - count_pow(n, a.alpha));
+      }
+      lb[hh] -= 1e-6 * fmax(1.0, fabs((double)msup[hh]));  // margin for the rounding of x
+#pragma unroll
+      for (int s = 0; s < SUB; ++s) {
+        keep[hh][s] = hv && msup[hh] > -INFINITY && (double)x[hh][s] > lb[hh];
+        const unsigned long long bal = __ballot(keep[hh][s]);
+        bits[hh][s] = (uint32_t)(bal >> (16 * grp)) & 0xffffu;
+        if (col == 0) s_cnt[hh][s][w][grp] = __popc(bits[hh][s]);
+      }
     }
     __syncthreads();
-    if (grp < G) {
-      const size_t bh = (size_t)b * a.n_q_heads + (size_t)g * G + grp;
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      const int h = 4 * hh + grp;
+      if (h >= G) continue;
+      const size_t bh = (size_t)b * a.n_q_heads + (size_t)g * G + h;
 #pragma unroll
       for (int s = 0; s < SUB; ++s) {
         const int j = sj * SUB + s;
@@ -252,20 +269,20 @@ __global__ __launch_bounds__(kDecThreads) void gather_mfma_kernel(DecodeArgs a, 
         int off = 0, tot = 0;
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
-          off += ww < w ? s_cnt[s][ww][grp] : 0;
-          tot += s_cnt[s][ww][grp];
+          off += ww < w ? s_cnt[hh][s][ww][grp] : 0;
+          tot += s_cnt[hh][s][ww][grp];
         }
-        if (keep[s]) {
-          const int pos = off + __popc(bits[s] & ((1u << col) - 1u));
+        if (keep[hh][s]) {
+          const int pos = off + __popc(bits[hh][s] & ((1u << col) - 1u));
           const size_t at = bh * tok_per_bh + (size_t)j * kItemTokens + pos;
-          a.cand_x[at] = x[s];
+          a.cand_x[at] = x[hh][s];
           a.cand_t[at] = tr[s].logical;
           a.cand_r[at] = tr[s].phys * a.page_size + tr[s].slot;
         }
         if (w == 0 && col == 0) {
           a.item_cnt[bh * a.max_items + j] = tot;
-          a.item_max[bh * a.max_items + j] = m[s];
-          a.item_lb[bh * a.max_items + j] = msup > -INFINITY ? __double2float_rd(lb) : -INFINITY;
+          a.item_max[bh * a.max_items + j] = m[hh][s];
+          a.item_lb[bh * a.max_items + j] = msup[hh] > -INFINITY ? __double2float_rd(lb[hh]) : -INFINITY;
         }
       }
     }
@@ -274,7 +291,7 @@ __global__ __launch_bounds__(kDecThreads) void gather_mfma_kernel(DecodeArgs a, 
 }
 
 // ---------------------------------------------------------------------------
-// Vector-ALU gather (fp32 keys or groups of 8): LPR lanes per K row, every
+// Vector-ALU gather (fp32 keys): LPR lanes per K row, every
 // load of the item issued up front, fp32 dot products reduced across the
 // row's lanes; scores staged in LDS, then one wave per head compacts.
 // ---------------------------------------------------------------------------
@@ -900,12 +917,13 @@ __global__ __launch_bounds__(kTauThreads) void tau_v_kernel(DecodeArgs a) {
 template <int DT, int D>
 static hipError_t decode_dispatch(const DecodeArgs& a, int slots, hipStream_t s) {
   const dim3 g1(slots, a.batch * a.n_kv_heads), b1(kDecThreads);
-  const bool mfma = DT == EKV_BF16 && a.group <= 4;
+  const bool mfma = DT == EKV_BF16;
   if (mfma) {
     switch (a.group) {
       case 1: hipLaunchKernelGGL((gather_mfma_kernel<D, 1, 4>), g1, b1, 0, s, a, slots); break;
       case 2: hipLaunchKernelGGL((gather_mfma_kernel<D, 2, 4>), g1, b1, 0, s, a, slots); break;
-      default: hipLaunchKernelGGL((gather_mfma_kernel<D, 4, 4>), g1, b1, 0, s, a, slots); break;
+      case 4: hipLaunchKernelGGL((gather_mfma_kernel<D, 4, 4>), g1, b1, 0, s, a, slots); break;
+      default: hipLaunchKernelGGL((gather_mfma_kernel<D, 8, 4>), g1, b1, 0, s, a, slots); break;
     }
   } else {
     switch (a.group) {
@@ -933,7 +951,7 @@ static hipError_t decode_dispatch(const DecodeArgs& a, int slots, hipStream_t s)
 hipError_t launch_decode(const DecodeArgs& a, int target_blocks, hipStream_t s) {
   const long long pages = a.sel ? (a.cap < a.max_pages ? a.cap : a.max_pages) : a.max_pages;
   const long long items = (pages * a.page_size + kItemTokens - 1) / kItemTokens;
-  const bool mfma = a.kv_dtype == EKV_BF16 && a.group <= 4;
+  const bool mfma = a.kv_dtype == EKV_BF16;
   const int sub = mfma ? 4 : 1;
   const long long supers = (items + sub - 1) / sub;
   const int units = a.batch * a.n_kv_heads;

@@ -71,13 +71,15 @@ __device__ __forceinline__ int page_phys(const SelectArgs& a, int b, int p, int 
 // limb l of c_h: c = l0 + l1 + l2 in bf16 with the remainder below 2^-24 |c|,
 // and bf16 x bf16 products are exact in fp32, so the products carry the full
 // fp32 coefficient.  Each 32-wide k block is accumulated from zero by the
-// matrix core and the block sums are added in float64.
+// matrix core and the block sums are added in float64.  A group of 8 heads
+// takes two such operands against the same record fragment.
 // ---------------------------------------------------------------------------
 template <int D, int G, int NG>
 __global__ __launch_bounds__(kScoreThreads) void score_bbox_mfma_kernel(SelectArgs a) {
   constexpr int K = 2 * D;   // record length (bf16 elements)
   constexpr int KB = K / 32;  // k blocks
-  __shared__ u32x4_t s_a[KB][kWave];
+  constexpr int NH = (G + 3) / 4;  // 16-row operands (four heads each)
+  __shared__ u32x4_t s_a[NH * KB][kWave];
   const int b = blockIdx.z, g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -87,8 +89,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_bbox_mfma_kernel(SelectAr
 
   // loads, in order: q for the A operand, page-table entries, page records
   const float* qg = a.q + ((size_t)b * a.n_q_heads + (size_t)g * G) * D;
-  LimbChunks<KB> lc;
-  limb_fetch<KB, G>(lc, [&](int h, int k0, float* v) {
+  LimbChunks<KB, NH> lc;
+  limb_fetch<KB, G, NH>(lc, [&](int h, int k0, float* v) {
     const int half = k0 >= D;
     const float4* qv = reinterpret_cast<const float4*>(qg + (size_t)h * D + (k0 - half * D));
     const float4 q0 = qv[0], q1 = qv[1];
@@ -111,27 +113,37 @@ __global__ __launch_bounds__(kScoreThreads) void score_bbox_mfma_kernel(SelectAr
     }
   }
   // coefficients [min(q,0) | max(q,0)] over the record, as bf16 limbs
-  limb_build<KB, G>(s_a, lc, [](int k, float qv) { return k >= D ? fmaxf(qv, 0.f) : fminf(qv, 0.f); });
+  limb_build<KB, G, NH>(s_a, lc, [](int k, float qv) { return k >= D ? fmaxf(qv, 0.f) : fminf(qv, 0.f); });
   __syncthreads();
 
 #pragma unroll
   for (int ng = 0; ng < NG; ++ng) {
-    double U = 0.0;
+    double U[NH];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const f32x4_t c = mfma_bf16(s_a[kb][lane], bv[ng][kb], f32x4_t{0.f, 0.f, 0.f, 0.f});
-      U += ((double)c[0] + (double)c[1]) + (double)c[2];
+    for (int hh = 0; hh < NH; ++hh) {
+      U[hh] = 0.0;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const f32x4_t c = mfma_bf16(s_a[hh * KB + kb][lane], bv[ng][kb], f32x4_t{0.f, 0.f, 0.f, 0.f});
+        U[hh] += ((double)c[0] + (double)c[1]) + (double)c[2];
+      }
     }
-    // lane holds head `grp` of page `col`; the shared page score is the
-    // group maximum, the per-head score the lane's own value
+    // lane holds heads grp, grp + 4, ... of page `col`; the shared page
+    // score is the group maximum, the per-head score the lane's own values
     const int p = p0 + (ng * 4 + w) * 16;
     if (a.per_head_scores) {
-      if (grp < G && p < a.max_pages)
-        a.scores[((size_t)b * a.n_q_heads + (size_t)g * G + grp) * a.score_stride + p] =
-            phys[ng] >= 0 ? float(U * (double)a.scale) : -INFINITY;
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) {
+        const int h = 4 * hh + grp;
+        if (h < G && p < a.max_pages)
+          a.scores[((size_t)b * a.n_q_heads + (size_t)g * G + h) * a.score_stride + p] =
+              phys[ng] >= 0 ? float(U[hh] * (double)a.scale) : -INFINITY;
+      }
       continue;
     }
-    double S = grp < G ? U : -INFINITY;
+    double S = -INFINITY;
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) S = 4 * hh + grp < G ? fmax(S, U[hh]) : S;
     S = fmax(S, __shfl_xor(S, 16, kWave));
     S = fmax(S, __shfl_xor(S, 32, kWave));
     if (grp == 0 && p < a.max_pages)
@@ -140,7 +152,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_bbox_mfma_kernel(SelectAr
 }
 
 // ---------------------------------------------------------------------------
-// Bounding-box score on the vector ALUs (fp32 records or groups > 4): four
+// Bounding-box score on the vector ALUs (fp32 records): four
 // lanes per page record, each lane walks a quarter of the record in 16-byte
 // loads issued together; coefficients min(q,0) / max(q,0) as above, float64
 // accumulation, a two-step reduction across the four lanes.
@@ -764,7 +776,7 @@ __global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
 template <int DT, int D>
 static hipError_t bbox_dispatch(const SelectArgs& a, hipStream_t s) {
   const dim3 blk(kScoreThreads);
-  if (DT == EKV_BF16 && a.group <= 4) {
+  if (DT == EKV_BF16) {
     // four 16-page groups per wave when that still leaves >= 512 blocks
     const long long recs = (long long)a.max_pages * a.n_kv_heads * a.batch;
     const bool fat = recs >= 512LL * 256;
@@ -776,7 +788,8 @@ static hipError_t bbox_dispatch(const SelectArgs& a, hipStream_t s) {
     switch (a.group) {
       case 1: EKV_BBOX(1); break;
       case 2: EKV_BBOX(2); break;
-      default: EKV_BBOX(4); break;
+      case 4: EKV_BBOX(4); break;
+      default: EKV_BBOX(8); break;
     }
 #undef EKV_BBOX
     return hipGetLastError();

@@ -92,6 +92,17 @@ def test_c2_reduced(ctx, P, topk):
     check_step(spec, run_step(sess, spec, q, sparse=False), q, all_units(spec), sparse=False)
 
 
+@pytest.mark.parametrize("ctx,topk", [(4099, 40), (1500, 200)])
+def test_c2_group_of_8(ctx, topk):
+    """Groups of 8 query heads per KV head: two 16-row operands on the
+    matrix cores in both the box scoring and the gather."""
+    spec = W.make_spec("c2", context=ctx, page_size=16, top_k=topk, n_q_heads=16, n_kv_heads=2, n_needles=16)
+    sess, _ = _session(spec)
+    q = W.queries(spec)
+    check_step(spec, run_step(sess, spec, q), q, all_units(spec))
+    check_step(spec, run_step(sess, spec, q, sparse=False), q, all_units(spec), sparse=False)
+
+
 def test_c2_full():
     spec = W.make_spec("c2")
     sess, _ = _session(spec)
