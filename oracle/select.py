@@ -16,6 +16,10 @@ EntmaxKV summary section 2.B names two policies:
            F(t) = sum_p n_p E[(Y_p - t)_+^(1/(alpha-1))] = 1,
          Y_p ~ N(mean_Y,p, sd_Y,p^2),
        solved per query head;
+     * for alpha other than 1.5 and 2 the expectation is the truncated
+       normal moment sd^e M_e(u) (a parabolic cylinder function), and the
+       estimate is defined for 1 < alpha <= 2, where the left end of the
+       bisection bracket follows from Jensen's inequality;
      * Delta is measured in the scaled domain where tau lives;
      * a page is kept for a KV head when any query head of its group keeps
        it: max_h (e_hat[h,p] - tau_hat[h]) > -Delta (strict);
@@ -28,7 +32,7 @@ from __future__ import annotations
 import math
 
 import numpy as np
-from scipy.special import erfc
+from scipy.special import erfc, gamma, pbdv
 
 _INV_SQRT2 = 1.0 / math.sqrt(2.0)
 _INV_SQRT2PI = 1.0 / math.sqrt(2.0 * math.pi)
@@ -42,12 +46,38 @@ def topk_pages(S: np.ndarray, k: int) -> np.ndarray:
     return np.sort(order[: min(k, n)])
 
 
+def truncated_normal_moment(u: np.ndarray, beta: float) -> np.ndarray:
+    """M_beta(u) = E[Z_+^beta] for Z ~ N(u, 1), beta > -1.
+
+    The integral representation of the parabolic cylinder function (DLMF
+    12.5.1 with D_nu = U(-nu - 1/2, .)) gives
+        int_0^inf z^beta exp(-z^2/2 + u z) dz = Gamma(beta+1) exp(u^2/4) D_{-beta-1}(-u),
+    so M_beta(u) = Gamma(beta+1) exp(-u^2/4) D_{-beta-1}(-u) / sqrt(2 pi).
+    For u > 25 that product under/overflows; there P(Z < 0) < 1e-137, so
+    M_beta(u) = u^beta E[(1 + W/u)^beta], W ~ N(0, 1), which is smooth in W
+    over |W| < u and is taken by 80-point Gauss-Hermite quadrature."""
+    u = np.atleast_1d(np.asarray(u, dtype=np.float64))
+    out = np.empty_like(u)
+    small = u <= 25.0
+    if np.any(small):
+        d, _ = pbdv(-beta - 1.0, -u[small])
+        out[small] = gamma(beta + 1.0) * np.exp(-0.25 * u[small] ** 2) * d / math.sqrt(2.0 * math.pi)
+    if np.any(~small):
+        x, w = np.polynomial.hermite_e.hermegauss(80)
+        w = w / math.sqrt(2.0 * math.pi)
+        ub = u[~small][:, None]
+        out[~small] = ub[:, 0] ** beta * np.sum(w * (1.0 + x / ub) ** beta, axis=1)
+    return out
+
+
 def gauss_expected_mass(mu: np.ndarray, sd: np.ndarray, t: float, alpha: float) -> np.ndarray:
     """E[(Y - t)_+^(1/(alpha-1))] for Y ~ N(mu, sd^2), per page.
 
     With u = (mu - t)/sd, Phi(u) = erfc(-u/sqrt 2)/2, phi(u) = exp(-u^2/2)/sqrt(2 pi):
       alpha=2   (exponent 1): (mu - t) Phi(u) + sd phi(u)
       alpha=1.5 (exponent 2): ((mu - t)^2 + sd^2) Phi(u) + (mu - t) sd phi(u)
+      any other alpha (exponent e = 1/(alpha-1)): sd^e M_e(u), the truncated
+        normal moment above
     and (mu - t)_+^exponent when sd = 0.
     """
     mu = np.asarray(mu, dtype=np.float64)
@@ -61,7 +91,11 @@ def gauss_expected_mass(mu: np.ndarray, sd: np.ndarray, t: float, alpha: float) 
     elif alpha == 1.5:
         out[z] = np.maximum(a[z], 0.0) ** 2
     else:
-        raise ValueError("Gaussian expectation implemented for alpha in {1.5, 2}")
+        beta = 1.0 / (alpha - 1.0)
+        out[z] = np.maximum(a[z], 0.0) ** beta
+        if np.any(nz):
+            out[nz] = sd[nz] ** beta * truncated_normal_moment(a[nz] / sd[nz], beta)
+        return out
     if np.any(nz):
         s = sd[nz]
         u = a[nz] / s
@@ -79,10 +113,13 @@ def gauss_tau_hat(mu: np.ndarray, sd: np.ndarray, count: np.ndarray, alpha: floa
     """Solve F(t) = sum_p n_p E_p(t) = 1 by bisection.
 
     F is continuous and strictly decreasing where positive.  Left end
-    t_lo = max_p mu_p - 1: there F >= 1, because E_p(t) >= (mu_p - t)_+^e
-    (Jensen, the integrand is convex in Y) and the top page alone gives
-    n_p * 1 >= 1.  Right end: step right from t_lo, doubling, until F <= 1.
+    t_lo = max_p mu_p - 1: there F >= 1 for alpha <= 2, because
+    E_p(t) >= (mu_p - t)_+^e (Jensen, the integrand is convex in Y for
+    e >= 1) and the top page alone gives n_p * 1 >= 1.  Right end: step
+    right from t_lo, doubling, until F <= 1.
     """
+    if not 1.0 < alpha <= 2.0:
+        raise ValueError("the Gaussian threshold estimate needs 1 < alpha <= 2")
     mu = np.asarray(mu, dtype=np.float64)
     sd = np.asarray(sd, dtype=np.float64)
     n = np.asarray(count, dtype=np.float64)
