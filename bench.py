@@ -565,6 +565,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--context", type=int, default=0, help="override the workload's context (scaling sweeps)")
+    ap.add_argument("--alpha", type=float, default=0.0, help="override the workload's entmax alpha")
     ap.add_argument("--q-heads", type=int, default=0,
                     help="override the workload's query-head count (query groups of other sizes)")
     ap.add_argument("--cpu-units", type=int, default=2, help="(sequence, KV head) units the CPU oracle is timed on")
@@ -602,6 +603,8 @@ def main():
     over = {"context": args.context} if args.context else {}
     if args.q_heads:
         over["n_q_heads"] = args.q_heads
+    if args.alpha:
+        over["alpha"] = args.alpha
     spec = W.make_spec(args.workload, **over)
     log(f"device {torch.cuda.get_device_name(0)}; workload {spec.name}")
     r = measure(spec, args.steps, args.warmup, torch, timer, not args.no_dense, not args.no_graph)

@@ -118,7 +118,9 @@ typedef struct {
  *   policy     ekv_policy
  *   top_k      pages kept per (sequence, KV head) by EKV_SELECT_BBOX_TOPK
  *              (all pages when top_k >= the sequence's page count)
- *   alpha      entmax alpha; EKV_SELECT_GAUSS supports 1.5 and 2 only
+ *   alpha      entmax alpha; EKV_SELECT_GAUSS supports alpha in [1.1, 2]
+ *              (closed-form expectations at 1.5 and 2, 32-point quadrature
+ *              otherwise)
  *   scale      score scale, normally 1/sqrt(head_dim)
  *   delta      EKV_SELECT_GAUSS safety margin, in the scaled score domain
  *              x = (alpha-1) scale q.k where the threshold lives

@@ -158,8 +158,8 @@ static ekv_status prepare_select(const ekv_cache* cache, const ekv_seqs* seqs, c
     if (seqs->max_pages > 65535) return fail(EKV_ERR_UNSUPPORTED, "top-k selection supports up to 65535 pages per sequence");
   } else if (p->policy == EKV_SELECT_GAUSS) {
     if (!cache->k_moments) return fail(EKV_ERR_INVALID_ARG, "Gaussian selection needs cache->k_moments");
-    if (p->alpha != 1.5f && p->alpha != 2.0f)
-      return fail(EKV_ERR_UNSUPPORTED, "Gaussian selection supports alpha 1.5 and 2 only");
+    if (!(p->alpha >= 1.1f && p->alpha <= 2.0f))
+      return fail(EKV_ERR_UNSUPPORTED, "Gaussian selection supports alpha in [1.1, 2]");
     if (!(p->delta >= 0.f) || !isfinite(p->delta)) return fail(EKV_ERR_INVALID_ARG, "delta must be finite and >= 0");
   } else {
     return fail(EKV_ERR_INVALID_ARG, "unknown selection policy");

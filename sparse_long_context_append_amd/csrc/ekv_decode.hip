@@ -426,7 +426,11 @@ __device__ double solve_threshold(const float* xs, int N, double m, double thr, 
   const int stride = WAVE ? kWave : blockDim.x;
   constexpr bool sparsemax = AK == 0, ent15 = AK == 1;
   const double beta = 1.0 / ((double)alpha_f - 1.0);
+  const float beta_f = (float)beta;
   double t = thr, tau = thr, t_prev = thr;
+  // other alpha: the powers are first taken in fp32 (hardware exp2/log2)
+  // while the steps are large, then in fp64 for the last steps
+  bool coarse = AK == 2;
   for (int it = 0; it < 4096; ++it) {
     tau = t;  // fallback if the iteration cap is ever reached
     double s1 = 0.0, s2 = 0.0, f = 0.0, fd = 0.0, xmin = INFINITY, cnt = 0.0;
@@ -435,7 +439,9 @@ __device__ double solve_threshold(const float* xs, int N, double m, double thr, 
       if (x > t) {
         const double y = x - m, d = x - t;
         cnt += 1.0; s1 += y; s2 += y * y; xmin = fmin(xmin, x);
-        const double pw = entmax_pow<AK>(d, beta);
+        const double pw = AK == 2 && coarse
+                              ? (double)__builtin_amdgcn_exp2f(beta_f * __builtin_amdgcn_logf((float)d))
+                              : entmax_pow<AK>(d, beta);
         f += pw;
         fd += sparsemax ? 1.0 : (ent15 ? 2.0 * d : beta * pw / d);
       }
@@ -463,11 +469,21 @@ __device__ double solve_threshold(const float* xs, int N, double m, double thr, 
       const double tn = t + (f - 1.0) / fd;
       t = fmax(tn, xmin);
     } else {
-      const double step = (f - 1.0) / fd;
-      if (!(step > 0.0)) { tau = t; break; }
+      // Newton's method on f^(1/e) - 1 (f^(1/e) is the e-norm of (x - t)_+,
+      // convex and decreasing in t, and linear for a single score): from
+      // below tau the steps stay below it and converge quadratically.  A
+      // step may cross tau only through the rounding of the fp32 phase; the
+      // next one then comes back from the right.
+      if (!(fd > 0.0)) { tau = t_prev; break; }
+      const double step = beta * (f - pow(f, 1.0 - 1.0 / beta)) / fd;
       t += step;
       tau = t;
-      if (step <= 1e-15 * fmax(1.0, fabs(t))) break;
+      const double size = fabs(step), scale_t = fmax(1.0, fabs(t));
+      if (coarse) {
+        if (size <= 1e-6 * scale_t) coarse = false;
+      } else if (size <= 1e-15 * scale_t || it > 4000) {
+        break;
+      }
     }
   }
   return tau;
@@ -833,7 +849,9 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
   // ---- threshold: one wave when the candidates are few, else the block ----
   double tau;
   double& s_tau = sm.s_tau;
-  if (N <= kTauThreads) {
+  // (other alpha: the pairwise test would take N^2 fp64 powers; Newton's
+  // method takes a few passes instead)
+  if (AK != 2 && N <= kTauThreads) {
     tau = solve_pairwise<AK>(xs, N, m, a.alpha, redd);
   } else if (N <= 8 * kWave) {
     if (tid_w == 0) {

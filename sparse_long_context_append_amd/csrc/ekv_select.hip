@@ -461,15 +461,17 @@ __global__ __launch_bounds__(kScoreThreads) void score_gauss_kernel(SelectArgs a
 // and E = (a)_+^e when sd = 0.  F is continuous and strictly decreasing
 // where positive, so the root is unique.
 //
-// Start: E_p(t) >= (mu_p - t)_+^e (Jensen), so every page alone bounds the
-// root from below by mu_p - n_p^{-(alpha-1)}; the largest of these is t0.
-// t only matters above t0, where a page with u < -7 contributes below
-// 2e-13 n_p sd^e: such pages are dropped once, at t0.  The iteration is
-// Newton's method on log F (exact in one step for an exponential tail, and
-// quadratic near the root), kept inside a bracket [lo, hi] with F(lo) >= 1 >
-// F(hi) and replaced by bisection whenever it would leave it.  Per-page terms
-// are evaluated in fp32 and summed in fp64; the step stops below
-// 2e-7 max(1, |t|).
+// Other alpha in [1.1, 2] use the quadrature of gauss_mass_general below.
+//
+// Start: E_p(t) >= (mu_p - t)_+^e (Jensen, e >= 1), so every page alone
+// bounds the root from below by mu_p - n_p^{-(alpha-1)}; the largest of
+// these is t0.  t only matters above t0, where a page with u < -7
+// contributes below 2e-13 n_p sd^e: such pages are dropped once, at t0.
+// The iteration is Halley's method on log F (alpha 1.5 and 2, where F'' is
+// at hand) or Newton's (other alpha), kept inside a bracket [lo, hi] with
+// F(lo) >= 1 > F(hi) and replaced by bisection whenever it would leave it.
+// Per-page terms are evaluated in fp32 and summed in fp64; the step stops
+// below 2e-7 max(1, |t|).
 //
 // The last block of a (sequence, KV head) to finish (arrival counter) keeps
 // the pages whose estimated maximum beats tau_hat - delta for some head of
@@ -507,13 +509,131 @@ __device__ __forceinline__ void gauss_mass(float mu, float sd, float tf, bool qu
   }
 }
 
-// live-list entries carry the partial last page as sd -> -sd - 1
-__device__ __forceinline__ void live_term(float2 v, float P, float last_n, float tf, bool quad, double& F,
-                                          double& dF, double& ddF) {
+// Other alpha in [1.1, 2] (e = 1/(alpha-1) in [1, 10]): with z = (Y - t)/sd,
+// E = sd^e M_e(u) and E' = -e sd^(e-1) M_(e-1)(u), where M_b(u) is the
+// integral over z > 0 of z^b phi(z - u).  The log integrand f(z) = e ln z -
+// (z - u)^2 / 2 peaks at zs = (u + sqrt(u^2 + 4e)) / 2.  Two 16-point
+// Gauss-Legendre rules cover it, the right one up to where f has dropped by
+// 30 (three Newton steps on the concave f), the left one down to zs - sqrt(60)
+// widths, or from 0 with z = s^2 when that end would pass 0 (the integrand
+// then behaves like s^(2e+1), smooth enough for the rule).  Node weights
+// are taken relative to the peak, exp(f(z) - f(zs)), from differences that
+// keep their precision in fp32; the peak factor is applied in fp64.  The
+// relative error is about 1e-7 over u in [-7, 40].  Beyond u = 40 the
+// truncation is negligible and E = a^e (1 + C(e,2)/u^2 + 3 C(e,4)/u^4 +
+// 15 C(e,6)/u^6), the moments of N(u, 1) to order u^-6.
+__constant__ float kGL16[8][2] = {
+    {0.095012510f, 0.189450610f}, {0.281603551f, 0.182603415f}, {0.458016778f, 0.169156519f},
+    {0.617876244f, 0.149595989f}, {0.755404408f, 0.124628971f}, {0.865631202f, 0.095158512f},
+    {0.944575023f, 0.062253524f}, {0.989400935f, 0.027152459f}};
+
+__device__ __forceinline__ float normal_power_series(float b, float u) {
+  const float v = 1.f / (u * u);
+  const float t2 = 0.5f * b * (b - 1.f);               // C(b,2)
+  const float t4 = 0.25f * t2 * (b - 2.f) * (b - 3.f);  // 3 C(b,4)
+  const float t6 = t4 * (b - 4.f) * (b - 5.f) / 6.f;    // 15 C(b,6)
+  return 1.f + v * (t2 + v * (t4 + v * t6));
+}
+
+__device__ void gauss_mass_general(float mu, float sd, float tf, float beta, float& e, float& de) {
+  const float am = mu - tf;
+  if (sd <= 0.f) {
+    if (am <= 0.f) { e = de = 0.f; return; }
+    e = exp2f(beta * log2f(am));
+    de = -beta * e / am;
+    return;
+  }
+  const float u = am / sd;
+  if (u < -7.f) {
+    e = de = 0.f;
+    return;
+  }
+  if (u > 40.f) {
+    const float la = log2f(am);
+    e = exp2f(beta * la) * normal_power_series(beta, u);
+    de = -beta * exp2f((beta - 1.f) * la) * normal_power_series(beta - 1.f, u);
+    return;
+  }
+  const float zs = 0.5f * (u + sqrtf(u * u + 4.f * beta));
+  const float rzs = 1.f / zs;
+  const float kLog2e = 1.44269504089f, kDrop = 30.f, kSpan = 7.745966692f;  // sqrt(2 kDrop)
+  // (f(z) - f(zs)) / ln 2 from differences; the node weights use the
+  // hardware exp2 / log2 / reciprocal (about 1 ulp), which the 1e-7 budget
+  // of the rule absorbs
+  const float hb = 0.5f * kLog2e;
+  auto rel2 = [&](float z) {
+    return beta * __builtin_amdgcn_logf(z * rzs) - hb * (z - zs) * (z + zs - 2.f * u);
+  };
+  float zr = zs + kSpan;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) zr -= (rel2(zr) * 0.69314718056f + kDrop) / (beta / zr - (zr - u));
+  const float zl = zs - kSpan * rsqrtf(beta * rzs * rzs + 1.f);
+  float m = 0.f, m1 = 0.f;  // relative to the peak: M_e and M_(e-1)
+  {
+    const float h = 0.5f * (zr - zs), c = zs + h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int sg = -1; sg <= 1; sg += 2) {
+        const float z = c + (float)sg * h * kGL16[i][0];
+        const float v = kGL16[i][1] * __builtin_amdgcn_exp2f(rel2(z));
+        m += v;
+        m1 += v * __builtin_amdgcn_rcpf(z);
+      }
+    }
+    m *= h;
+    m1 *= h;
+  }
+  if (zl > 0.f) {
+    const float h = 0.5f * (zs - zl), c = zl + h;
+    float ml = 0.f, ml1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int sg = -1; sg <= 1; sg += 2) {
+        const float z = c + (float)sg * h * kGL16[i][0];
+        const float v = kGL16[i][1] * __builtin_amdgcn_exp2f(rel2(z));
+        ml += v;
+        ml1 += v * __builtin_amdgcn_rcpf(z);
+      }
+    }
+    m += h * ml;
+    m1 += h * ml1;
+  } else {  // z = s^2 over s in [0, sqrt(zs)]: dz = 2 s ds
+    const float h = 0.5f * sqrtf(zs);
+    float ml = 0.f, ml1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int sg = -1; sg <= 1; sg += 2) {
+        const float sv = h + (float)sg * h * kGL16[i][0];
+        const float z = sv * sv;
+        const float v = kGL16[i][1] * 2.f * sv * __builtin_amdgcn_exp2f(rel2(z));
+        ml += v;
+        ml1 += v * __builtin_amdgcn_rcpf(z);
+      }
+    }
+    m += h * ml;
+    m1 += h * ml1;
+  }
+  // peak factor exp(f(zs)) sd^e / sqrt(2 pi)
+  const double zd = zs, ud = u;
+  const double sc = exp((double)beta * log(zd * (double)sd) - 0.5 * (zd - ud) * (zd - ud)) * 0.3989422804014327;
+  e = (float)(sc * (double)m);
+  de = (float)(-(double)beta * sc / (double)sd * (double)m1);
+}
+
+// live-list entries carry the partial last page as sd -> -sd - 1.
+// mode: 0 alpha = 2, 1 alpha = 1.5, 2 other alpha (beta = 1/(alpha-1);
+// no second derivative, ddF is left unchanged).
+template <bool GEN>
+__device__ __forceinline__ void live_term(float2 v, float P, float last_n, float tf, int mode, float beta,
+                                          double& F, double& dF, double& ddF) {
   float n = P, sd = v.y;
   if (sd < 0.f) { sd = -sd - 1.f; n = last_n; }
-  float e, de, dde;
-  gauss_mass(v.x, sd, tf, quad, e, de, dde);
+  float e, de, dde = 0.f;
+  if (GEN) gauss_mass_general(v.x, sd, tf, beta, e, de);
+  else gauss_mass(v.x, sd, tf, mode == 1, e, de, dde);
   F += (double)n * (double)e;
   dF += (double)n * (double)de;
   ddF += (double)n * (double)dde;
@@ -556,7 +676,9 @@ __device__ void gauss_floor_unit(const SelectArgs& a, int b, int g, int n_b, int
   }
 }
 
-template <int G>
+// GEN: alpha other than 1.5 and 2 (a separate instance, so that the
+// quadrature's registers do not weigh on the closed-form one)
+template <int G, bool GEN>
 __global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
   constexpr int PPT = kTauHatPPT;
   constexpr int NW = kTauHatThreads / kWave;
@@ -577,11 +699,16 @@ __global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
   __shared__ int s_last;
   double t = 0.0;
   const bool in_regs = n_b <= PPT * kTauHatThreads;
+  // the general-alpha instance re-reads the estimated maxima for the keep
+  // test instead of holding them through the iteration: its quadrature
+  // needs the registers
+  const bool er_regs = !GEN && in_regs;
   float er[PPT];  // this thread's estimated maxima (pages tid + 1024 i)
 #pragma unroll
   for (int i = 0; i < PPT; ++i) er[i] = -INFINITY;
   if (n_b > 0) {
-    const bool quad = a.alpha == 1.5f;
+    const int mode = GEN ? 2 : (a.alpha == 1.5f ? 1 : 0);
+    const float beta = 1.f / (a.alpha - 1.f);
     const float Pf = (float)P;
     const float last_n = (float)(L - (n_b - 1) * P);  // tokens of the last page
     // thread t owns pages t, t + 1024, ...: one round of coalesced loads
@@ -589,14 +716,15 @@ __global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
     double lb = -INFINITY;
     auto bound = [&](float2 v, int p) {
       const double n = p == n_b - 1 ? (double)last_n : (double)P;
-      return (double)v.x - (quad ? 1.0 / sqrt(n) : 1.0 / n);
+      const double r = mode == 0 ? 1.0 / n : (mode == 1 ? 1.0 / sqrt(n) : pow(n, -(double)(a.alpha - 1.f)));
+      return (double)v.x - r;
     };
     if (in_regs) {
 #pragma unroll
       for (int i = 0; i < PPT; ++i) {
         const int p = i * kTauHatThreads + tid;
         ms[i] = p < n_b ? st[p] : make_float2(-INFINITY, 0.f);
-        er[i] = p < n_b ? eh[p] : -INFINITY;
+        if (!GEN) er[i] = p < n_b ? eh[p] : -INFINITY;
         if (p < n_b) lb = fmax(lb, bound(ms[i], p));
       }
     } else {
@@ -633,12 +761,13 @@ __global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
       const float tf = (float)t;
       double F = 0.0, dF = 0.0, ddF = 0.0;
       if (use_live) {
-        for (int i = tid; i < n_live; i += kTauHatThreads) live_term(live[i], Pf, last_n, tf, quad, F, dF, ddF);
+        for (int i = tid; i < n_live; i += kTauHatThreads)
+          live_term<GEN>(live[i], Pf, last_n, tf, mode, beta, F, dF, ddF);
       } else {
         for (int p = tid; p < n_b; p += kTauHatThreads) {
           float2 v = st[p];
           if (p == n_b - 1 && last_n != Pf) v.y = -v.y - 1.f;
-          live_term(v, Pf, last_n, tf, quad, F, dF, ddF);
+          live_term<GEN>(v, Pf, last_n, tf, mode, beta, F, dF, ddF);
         }
       }
       // wave partials -> wave 0 computes the step -> every wave reads it
@@ -680,7 +809,7 @@ __global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
             const double iF = 1.0 / F;
             const double g1 = dF * iF, g2 = ddF * iF - g1 * g1;
             const double cn = t - gl / g1;
-            const float r = (float)(gl * g2 / (g1 * g1));
+            const float r = mode == 2 ? 0.f : (float)(gl * g2 / (g1 * g1));  // 0: Newton
             const float den = 1.f - 0.5f * r;
             const double ch = den > 0.f ? t + (cn - t) * (double)(1.f / den) : cn;  // Halley = Newton / (1 - r/2)
             if (den > 0.f && ch > lo && ch < hi) { cand = ch; ok = true; }
@@ -711,7 +840,7 @@ __global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
   // this head's keep decisions as a bitmap (bit p: e_hat_p - tau_hat > -delta)
   const double ndelta = -(double)a.delta;
   const int nwords = (n_b + 63) / 64;
-  if (in_regs) {
+  if (er_regs) {
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int p0 = i * kTauHatThreads + w * kWave;  // this wave's 64 pages
@@ -833,16 +962,21 @@ hipError_t launch_score_gauss(const SelectArgs& a, hipStream_t s) {
   return a.head_dim == 128 ? gauss_dispatch_g<128>(a, grid, s) : gauss_dispatch_g<64>(a, grid, s);
 }
 
-hipError_t launch_tau_hat(const SelectArgs& a, hipStream_t s) {
+template <bool GEN>
+static hipError_t tau_hat_dispatch(const SelectArgs& a, hipStream_t s) {
   const dim3 grid(a.n_q_heads, a.batch), block(kTauHatThreads);
   switch (a.group) {
-    case 1: hipLaunchKernelGGL(tau_hat_kernel<1>, grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL(tau_hat_kernel<2>, grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL(tau_hat_kernel<4>, grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL(tau_hat_kernel<8>, grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((tau_hat_kernel<1, GEN>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((tau_hat_kernel<2, GEN>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((tau_hat_kernel<4, GEN>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((tau_hat_kernel<8, GEN>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_tau_hat(const SelectArgs& a, hipStream_t s) {
+  return (a.alpha == 1.5f || a.alpha == 2.0f) ? tau_hat_dispatch<false>(a, s) : tau_hat_dispatch<true>(a, s);
 }
 
 }  // namespace ekv

@@ -76,7 +76,8 @@ def test_select_validation(L):
     assert call_select(L, p=sp(policy=7)) == B.EKV_ERR_INVALID_ARG
     assert call_select(L, p=sp(alpha=1.0)) == B.EKV_ERR_INVALID_ARG
     assert call_select(L, p=sp(scale=0.0)) == B.EKV_ERR_INVALID_ARG
-    assert call_select(L, p=sp(policy=B.EKV_SELECT_GAUSS, alpha=1.25)) == B.EKV_ERR_UNSUPPORTED
+    assert call_select(L, p=sp(policy=B.EKV_SELECT_GAUSS, alpha=1.05)) == B.EKV_ERR_UNSUPPORTED
+    assert call_select(L, p=sp(policy=B.EKV_SELECT_GAUSS, alpha=2.5)) == B.EKV_ERR_UNSUPPORTED
     assert call_select(L, c=cache(k_box=None)) == B.EKV_ERR_INVALID_ARG
     assert call_select(L, c=cache(k_moments=None), p=sp(policy=B.EKV_SELECT_GAUSS)) == B.EKV_ERR_INVALID_ARG
     assert call_select(L, cap=4) == B.EKV_ERR_CAPACITY

@@ -139,6 +139,18 @@ def test_gauss_more_pages_than_register_tiles():
     check_step(spec, run_step(sess, spec, q), q, all_units(spec))
 
 
+@pytest.mark.parametrize("alpha,hkv,ctx", [(1.25, 2, 4096 + 17), (1.8, 2, 8192 + 3), (1.3, 1, 2048 + 40),
+                                           (1.1, 2, 3000)])
+def test_gauss_general_alpha(alpha, hkv, ctx):
+    """Gaussian selection for alpha outside {1.5, 2}: the threshold estimate
+    takes its expectations from quadrature and steps by Newton's method."""
+    spec = W.make_spec("c3", batch=2, context=ctx, n_q_heads=8, n_kv_heads=hkv, alpha=alpha)
+    sess, _ = _session(spec)
+    q = W.queries(spec)
+    check_step(spec, run_step(sess, spec, q), q, all_units(spec))
+    assert sess.device_status() == 0
+
+
 @pytest.mark.parametrize("alpha,hkv", [(1.3, 2), (1.8, 2), (1.3, 1)])
 def test_general_alpha_decode(alpha, hkv):
     """alpha outside {1.5, 2}: the threshold comes from Newton's method on the
