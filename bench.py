@@ -517,6 +517,47 @@ def run_gqa(args, torch, timer):
                       "gqa": out}), flush=True)
 
 
+def run_prefill(args, torch, timer):
+    """Bulk prefill: one append_kv call writes a whole sequence (K and V
+    rows) and builds its page metadata (box and moments) from scratch.
+    Bytes per call: new K and V read, K and V written, box and moment
+    records written."""
+    import sparse_long_context_append_amd as ekv
+    from sparse_long_context_append_amd.runtime import DecodeSession
+    rows = []
+    for name in ("c4", "c3"):
+        spec = W.make_spec(name)
+        B, Hkv, d, P = 1, spec.n_kv_heads, spec.head_dim, spec.page_size
+        n = spec.context
+        n_pages = -(-n // P)
+        table = np.arange(n_pages, dtype=np.int32)[None, :]
+        sess = DecodeSession(batch=B, n_kv_heads=Hkv, n_q_heads=spec.n_q_heads, head_dim=d, page_size=P,
+                             kv_dtype=ekv.EKV_BF16, n_phys_pages=n_pages, page_table=table, cap=1)
+        g = torch.Generator(device="cuda").manual_seed(7)
+        k_new = torch.randn((B, n, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+        v_new = torch.randn((B, n, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+
+        def call():
+            sess.seq_lens.zero_()
+            ekv.append_kv(sess.cache, sess.seqs, k_new, v_new, n, sess.ws)
+
+        ms, _ = timer.run(call, args.steps, args.warmup)
+        med = statistics.median(ms)
+        kv_bytes = 2 * B * n * Hkv * d * 2
+        meta_bytes = B * n_pages * Hkv * (2 * d * 2 + 2 * d * 4)
+        total = 2 * kv_bytes + meta_bytes
+        rows.append({"workload": f"{name} prefill: {n} tokens, {Hkv} KV heads, d={d}, page={P}, bf16",
+                     "us_per_call": round(med * 1e3, 2), "bytes": total,
+                     "gbs": round(total / (med * 1e-3) / 1e9, 1),
+                     "hbm_fraction": round(total / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "tokens_per_s": round(B * n / (med * 1e-3), 1)})
+        log(f"prefill {name}: {rows[-1]['us_per_call']} us, {rows[-1]['gbs']} GB/s")
+        del sess, k_new, v_new
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "bulk prefill: K/V write and page metadata build", "n_gpus": 1,
+                      "data": "synthetic", "steps": args.steps, "warmup": args.warmup, "prefill": rows}), flush=True)
+
+
 def copy_probe(mib):
     """A plain copy kernel of known size: HBM read and write counters of its
     dispatches calibrate the counters of the path's kernels."""
@@ -578,6 +619,9 @@ def main():
     ap.add_argument("--gqa", action="store_true",
                     help="instead of the headline line: shared vs per-query-head selection (dropped mass, "
                          "support retention, output error, pages read, step time) on c2, c3, c4")
+    ap.add_argument("--prefill", action="store_true",
+                    help="instead of the headline line: bulk prefill throughput of append_kv (one call per "
+                         "sequence: K/V rows and page metadata) at the c4 and c3 shapes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (counter calibration)")
     args = ap.parse_args()
@@ -599,6 +643,9 @@ def main():
         return
     if args.gqa:
         run_gqa(args, torch, timer)
+        return
+    if args.prefill:
+        run_prefill(args, torch, timer)
         return
     over = {"context": args.context} if args.context else {}
     if args.q_heads:

@@ -160,7 +160,8 @@ ekv_status ekv_workspace_init(void* workspace, size_t ws_bytes, void* stream);
  * the token starts the page and updated otherwise (k_min/k_max by min/max,
  * moments by Welford's update in token order), so appending tokens one call
  * at a time and appending them in one call give bit-identical metadata.
- *   k_new, v_new  [batch][n_new][n_kv_heads][head_dim], kv_dtype
+ *   k_new, v_new  [batch][n_new][n_kv_heads][head_dim], kv_dtype, 16-byte
+ *                 aligned
  * seq_lens holds the lengths BEFORE the append and is not modified; the
  * caller advances it.  Needs seq_lens[b] + n_new <= max_pages * page_size
  * and page-table entries for every touched page.

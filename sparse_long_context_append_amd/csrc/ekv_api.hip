@@ -124,6 +124,8 @@ ekv_status ekv_append_kv(const ekv_cache* cache, const ekv_seqs* seqs, const voi
   if ((st = check_seqs(cache, seqs)) != EKV_OK) return st;
   if (n_new < 0) return fail(EKV_ERR_INVALID_ARG, "n_new must be >= 0");
   if (n_new > 0 && (!k_new || !v_new)) return fail(EKV_ERR_INVALID_ARG, "k_new/v_new is NULL");
+  if (n_new > 0 && (!aligned16(k_new) || !aligned16(v_new)))
+    return fail(EKV_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned");
   if ((long long)n_new > (long long)seqs->max_pages * cache->page_size)
     return fail(EKV_ERR_INVALID_ARG, "n_new exceeds max_pages * page_size");
   // append only touches the status word at the start of the workspace

@@ -132,6 +132,7 @@ def test_append_validation(L):
     f = L.ekv_append_kv
     assert f(ctypes.byref(cache()), ctypes.byref(seqs()), FAKE, FAKE, -1, FAKE, 1 << 20, None) == B.EKV_ERR_INVALID_ARG
     assert f(ctypes.byref(cache()), ctypes.byref(seqs()), None, FAKE, 4, FAKE, 1 << 20, None) == B.EKV_ERR_INVALID_ARG
+    assert f(ctypes.byref(cache()), ctypes.byref(seqs()), FAKE + 8, FAKE, 4, FAKE, 1 << 20, None) == B.EKV_ERR_INVALID_ARG
     assert f(ctypes.byref(cache()), ctypes.byref(seqs()), FAKE, FAKE, 4, None, 1 << 20, None) == B.EKV_ERR_WORKSPACE
     assert f(ctypes.byref(cache()), ctypes.byref(seqs()), FAKE, FAKE, 10 ** 6, FAKE, 1 << 20, None) == B.EKV_ERR_INVALID_ARG
     # n_new == 0 is a valid no-op that launches nothing
