@@ -764,40 +764,15 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
     }
   }
   if (!done) {
-    // general case: chunks of up to 1024 items.  Per chunk the non-empty
-    // items are listed with their first candidate's rank (one scan); the raw
-    // candidates are then read RPT per thread per round (one round of loads,
-    // one scan), and the kept ones appended to the workspace list, which is
-    // copied on chip afterwards when it fits.
+    // general case.  The raw candidates of the listed items (s_item, with
+    // their first candidate's rank in s_pre) are read RPT per thread per
+    // round (one round of loads, one scan), and the kept ones appended to
+    // the workspace list, which is copied on chip afterwards when it fits.
     float* ox = a.ovf_x + bh * tok_per_bh;
     int32_t* ot = a.ovf_t + bh * tok_per_bh;
     int32_t* orow = a.ovf_r + bh * tok_per_bh;
     int run = 0;
-    for (int c0 = 0; c0 < n_items; c0 += kTauItemChunk) {
-      const int nc = min(kTauItemChunk, n_items - c0);
-      int lc[4], sum = 0, nz = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int jj = 4 * tid + i;
-        lc[i] = jj < nc && (double)imax[c0 + jj] > thr ? icnt[c0 + jj] : 0;
-        sum += lc[i];
-        nz += lc[i] > 0;
-      }
-      int packed_tot;
-      const int packed = block_exclusive_scan((nz << 17) | sum, redi, &packed_tot);
-      const int raw_tot = packed_tot & 0x1ffff, n_ne = packed_tot >> 17;
-      int base = packed & 0x1ffff, rank = packed >> 17;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (lc[i] > 0) {
-          s_pre[rank] = base;
-          sm.s_item[rank] = c0 + 4 * tid + i;
-          ++rank;
-        }
-        base += lc[i];
-      }
-      if (tid == 0) s_pre[n_ne] = raw_tot;
-      __syncthreads();
+    auto read_rounds = [&](int n_ne, int raw_tot) {
       for (int r0 = 0; r0 < raw_tot; r0 += RPT * kTauThreads) {
         float xv[RPT];
         size_t av[RPT];
@@ -832,6 +807,84 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
           if ((double)xv[c] > thr) { ox[pos] = xv[c]; ot[pos] = ct[av[c]]; orow[pos] = cr[av[c]]; ++pos; }
         run += tot;
       }
+    };
+    // Usually few items reach above thr (it lies close to the top score):
+    // list them all at once, in item order.  Thread t takes the contiguous
+    // items [t E, t E + E), E <= 64, and marks the ones above thr in a bit
+    // mask; one scan places them.
+    bool listed = false;
+    if (n_items <= 64 * kTauThreads) {
+      const int E = (n_items + kTauThreads - 1) / kTauThreads;
+      const int e0 = min(tid * E, n_items), e1 = min(e0 + E, n_items);
+      uint64_t smask = 0;
+      int scount = 0;
+      for (int i0 = e0; i0 < e1; i0 += 8) {
+        float vm[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) vm[q] = i0 + q < e1 ? imax[i0 + q] : -INFINITY;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if ((double)vm[q] > thr) { smask |= 1ull << (i0 + q - e0); ++scount; }
+      }
+      int n_sv;
+      int spos = block_exclusive_scan(scount, redi, &n_sv);
+      if (n_sv <= kTauItemChunk) {
+        listed = true;
+        while (smask) {
+          const int k = __ffsll((unsigned long long)smask) - 1;
+          smask &= smask - 1;
+          sm.s_item[spos++] = e0 + k;
+        }
+        __syncthreads();
+        // their raw counts and first ranks: thread t takes listed items 4t .. 4t+3
+        int lc[4], sum = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int k = 4 * tid + q;
+          lc[q] = k < n_sv ? icnt[sm.s_item[k]] : 0;
+          sum += lc[q];
+        }
+        int raw_tot;
+        int base = block_exclusive_scan(sum, redi, &raw_tot);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int k = 4 * tid + q;
+          if (k < n_sv) s_pre[k] = base;
+          base += lc[q];
+        }
+        if (tid == 0) s_pre[n_sv] = raw_tot;
+        __syncthreads();
+        read_rounds(n_sv, raw_tot);
+      }
+    }
+    // otherwise chunks of up to 1024 items, each listing its non-empty items
+    // above thr (one scan)
+    for (int c0 = 0; !listed && c0 < n_items; c0 += kTauItemChunk) {
+      const int nc = min(kTauItemChunk, n_items - c0);
+      int lc[4], sum = 0, nz = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int jj = 4 * tid + i;
+        lc[i] = jj < nc && (double)imax[c0 + jj] > thr ? icnt[c0 + jj] : 0;
+        sum += lc[i];
+        nz += lc[i] > 0;
+      }
+      int packed_tot;
+      const int packed = block_exclusive_scan((nz << 17) | sum, redi, &packed_tot);
+      const int raw_tot = packed_tot & 0x1ffff, n_ne = packed_tot >> 17;
+      int base = packed & 0x1ffff, rank = packed >> 17;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (lc[i] > 0) {
+          s_pre[rank] = base;
+          sm.s_item[rank] = c0 + 4 * tid + i;
+          ++rank;
+        }
+        base += lc[i];
+      }
+      if (tid == 0) s_pre[n_ne] = raw_tot;
+      __syncthreads();
+      read_rounds(n_ne, raw_tot);
       __syncthreads();  // s_pre / s_item are rewritten by the next chunk
     }
     N = run;

@@ -244,7 +244,7 @@ __device__ void topk_block(const SelectArgs& a, const float* s, int n_b, int k_e
   __shared__ uint32_t hist[2][256];
   __shared__ uint32_t red[2][16];
   __shared__ int redi[17];
-  __shared__ uint32_t sh_digit[2], sh_above[2];
+  __shared__ uint32_t sh_digit[2], sh_above[2], sh_bucket[2];
   const int per = E > 0 ? E : (n_b + blockDim.x - 1) / blockDim.x;
   const int e0 = min(tid * per, n_b), e1 = min(e0 + per, n_b);
   const int cnt = e1 - e0;
@@ -280,6 +280,7 @@ __device__ void topk_block(const SelectArgs& a, const float* s, int n_b, int k_e
   int rem = k_eff;
   if (diff == 0u) {
     prefix = kand;  // every score equal: the k lowest page ids
+    mask = 0xffffffffu;
   } else {
     const int top = 31 - __clz(diff);
     const int start = (top / 8) * 8;
@@ -305,30 +306,39 @@ __device__ void topk_block(const SelectArgs& a, const float* s, int n_b, int k_e
           uint32_t above = Snext;
           const uint32_t cs[4] = {c0, c1, c2, c3};
           int digit = 4 * lane;
+          uint32_t bucket = 0u;
+#pragma unroll
           for (int bin = 3; bin >= 0; --bin) {
-            if (above + cs[bin] >= (uint32_t)rem) { digit = 4 * lane + bin; break; }
+            if (above + cs[bin] >= (uint32_t)rem) { digit = 4 * lane + bin; bucket = cs[bin]; break; }
             above += cs[bin];
           }
           sh_digit[buf] = (uint32_t)digit;
           sh_above[buf] = above;
+          sh_bucket[buf] = bucket;
         }
       }
       __syncthreads();
       prefix |= sh_digit[buf] << shift;
       mask |= 0xffu << shift;
       rem -= (int)sh_above[buf];
+      // the chosen bucket holds exactly the keys still wanted: all of it is
+      // taken, and its lower digits need not be resolved
+      if (sh_bucket[buf] == (uint32_t)rem) break;
     }
   }
-  const uint32_t kstar = prefix;  // key of the k-th largest; take `rem` of the ties
+  // keys compared on the resolved digits: above kstar are taken, and `rem`
+  // of those equal to it, lowest page id first
+  const uint32_t kstar = prefix;
   // one scan of (greater, equal) counts packed in 16 bits each (n <= 65535)
   int c_gt = 0, c_eq = 0;
-  EKV_FOR_KEYS(c_gt += (k > kstar); c_eq += (k == kstar);)
+  EKV_FOR_KEYS(const uint32_t km = k & mask; c_gt += (km > kstar); c_eq += (km == kstar);)
   int tot;
   const int packed = block_exclusive_scan(c_gt | (c_eq << 16), redi, &tot);
   const int gt_before = packed & 0xffff, eq_before = packed >> 16;
   int pos = gt_before + min(eq_before, rem);
   int r = eq_before;
-  EKV_FOR_KEYS(bool take = k > kstar; if (k == kstar) { take = r < rem; ++r; } if (take) out[pos++] = e0 + i;)
+  EKV_FOR_KEYS(const uint32_t km = k & mask; bool take = km > kstar;
+               if (km == kstar) { take = r < rem; ++r; } if (take) out[pos++] = e0 + i;)
   if (tid == 0) a.sel_count[unit] = k_eff;
 }
 #undef EKV_FOR_KEYS

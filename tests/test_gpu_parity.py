@@ -215,12 +215,14 @@ def test_topk_covering_every_page_equals_dense():
 
 
 @pytest.mark.parametrize("kv", ["f32", "bf16"])
-@pytest.mark.parametrize("L", [1500, 5000])
+@pytest.mark.parametrize("L", [1500, 5000, 70000])
 @pytest.mark.parametrize("alpha", [1.5, 2.0])
 def test_all_keys_equal_large_support(alpha, L, kv):
     """Every key identical: every page ties (lowest ids win) and every token
     is in the support.  1500 tokens overflow the on-chip candidate list from
-    the register path, 5000 from the chunked path; bf16 runs the matrix-core
+    the register path, 5000 from the listed-items path; at 70000 (1094 items
+    of 64 tokens, all at the maximum) the full-cache decode lists more items
+    than fit on chip and takes the chunked path.  bf16 runs the matrix-core
     gather, fp32 the vector one."""
     from sparse_long_context_append_amd.runtime import DecodeSession
     import sparse_long_context_append_amd as ekv
