@@ -57,8 +57,8 @@ __device__ __forceinline__ TokenRef token_ref(const DecodeArgs& a, int u, int b,
   const int P = a.page_size;
   const long long T = (long long)j * kItemTokens + r;
   if (T >= (long long)npu * P) return t;
-  const int k = (int)(T / P);
-  t.slot = (int)(T - (long long)k * P);
+  const int k = (int)(T >> __builtin_ctz(P));  // P is a power of two
+  t.slot = (int)(T & (P - 1));
   const int lp = a.sel ? a.sel[(size_t)u * a.cap + k] : k;
   if (lp < 0 || lp >= n_b) {
     set_status(a.status, EKV_DEV_BAD_PAGE);
@@ -81,50 +81,82 @@ struct UnitCtx {
 };
 
 // References of token r in items j0 .. j0+SUB-1 of unit u, resolved in two
-// dependent rounds whose loads all travel together: round one reads the
-// page-list entries (and, when `first`, the sequence length and selection
-// count), round two the page-table entries.  Entries are range-checked
-// against the table before the length is known and against the length
-// afterwards.
+// dependent rounds whose loads all travel together: round one (refs_list)
+// reads the page-list entries (and, when `first`, the sequence length and
+// selection count), round two (refs_table) the page-table entries.  Entries
+// are range-checked against the table before the length is known and
+// against the length afterwards (refs_finish).  Split in three so that a
+// kernel can keep the next super-item's rounds in flight behind its current
+// work.
+template <int SUB> struct RefPipe {
+  int lp[SUB], ph[SUB];
+  int j0, r, L, cnt, b;
+  bool first;
+};
+
 template <int SUB>
-__device__ __forceinline__ void resolve_refs(const DecodeArgs& a, int u, int b, int j0, int r, bool first,
-                                             UnitCtx* ctx, TokenRef* tr) {
+__device__ __forceinline__ void refs_list(const DecodeArgs& a, int u, int b, int j0, int r, bool first,
+                                          RefPipe<SUB>& rp) {
   const int P = a.page_size;
   const int capk = a.sel ? min(a.cap, a.max_pages) : a.max_pages;
-  long long T[SUB];
-  int lp[SUB], ph[SUB];
+  rp.b = b;
+  rp.j0 = j0;
+  rp.r = r;
+  rp.first = first;
 #pragma unroll
   for (int s = 0; s < SUB; ++s) {
-    T[s] = (long long)(j0 + s) * kItemTokens + r;
-    const int k = (int)(T[s] / P);
-    lp[s] = k < capk ? (a.sel ? a.sel[(size_t)u * a.cap + k] : k) : -1;
+    const long long T = (long long)(j0 + s) * kItemTokens + r;
+    const int k = (int)(T >> __builtin_ctz(P));  // P is a power of two
+    rp.lp[s] = k < capk ? (a.sel ? a.sel[(size_t)u * a.cap + k] : k) : -1;
   }
   if (first) {
-    int L = a.seq_lens[b];
-    const int cnt = a.sel ? a.sel_count[u] : 0;
+    rp.L = a.seq_lens[b];
+    rp.cnt = a.sel ? a.sel_count[u] : 0;
+  }
+}
+
+template <int SUB>
+__device__ __forceinline__ void refs_table(const DecodeArgs& a, RefPipe<SUB>& rp) {
+#pragma unroll
+  for (int s = 0; s < SUB; ++s)
+    rp.ph[s] = (rp.lp[s] >= 0 && rp.lp[s] < a.max_pages) ? a.page_table[(size_t)rp.b * a.max_pages + rp.lp[s]] : -1;
+}
+
+template <int SUB>
+__device__ __forceinline__ void refs_finish(const DecodeArgs& a, const RefPipe<SUB>& rp, UnitCtx* ctx, TokenRef* tr) {
+  const int P = a.page_size;
+  if (rp.first) {
+    int L = rp.L;
     if (L < 0 || (long long)L > (long long)a.max_pages * P) L = L < 0 ? 0 : a.max_pages * P;
     ctx->L = L;
     ctx->n_b = pages_of(L, P);
-    ctx->npu = a.sel ? min(max(cnt, 0), min(a.cap, ctx->n_b)) : ctx->n_b;
+    ctx->npu = a.sel ? min(max(rp.cnt, 0), min(a.cap, ctx->n_b)) : ctx->n_b;
     ctx->n_items = (int)(((long long)ctx->npu * P + kItemTokens - 1) / kItemTokens);
   }
 #pragma unroll
-  for (int s = 0; s < SUB; ++s)
-    ph[s] = (lp[s] >= 0 && lp[s] < a.max_pages) ? a.page_table[(size_t)b * a.max_pages + lp[s]] : -1;
-#pragma unroll
   for (int s = 0; s < SUB; ++s) {
-    const int k = (int)(T[s] / P);
-    const int slot = (int)(T[s] - (long long)k * P);
+    const long long T = (long long)(rp.j0 + s) * kItemTokens + rp.r;
+    const int k = (int)(T >> __builtin_ctz(P));  // P is a power of two
+    const int slot = (int)(T & (P - 1));
     tr[s] = TokenRef{-1, slot, 0, false};
-    if (T[s] >= (long long)ctx->npu * P) continue;
-    if (lp[s] < 0 || lp[s] >= ctx->n_b || ph[s] < 0 || ph[s] >= a.n_phys) {
+    if (T >= (long long)ctx->npu * P) continue;
+    if (rp.lp[s] < 0 || rp.lp[s] >= ctx->n_b || rp.ph[s] < 0 || rp.ph[s] >= a.n_phys) {
       set_status(a.status, EKV_DEV_BAD_PAGE);
       continue;
     }
-    tr[s].phys = ph[s];
-    tr[s].logical = lp[s] * P + slot;
-    tr[s].valid = slot < ctx->L - lp[s] * P;
+    tr[s].phys = rp.ph[s];
+    tr[s].logical = rp.lp[s] * P + slot;
+    tr[s].valid = slot < ctx->L - rp.lp[s] * P;
   }
+}
+
+template <int SUB>
+__device__ __forceinline__ void resolve_refs(const DecodeArgs& a, int u, int b, int j0, int r, bool first,
+                                             UnitCtx* ctx, TokenRef* tr) {
+  RefPipe<SUB> rp;
+  refs_list<SUB>(a, u, b, j0, r, first, rp);
+  refs_table<SUB>(a, rp);
+  refs_finish<SUB>(a, rp, ctx, tr);
 }
 
 // ---------------------------------------------------------------------------
@@ -149,8 +181,54 @@ __device__ __forceinline__ double count_pow(int n, float alpha) {
   return (double)v * (1.0 + 1e-5);
 }
 
-template <int D, int G, int SUB>
-__global__ __launch_bounds__(kDecThreads) void gather_mfma_kernel(DecodeArgs a, int slots) {
+// Balanced assignment (BAL): the super-items of all units are numbered
+// unit by unit, and block i takes the contiguous range [i C, i C + C),
+// C = ceil(total / blocks), so every block gets the same work whatever the
+// units' sizes and most blocks stay inside one unit.  Every wave computes
+// the numbering itself from the units' sizes (lane l: units 8 l .. 8 l + 7,
+// at most 512 units), without a block barrier.
+struct UnitWalk {
+  int incl;     // inclusive count of super-items through this lane's units
+  int pre[8];   // first super-item of each of this lane's units
+  int sup[8];   // super-items of each
+};
+
+template <int SUB>
+__device__ __forceinline__ int unit_walk(const DecodeArgs& a, UnitWalk* uw) {
+  const int lane = threadIdx.x & 63, units = a.batch * a.n_kv_heads;
+  int sum = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int u = 8 * lane + k;
+    uw->sup[k] = u < units ? (unit_items(a, u) + SUB - 1) / SUB : 0;
+    sum += uw->sup[k];
+  }
+  uw->incl = wave_incl_scan(sum);
+  int run = uw->incl - sum;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    uw->pre[k] = run;
+    run += uw->sup[k];
+  }
+  return __builtin_amdgcn_readlane(uw->incl, 63);
+}
+
+// The unit holding super-item gs (gs < total) and gs's index inside it.
+__device__ __forceinline__ void unit_locate(const UnitWalk& uw, int gs, int* u, int* sj) {
+  const int owner = __popcll(__ballot(uw.incl <= gs));  // lanes whose units all end at or before gs
+  int k = 0;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) k += __builtin_amdgcn_readlane(uw.pre[kk] + uw.sup[kk], owner) <= gs;
+  int p = 0;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) p = kk == k ? uw.pre[kk] : p;
+  *u = 8 * owner + k;
+  *sj = gs - __builtin_amdgcn_readlane(p, owner);
+}
+
+template <int D, int G, int SUB, bool BAL>
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(BAL || G > 4 ? 2 : 4))) void gather_mfma_kernel(
+    DecodeArgs a, int slots) {
   constexpr int KB = D / 32;
   constexpr int NH = (G + 3) / 4;  // 16-row operands (four heads each)
   __shared__ u32x4_t s_a[NH * KB][kWave];
@@ -158,28 +236,44 @@ __global__ __launch_bounds__(kDecThreads) void gather_mfma_kernel(DecodeArgs a, 
   __shared__ int s_cnt[NH][SUB][4][4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int u = blockIdx.y, Hkv = a.n_kv_heads;
-  const int b = u / Hkv, g = u - b * Hkv;
+  const int Hkv = a.n_kv_heads;
   const size_t tok_per_bh = (size_t)a.max_items * kItemTokens;
   const int r = 16 * w + col;  // this lane's token within an item
+  int u, sj, gs = 0, gs_end = 0;
+  UnitWalk uw;
+  if (BAL) {
+    const int total = unit_walk<SUB>(a, &uw);
+    const int C = (total + (int)gridDim.x - 1) / (int)gridDim.x;
+    gs = (int)blockIdx.x * C;
+    gs_end = min(gs + C, total);
+    if (gs >= gs_end) return;  // block-uniform: nothing left for this block
+    unit_locate(uw, gs, &u, &sj);
+  } else {
+    u = blockIdx.y;
+    sj = blockIdx.x;
+  }
+  int b = u / Hkv, g = u - b * Hkv;
 
   // loads, in order: q for the A operand, then the first super-item's
   // references (resolved speculatively with the unit's size)
   const float qs = (a.alpha - 1.f) * a.scale;
-  const float* qg = a.q + ((size_t)b * a.n_q_heads + (size_t)g * G) * D;
   LimbChunks<KB, NH> lc;
-  limb_fetch<KB, G, NH>(lc, [&](int h, int k0, float* v) {
-    const float4* qv = reinterpret_cast<const float4*>(qg + (size_t)h * D + k0);
-    const float4 q0 = qv[0], q1 = qv[1];
-    v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w; v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
-  });
+  auto fetch_q = [&]() {
+    const float* qg = a.q + ((size_t)b * a.n_q_heads + (size_t)g * G) * D;
+    limb_fetch<KB, G, NH>(lc, [&](int h, int k0, float* v) {
+      const float4* qv = reinterpret_cast<const float4*>(qg + (size_t)h * D + k0);
+      const float4 q0 = qv[0], q1 = qv[1];
+      v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w; v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
+    });
+  };
+  fetch_q();
   UnitCtx ctx;
   TokenRef tr[SUB];
-  resolve_refs<SUB>(a, u, b, blockIdx.x * SUB, r, true, &ctx, tr);
+  resolve_refs<SUB>(a, u, b, sj * SUB, r, true, &ctx, tr);
   bool a_ready = false;
   const int n_super = (ctx.n_items + SUB - 1) / SUB;
-  for (int sj = blockIdx.x; sj < n_super; sj += slots) {
-    if (sj != (int)blockIdx.x) resolve_refs<SUB>(a, u, b, sj * SUB, r, false, &ctx, tr);
+  RefPipe<SUB> nxt;  // the next super-item's references, in flight behind this one
+  while (BAL || sj < n_super) {
     u32x4_t bv[SUB][KB];
 #pragma unroll
     for (int s = 0; s < SUB; ++s) {
@@ -193,6 +287,17 @@ __global__ __launch_bounds__(kDecThreads) void gather_mfma_kernel(DecodeArgs a, 
         for (int kb = 0; kb < KB; ++kb) bv[s][kb] = u32x4_t{0u, 0u, 0u, 0u};
       }
     }
+    // the next super-item of this block, and its page-list round
+    int nu = u, nsj;
+    bool has_next;
+    if (BAL) {
+      has_next = gs + 1 < gs_end;
+      if (has_next) unit_locate(uw, gs + 1, &nu, &nsj);
+    } else {
+      nsj = sj + slots;
+      has_next = nsj < n_super;
+    }
+    if (has_next) refs_list<SUB>(a, nu, nu / Hkv, nsj * SUB, r, BAL, nxt);
     if (!a_ready) {  // q limbs: coefficients q_h (alpha-1) scale (block-uniform)
       limb_build<KB, G, NH>(s_a, lc, [qs](int, float qv) { return qv * qs; });
       __syncthreads();
@@ -213,6 +318,17 @@ __global__ __launch_bounds__(kDecThreads) void gather_mfma_kernel(DecodeArgs a, 
         if (col == 0) s_max[hh][s][w][grp] = m;
       }
     }
+    // this super-item's token ids and rows, kept aside so that the next
+    // super-item's references can be finished before the stores below (a
+    // later wait on them would also wait for those stores)
+    int ct_cur[SUB], cr_cur[SUB];
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      ct_cur[s] = tr[s].logical;
+      cr_cur[s] = tr[s].phys * a.page_size + tr[s].slot;
+    }
+    const int n_items_cur = ctx.n_items;
+    if (has_next) refs_table<SUB>(a, nxt);  // its page-list entries are in by now
     __syncthreads();
     // candidates: above a lower bound on tau (tokens at or below it have
     // weight 0).  The super-item maximum gives msup - 1 (the top token alone
@@ -256,6 +372,7 @@ __global__ __launch_bounds__(kDecThreads) void gather_mfma_kernel(DecodeArgs a, 
         if (col == 0) s_cnt[hh][s][w][grp] = __popc(bits[hh][s]);
       }
     }
+    if (has_next) refs_finish<SUB>(a, nxt, &ctx, tr);
     __syncthreads();
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh) {
@@ -265,7 +382,7 @@ __global__ __launch_bounds__(kDecThreads) void gather_mfma_kernel(DecodeArgs a, 
 #pragma unroll
       for (int s = 0; s < SUB; ++s) {
         const int j = sj * SUB + s;
-        if (j >= ctx.n_items) break;
+        if (j >= n_items_cur) break;
         int off = 0, tot = 0;
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
@@ -276,8 +393,8 @@ __global__ __launch_bounds__(kDecThreads) void gather_mfma_kernel(DecodeArgs a, 
           const int pos = off + __popc(bits[hh][s] & ((1u << col) - 1u));
           const size_t at = bh * tok_per_bh + (size_t)j * kItemTokens + pos;
           a.cand_x[at] = x[hh][s];
-          a.cand_t[at] = tr[s].logical;
-          a.cand_r[at] = tr[s].phys * a.page_size + tr[s].slot;
+          a.cand_t[at] = ct_cur[s];
+          a.cand_r[at] = cr_cur[s];
         }
         if (w == 0 && col == 0) {
           a.item_cnt[bh * a.max_items + j] = tot;
@@ -286,7 +403,19 @@ __global__ __launch_bounds__(kDecThreads) void gather_mfma_kernel(DecodeArgs a, 
         }
       }
     }
-    __syncthreads();  // s_max / s_cnt are rewritten by the next super-item
+    __syncthreads();  // s_max / s_cnt (and s_a on a unit change) are rewritten next
+    if (!has_next) break;
+    if (BAL) {
+      ++gs;
+      if (nu != u) {  // the next unit's queries
+        u = nu;
+        b = u / Hkv;
+        g = u - b * Hkv;
+        fetch_q();
+        a_ready = false;
+      }
+    }
+    sj = nsj;
   }
 }
 
@@ -956,7 +1085,7 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
   for (int s = rr; s < nsup; s += RPB) {
     const int row = rs[s];
     const float p = xs[s];
-    const int phys = row / P, slot = row - phys * P;
+    const int phys = row >> __builtin_ctz(P), slot = row & (P - 1);  // P is a power of two
     const char* vrow = reinterpret_cast<const char*>(a.v) +
                        ((((size_t)phys * a.hkv_mem + (g >> a.kv_shift)) * P + slot) * D + (size_t)sub * EPL) * E::kBytes;
     float f[EPL];
@@ -986,15 +1115,22 @@ __global__ __launch_bounds__(kTauThreads) void tau_v_kernel(DecodeArgs a) {
 }
 
 template <int DT, int D>
-static hipError_t decode_dispatch(const DecodeArgs& a, int slots, hipStream_t s) {
-  const dim3 g1(slots, a.batch * a.n_kv_heads), b1(kDecThreads);
+static hipError_t decode_dispatch(const DecodeArgs& a, int slots, int bal_blocks, hipStream_t s) {
+  const dim3 g1(slots, a.batch * a.n_kv_heads), b1(kDecThreads), gb(bal_blocks);
   const bool mfma = DT == EKV_BF16;
-  if (mfma) {
+  if (mfma && bal_blocks > 0) {
     switch (a.group) {
-      case 1: hipLaunchKernelGGL((gather_mfma_kernel<D, 1, 4>), g1, b1, 0, s, a, slots); break;
-      case 2: hipLaunchKernelGGL((gather_mfma_kernel<D, 2, 4>), g1, b1, 0, s, a, slots); break;
-      case 4: hipLaunchKernelGGL((gather_mfma_kernel<D, 4, 4>), g1, b1, 0, s, a, slots); break;
-      default: hipLaunchKernelGGL((gather_mfma_kernel<D, 8, 4>), g1, b1, 0, s, a, slots); break;
+      case 1: hipLaunchKernelGGL((gather_mfma_kernel<D, 1, 4, true>), gb, b1, 0, s, a, 0); break;
+      case 2: hipLaunchKernelGGL((gather_mfma_kernel<D, 2, 4, true>), gb, b1, 0, s, a, 0); break;
+      case 4: hipLaunchKernelGGL((gather_mfma_kernel<D, 4, 4, true>), gb, b1, 0, s, a, 0); break;
+      default: hipLaunchKernelGGL((gather_mfma_kernel<D, 8, 4, true>), gb, b1, 0, s, a, 0); break;
+    }
+  } else if (mfma) {
+    switch (a.group) {
+      case 1: hipLaunchKernelGGL((gather_mfma_kernel<D, 1, 4, false>), g1, b1, 0, s, a, slots); break;
+      case 2: hipLaunchKernelGGL((gather_mfma_kernel<D, 2, 4, false>), g1, b1, 0, s, a, slots); break;
+      case 4: hipLaunchKernelGGL((gather_mfma_kernel<D, 4, 4, false>), g1, b1, 0, s, a, slots); break;
+      default: hipLaunchKernelGGL((gather_mfma_kernel<D, 8, 4, false>), g1, b1, 0, s, a, slots); break;
     }
   } else {
     switch (a.group) {
@@ -1016,9 +1152,12 @@ static hipError_t decode_dispatch(const DecodeArgs& a, int slots, hipStream_t s)
 
 // Gather grid: (slots, units).  A unit has at most `items` 64-token items
 // (the largest possible selection); on the matrix-core path items are
-// grouped into super-items of four for the full cache (more loads in flight
-// per block) and taken one by one for a selection.  slots is chosen so the
-// grid holds about `target_blocks` blocks, and never exceeds the work.
+// grouped into super-items of four (more loads in flight per block).  slots
+// is chosen so the grid holds about `target_blocks` blocks, and never
+// exceeds the work.  With 64 to 512 units on the matrix-core path the
+// `target_blocks` blocks instead share all units' super-items evenly (the
+// balanced assignment above): selections differ in size between units, and
+// a fixed number of blocks per unit would wait for the largest.
 hipError_t launch_decode(const DecodeArgs& a, int target_blocks, hipStream_t s) {
   const long long pages = a.sel ? (a.cap < a.max_pages ? a.cap : a.max_pages) : a.max_pages;
   const long long items = (pages * a.page_size + kItemTokens - 1) / kItemTokens;
@@ -1030,11 +1169,12 @@ hipError_t launch_decode(const DecodeArgs& a, int target_blocks, hipStream_t s) 
   if (slots > supers) slots = supers;
   if (slots < 1) slots = 1;
   if (slots > 65535) slots = 65535;
+  const int bal = mfma && units >= 64 && units <= 512 ? target_blocks : 0;
   if (a.kv_dtype == EKV_BF16)
-    return a.head_dim == 128 ? decode_dispatch<EKV_BF16, 128>(a, (int)slots, s)
-                             : decode_dispatch<EKV_BF16, 64>(a, (int)slots, s);
-  return a.head_dim == 128 ? decode_dispatch<EKV_F32, 128>(a, (int)slots, s)
-                           : decode_dispatch<EKV_F32, 64>(a, (int)slots, s);
+    return a.head_dim == 128 ? decode_dispatch<EKV_BF16, 128>(a, (int)slots, bal, s)
+                             : decode_dispatch<EKV_BF16, 64>(a, (int)slots, bal, s);
+  return a.head_dim == 128 ? decode_dispatch<EKV_F32, 128>(a, (int)slots, 0, s)
+                           : decode_dispatch<EKV_F32, 64>(a, (int)slots, 0, s);
 }
 
 // ---------------------------------------------------------------------------

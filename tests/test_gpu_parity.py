@@ -198,6 +198,23 @@ def test_c5_reduced_with_appends():
 
 
 # ----------------------------------------------------------- edge cases ---
+@pytest.mark.parametrize("per_head", [False, True])
+def test_balanced_gather_many_units(per_head):
+    """18 (sequence, KV head) units of 300 to 4000 tokens, or 72 query-head
+    units: the gather spreads all units' work evenly over its blocks, so a
+    block's range crosses unit boundaries and rebuilds its query operand."""
+    spec = W.make_spec("c5", batch=9, ctx_lo=300, ctx_hi=4000, steps=0, n_q_heads=8, n_kv_heads=2)
+    sess, _ = _session(spec)
+    q = W.queries(spec)
+    res = run_step(sess, spec, q, per_head=per_head)
+    if per_head:
+        units = [(b, h) for b in range(spec.batch) for h in range(spec.n_q_heads)]
+    else:
+        units = all_units(spec)
+    check_step(spec, res, q, units, per_head=per_head)
+    assert sess.device_status() == 0
+
+
 def test_topk_covering_every_page_equals_dense():
     spec = W.make_spec("c2", context=1000, n_q_heads=8, n_kv_heads=2, n_needles=8, top_k=10 ** 6)
     sess, _ = _session(spec)
