@@ -26,6 +26,7 @@ constexpr int kSelThreads = 1024;
 constexpr int kTauHatThreads = 1024;
 constexpr int kTauHatPPT = 16;           // pages per thread held in registers (n_b <= 16384)
 constexpr int kTauHatLive = 8192;        // pages alive at the start point kept in LDS
+constexpr int kTauHatLiveBig = 16384;    // the same for sequences of more than 8192 pages (one block per CU)
 
 __device__ __forceinline__ int clamp_len(int L, int max_pages, int P, uint32_t* status) {
   if (L < 0 || (long long)L > (long long)max_pages * P) {
@@ -688,7 +689,7 @@ __device__ void gauss_floor_unit(const SelectArgs& a, int b, int g, int n_b, int
 
 // GEN: alpha other than 1.5 and 2 (a separate instance, so that the
 // quadrature's registers do not weigh on the closed-form one)
-template <int G, bool GEN>
+template <int G, bool GEN, int LIVE>
 __global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
   constexpr int PPT = kTauHatPPT;
   constexpr int NW = kTauHatThreads / kWave;
@@ -702,7 +703,7 @@ __global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
   const float2* st = a.musd + bh * a.max_pages;
   const float* eh = a.ehat + bh * a.max_pages;
   uint64_t* kbits = a.keep_bits + bh * a.keep_words;
-  __shared__ float2 live[kTauHatLive];
+  __shared__ float2 live[LIVE];
   __shared__ double part[2][NW][3];
   __shared__ double redd[16];
   __shared__ int redi[17];
@@ -751,7 +752,7 @@ __global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
 #pragma unroll
       for (int i = 0; i < PPT; ++i) c += (i * kTauHatThreads + tid < n_b) && alive(ms[i]);
       int pos = block_exclusive_scan(c, redi, &n_live);
-      use_live = n_live <= kTauHatLive;
+      use_live = n_live <= LIVE;
       if (use_live) {
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
@@ -972,21 +973,27 @@ hipError_t launch_score_gauss(const SelectArgs& a, hipStream_t s) {
   return a.head_dim == 128 ? gauss_dispatch_g<128>(a, grid, s) : gauss_dispatch_g<64>(a, grid, s);
 }
 
-template <bool GEN>
+template <bool GEN, int LIVE>
 static hipError_t tau_hat_dispatch(const SelectArgs& a, hipStream_t s) {
   const dim3 grid(a.n_q_heads, a.batch), block(kTauHatThreads);
   switch (a.group) {
-    case 1: hipLaunchKernelGGL((tau_hat_kernel<1, GEN>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((tau_hat_kernel<2, GEN>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((tau_hat_kernel<4, GEN>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((tau_hat_kernel<8, GEN>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((tau_hat_kernel<1, GEN, LIVE>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((tau_hat_kernel<2, GEN, LIVE>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((tau_hat_kernel<4, GEN, LIVE>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((tau_hat_kernel<8, GEN, LIVE>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+// The live-page list holds 8192 pages (two blocks per compute unit) unless a
+// sequence can have more pages; then 16384 (128 KB of LDS, one block per
+// unit), so that long sequences keep iterating on chip.
 hipError_t launch_tau_hat(const SelectArgs& a, hipStream_t s) {
-  return (a.alpha == 1.5f || a.alpha == 2.0f) ? tau_hat_dispatch<false>(a, s) : tau_hat_dispatch<true>(a, s);
+  const bool gen = !(a.alpha == 1.5f || a.alpha == 2.0f);
+  if (a.max_pages > kTauHatLive)
+    return gen ? tau_hat_dispatch<true, kTauHatLiveBig>(a, s) : tau_hat_dispatch<false, kTauHatLiveBig>(a, s);
+  return gen ? tau_hat_dispatch<true, kTauHatLive>(a, s) : tau_hat_dispatch<false, kTauHatLive>(a, s);
 }
 
 }  // namespace ekv
