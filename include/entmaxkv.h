@@ -239,9 +239,9 @@ ekv_status ekv_entmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const
  *   lse   optional [batch][n_q_heads] float32: log sum_j exp(z_j) over the
  *         set (-inf when it is empty); the full-cache mass outside a kept
  *         set J is 1 - exp(lse_J - lse_full)
- * Other arguments as for ekv_entmax_decode.  Needs bf16 K/V and query
- * groups of at most 4 heads (else EKV_ERR_UNSUPPORTED).  Accumulates in
- * float32 with a running maximum per block, merged in a fixed order.
+ * Other arguments as for ekv_entmax_decode.  Needs bf16 K/V (else
+ * EKV_ERR_UNSUPPORTED).  Accumulates in float32 with a running maximum per
+ * block, merged in a fixed order.
  */
 ekv_status ekv_softmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const float* q,
                               int32_t n_q_heads, float scale, const int32_t* sel,

@@ -263,7 +263,7 @@ ekv_status prepare_decode(const ekv_cache* cache, const ekv_seqs* seqs, const fl
   if ((st = check_ws(cache, seqs, n_q_heads, workspace, ws_bytes, L)) != EKV_OK) return st;
   *a = ekv::DecodeArgs{};
   a->batch = seqs->batch; a->n_kv_heads = cache->n_kv_heads; a->n_q_heads = n_q_heads; a->group = G;
-  a->hkv_mem = cache->n_kv_heads; a->kv_shift = 0;
+  a->hkv_mem = cache->n_kv_heads; a->kv_shift = 0; a->sel_shift = 0;
   a->page_size = cache->page_size; a->head_dim = cache->head_dim; a->kv_dtype = cache->kv_dtype;
   a->max_pages = seqs->max_pages; a->n_phys = cache->n_phys_pages;
   a->page_table = seqs->page_table; a->seq_lens = seqs->seq_lens;
@@ -312,8 +312,15 @@ ekv_status ekv_softmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, cons
   ekv_status st = prepare_decode(cache, seqs, q, n_q_heads, 2.0f, scale, sel, sel_count, cap, sel_heads, out,
                                  workspace, ws_bytes, &a, &L);
   if (st != EKV_OK) return st;
-  if (cache->kv_dtype != EKV_BF16 || a.group > 4)
-    return fail(EKV_ERR_UNSUPPORTED, "softmax decode needs bf16 keys/values and at most 4 query heads per KV head");
+  if (cache->kv_dtype != EKV_BF16) return fail(EKV_ERR_UNSUPPORTED, "softmax decode needs bf16 keys/values");
+  if (a.group == 8) {
+    // the kernels hold four heads per unit: split each query group in two
+    // halves, each reading its KV head's rows and page list
+    a.n_kv_heads *= 2;
+    a.group = 4;
+    a.kv_shift += 1;
+    if (a.sel) a.sel_shift = 1;
+  }
   float* part = at<float>(workspace, L.smx_part);
   return hip_status(ekv::launch_softmax(a, 4 * device_cus(), part, ekv::kSmxMaxSlots, lse, (hipStream_t)stream),
                     "softmax_decode launch");

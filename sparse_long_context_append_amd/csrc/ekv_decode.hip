@@ -37,7 +37,7 @@ __device__ __forceinline__ int unit_pages(const DecodeArgs& a, int u) {
   const int b = u / a.n_kv_heads;
   const int n_b = pages_of(dec_len(a, b), a.page_size);
   if (!a.sel) return n_b;
-  return min(max(a.sel_count[u], 0), min(a.cap, n_b));
+  return min(max(a.sel_count[u >> a.sel_shift], 0), min(a.cap, n_b));
 }
 
 __device__ __forceinline__ int unit_items(const DecodeArgs& a, int u) {
@@ -59,7 +59,7 @@ __device__ __forceinline__ TokenRef token_ref(const DecodeArgs& a, int u, int b,
   if (T >= (long long)npu * P) return t;
   const int k = (int)(T >> __builtin_ctz(P));  // P is a power of two
   t.slot = (int)(T & (P - 1));
-  const int lp = a.sel ? a.sel[(size_t)u * a.cap + k] : k;
+  const int lp = a.sel ? a.sel[(size_t)(u >> a.sel_shift) * a.cap + k] : k;
   if (lp < 0 || lp >= n_b) {
     set_status(a.status, EKV_DEV_BAD_PAGE);
     return t;
@@ -107,11 +107,11 @@ __device__ __forceinline__ void refs_list(const DecodeArgs& a, int u, int b, int
   for (int s = 0; s < SUB; ++s) {
     const long long T = (long long)(j0 + s) * kItemTokens + r;
     const int k = (int)(T >> __builtin_ctz(P));  // P is a power of two
-    rp.lp[s] = k < capk ? (a.sel ? a.sel[(size_t)u * a.cap + k] : k) : -1;
+    rp.lp[s] = k < capk ? (a.sel ? a.sel[(size_t)(u >> a.sel_shift) * a.cap + k] : k) : -1;
   }
   if (first) {
     rp.L = a.seq_lens[b];
-    rp.cnt = a.sel ? a.sel_count[u] : 0;
+    rp.cnt = a.sel ? a.sel_count[u >> a.sel_shift] : 0;
   }
 }
 

@@ -57,6 +57,8 @@ struct SelectArgs {
 struct DecodeArgs {
   int batch, n_kv_heads, n_q_heads, group, page_size, head_dim, kv_dtype, max_pages, n_phys;
   int hkv_mem, kv_shift;  // as in SelectArgs
+  int sel_shift;          // unit u reads page-list row u >> sel_shift (two units per list row when a
+                          // query group is split in halves)
   const int32_t* page_table;
   const int32_t* seq_lens;
   const void* k;

@@ -56,8 +56,10 @@ def _check_softmax(spec, q, units, out, lse, sel=None, cnt=None, lens=None, kv=N
             assert abs(lse[b, h] - r["lse"]) <= 1e-4 * max(1.0, abs(r["lse"])), f"lse {lse[b, h]} vs {r['lse']}"
 
 
-@pytest.mark.parametrize("hkv,d", [(2, 128), (8, 128), (4, 64)])
+@pytest.mark.parametrize("hkv,d", [(2, 128), (8, 128), (4, 64), (1, 128)])
 def test_softmax_sparse_and_full(hkv, d):
+    """Groups of 4, 1, 2 and 8 query heads (8: two half-group units per KV
+    head, each reading the shared page list)."""
     spec = W.make_spec("c2", context=4099, page_size=16, top_k=40, n_q_heads=8, n_kv_heads=hkv, head_dim=d,
                        n_needles=16)
     sess, _ = _session(spec)
