@@ -215,6 +215,38 @@ def test_balanced_gather_many_units(per_head):
     assert sess.device_status() == 0
 
 
+@pytest.mark.parametrize("P,ctx,policy", [(1, 517, "bbox"), (1, 517, "gauss"), (2, 1031, "bbox"),
+                                          (1024, 5000, "bbox"), (1024, 5000, "gauss")])
+def test_extreme_page_sizes(P, ctx, policy):
+    """Pages of 1 and 2 tokens (an item spans 64 or 32 pages; one-token pages
+    have zero variance) and of 1024 tokens (one page spans 16 items, the last
+    page is partial); selected and full-cache decode."""
+    if policy == "bbox":
+        spec = W.make_spec("c2", context=ctx, page_size=P, top_k=max(2, (ctx // P) // 8), n_q_heads=8,
+                           n_kv_heads=2, n_needles=8)
+    else:
+        spec = W.make_spec("c3", batch=1, context=ctx, page_size=P, n_q_heads=8, n_kv_heads=2)
+    sess, _ = _session(spec)
+    q = W.queries(spec)
+    cache = {}
+    check_step(spec, run_step(sess, spec, q), q, all_units(spec), kv_cache=cache)
+    check_step(spec, run_step(sess, spec, q, sparse=False), q, all_units(spec), sparse=False, kv_cache=cache)
+    assert sess.device_status() == 0
+
+
+def test_topk_at_max_pages():
+    """65535 pages, the most top-k accepts: 64 keys per thread, streamed from
+    memory on every radix pass instead of held in registers."""
+    spec = W.make_spec("c2", context=65535 * 16, page_size=16, top_k=300, n_q_heads=4, n_kv_heads=1,
+                       n_needles=64)
+    sess, _ = _session(spec)
+    q = W.queries(spec)
+    res = run_step(sess, spec, q)
+    assert int(res["cnt"][0, 0]) == 300
+    check_step(spec, res, q, [(0, 0)])
+    assert sess.device_status() == 0
+
+
 def test_topk_covering_every_page_equals_dense():
     spec = W.make_spec("c2", context=1000, n_q_heads=8, n_kv_heads=2, n_needles=8, top_k=10 ** 6)
     sess, _ = _session(spec)
