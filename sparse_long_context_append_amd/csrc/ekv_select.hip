@@ -634,16 +634,72 @@ __device__ void gauss_mass_general(float mu, float sd, float tf, float beta, flo
   de = (float)(-(double)beta * sc / (double)sd * (double)m1);
 }
 
+// Other alpha, per page and Newton step: log M_e and log M_(e-1) are
+// tabulated once per block on the grid u = -7 + i/32 (1536 nodes up to
+// u = 40.97; the step is a power of two, so the nodes are exact in fp32)
+// with the quadrature above; a page's expectation is then a four-point
+// Lagrange interpolation of the logs (log M is smooth in u: error near
+// 1e-8) and two exponentials, split into 2^k times a hardware exp2 of the
+// fraction.  Zero variance and u > 40 keep the closed forms above.
+constexpr int kMomNodes = 1536;
+constexpr float kMomU0 = -7.f;
+constexpr double kMomInvH = 32.0;
+
+template <bool GEN> struct MomTable {
+  double lm[kMomNodes], lm1[kMomNodes];
+};
+template <> struct MomTable<false> {};  // the closed-form instance needs no table
+
+__device__ void mom_table_build(MomTable<true>& T, float beta) {
+  for (int i = threadIdx.x; i < kMomNodes; i += blockDim.x) {
+    float e, de;
+    gauss_mass_general(kMomU0 + (float)i * (1.f / 32.f), 1.f, 0.f, beta, e, de);  // M_e(u), -e M_(e-1)(u)
+    T.lm[i] = log((double)e);
+    T.lm1[i] = log(-(double)de / (double)beta);
+  }
+}
+
+// e^y with fp32 relative accuracy: 2^k times the hardware 2^f, f in [0, 1)
+__device__ __forceinline__ float exp_split(double y) {
+  const double x = y * 1.4426950408889634;
+  const double k = floor(x);
+  return __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f((float)(x - k)), (int)k);
+}
+
+__device__ void gauss_mass_table(float mu, float sd, float tf, float beta, const MomTable<true>& T, float& e,
+                                 float& de) {
+  const float am = mu - tf;
+  if (sd <= 0.f || am > 40.f * sd) {  // a single point, or beyond the table: closed forms
+    gauss_mass_general(mu, sd, tf, beta, e, de);
+    return;
+  }
+  const float u = am / sd;
+  if (u < -7.f) {
+    e = de = 0.f;
+    return;
+  }
+  const double x = ((double)u - (double)kMomU0) * kMomInvH;
+  const int i = max(0, min((int)x - 1, kMomNodes - 4));
+  const double s = x - (double)i;  // position among the nodes i .. i + 3
+  const double w0 = -(s - 1.0) * (s - 2.0) * (s - 3.0) * (1.0 / 6.0), w1 = s * (s - 2.0) * (s - 3.0) * 0.5,
+               w2 = -s * (s - 1.0) * (s - 3.0) * 0.5, w3 = s * (s - 1.0) * (s - 2.0) * (1.0 / 6.0);
+  const double lm = ((w0 * T.lm[i] + w1 * T.lm[i + 1]) + w2 * T.lm[i + 2]) + w3 * T.lm[i + 3];
+  const double lm1 = ((w0 * T.lm1[i] + w1 * T.lm1[i + 1]) + w2 * T.lm1[i + 2]) + w3 * T.lm1[i + 3];
+  const double ls = log((double)sd);
+  e = exp_split((double)beta * ls + lm);
+  de = -beta * exp_split(((double)beta - 1.0) * ls + lm1);
+}
+
 // live-list entries carry the partial last page as sd -> -sd - 1.
 // mode: 0 alpha = 2, 1 alpha = 1.5, 2 other alpha (beta = 1/(alpha-1);
 // no second derivative, ddF is left unchanged).
 template <bool GEN>
 __device__ __forceinline__ void live_term(float2 v, float P, float last_n, float tf, int mode, float beta,
-                                          double& F, double& dF, double& ddF) {
+                                          const MomTable<GEN>& T, double& F, double& dF, double& ddF) {
   float n = P, sd = v.y;
   if (sd < 0.f) { sd = -sd - 1.f; n = last_n; }
   float e, de, dde = 0.f;
-  if (GEN) gauss_mass_general(v.x, sd, tf, beta, e, de);
+  if constexpr (GEN) gauss_mass_table(v.x, sd, tf, beta, T, e, de);
   else gauss_mass(v.x, sd, tf, mode == 1, e, de, dde);
   F += (double)n * (double)e;
   dF += (double)n * (double)de;
@@ -704,6 +760,7 @@ __global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
   const float* eh = a.ehat + bh * a.max_pages;
   uint64_t* kbits = a.keep_bits + bh * a.keep_words;
   __shared__ float2 live[LIVE];
+  __shared__ MomTable<GEN> mom;
   __shared__ double part[2][NW][3];
   __shared__ double redd[16];
   __shared__ int redi[17];
@@ -722,6 +779,9 @@ __global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
     const float beta = 1.f / (a.alpha - 1.f);
     const float Pf = (float)P;
     const float last_n = (float)(L - (n_b - 1) * P);  // tokens of the last page
+    // (other alpha: the moment tables first, while few registers are live;
+    // the barriers of block_max below publish them)
+    if constexpr (GEN) mom_table_build(mom, beta);
     // thread t owns pages t, t + 1024, ...: one round of coalesced loads
     float2 ms[PPT];
     double lb = -INFINITY;
@@ -773,12 +833,12 @@ __global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
       double F = 0.0, dF = 0.0, ddF = 0.0;
       if (use_live) {
         for (int i = tid; i < n_live; i += kTauHatThreads)
-          live_term<GEN>(live[i], Pf, last_n, tf, mode, beta, F, dF, ddF);
+          live_term<GEN>(live[i], Pf, last_n, tf, mode, beta, mom, F, dF, ddF);
       } else {
         for (int p = tid; p < n_b; p += kTauHatThreads) {
           float2 v = st[p];
           if (p == n_b - 1 && last_n != Pf) v.y = -v.y - 1.f;
-          live_term<GEN>(v, Pf, last_n, tf, mode, beta, F, dF, ddF);
+          live_term<GEN>(v, Pf, last_n, tf, mode, beta, mom, F, dF, ddF);
         }
       }
       // wave partials -> wave 0 computes the step -> every wave reads it
