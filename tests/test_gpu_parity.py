@@ -130,10 +130,14 @@ def test_gauss_group_sizes(hkv):
     check_step(spec, run_step(sess, spec, q), q, all_units(spec))
 
 
-def test_gauss_more_pages_than_register_tiles():
-    """16392 pages of 16 tokens: the threshold estimate streams the page
-    statistics from memory instead of holding them in registers."""
-    spec = W.make_spec("c3", batch=1, context=16391 * 16 + 7, page_size=16, n_q_heads=4, n_kv_heads=1)
+@pytest.mark.parametrize("pages,alpha", [(16392, 2.0), (16392, 1.3), (12000, 1.3)])
+def test_gauss_more_pages_than_register_tiles(pages, alpha):
+    """More than 8192 pages: the threshold estimate keeps up to 16384 live
+    pages in LDS (with the tabulated moments at alpha 1.3), and beyond 16384
+    pages streams the page statistics from memory instead of holding them in
+    registers."""
+    spec = W.make_spec("c3", batch=1, context=(pages - 1) * 16 + 7, page_size=16, n_q_heads=2 if alpha != 2.0 else 4,
+                       n_kv_heads=1, alpha=alpha)
     sess, _ = _session(spec)
     q = W.queries(spec)
     check_step(spec, run_step(sess, spec, q), q, all_units(spec))
