@@ -119,8 +119,10 @@ typedef struct {
  *   top_k      pages kept per (sequence, KV head) by EKV_SELECT_BBOX_TOPK
  *              (all pages when top_k >= the sequence's page count)
  *   alpha      entmax alpha; EKV_SELECT_GAUSS supports alpha in [1.1, 2]
- *              (closed-form expectations at 1.5 and 2, 32-point quadrature
- *              otherwise)
+ *              (closed-form expectations at 1.5 and 2; otherwise truncated
+ *              normal moments tabulated by quadrature on each call and
+ *              interpolated)
+ *   top_k      also applies per query head when per_head = 1
  *   scale      score scale, normally 1/sqrt(head_dim)
  *   delta      EKV_SELECT_GAUSS safety margin, in the scaled score domain
  *              x = (alpha-1) scale q.k where the threshold lives
