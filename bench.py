@@ -44,12 +44,16 @@ def log(*a):
 
 
 # ---------------------------------------------------------------- bytes ----
-def step_bytes(spec, sel, sel_count, lens, support_union, sparse=True):
-    """Algorithmic bytes of one step (what the method must move)."""
+def step_bytes(spec, sel, sel_count, lens, support_union, sparse=True, appends=False):
+    """Algorithmic bytes of one step (what the method must move).  With
+    appends, each (sequence, KV head) also reads its new K and V row, writes
+    it into the cache and reads and writes its page's box and moment rows."""
     P, d, s = spec.page_size, spec.head_dim, spec.elem_bytes
     G = spec.group
     meta_rec = 2 * d * s if spec.policy == "bbox" else 2 * d * 4
     total = 0
+    if appends:
+        total += spec.batch * spec.n_kv_heads * (4 * d * s + 2 * (2 * d * s) + 2 * (2 * d * 4))
     for b in range(spec.batch):
         L = int(lens[b])
         n_b = -(-L // P)
@@ -163,15 +167,29 @@ def pct(xs, q):
 def measure(spec, steps, warmup, torch, timer, do_dense=True, do_graph=True):
     import sparse_long_context_append_amd as ekv
     from workloads.upload import build_session, queries_device
+    from workloads.upload import step_tokens
     t0 = time.perf_counter()
-    sess, _ = build_session(spec)
+    sess, appended = build_session(spec)
     log(f"{spec.name}: cache built in {time.perf_counter() - t0:.1f}s")
     q = queries_device(spec)
     pol = ekv.EKV_SELECT_BBOX_TOPK if spec.policy == "bbox" else ekv.EKV_SELECT_GAUSS
     SC = 4096
     supp = torch.full((spec.batch, spec.n_q_heads, SC), -1, dtype=torch.int32, device="cuda")
+    # workloads with decode-time appends (c5): every step first appends one
+    # token per sequence (its metadata update is part of the step); the
+    # tokens sit on the device beforehand, and after the last one the lengths
+    # go back to the prefilled ones (the same tokens are then written again)
+    toks = [step_tokens(spec, appended, s) for s in range(spec.steps)]
+    lens0 = sess.seq_lens.clone()
+    n_app = [0]
 
     def sparse_step():
+        if toks:
+            if n_app[0] == len(toks):
+                sess.seq_lens.copy_(lens0)
+                n_app[0] = 0
+            sess.append(*toks[n_app[0]])
+            n_app[0] += 1
         sess.select(q, policy=pol, alpha=spec.alpha, scale=spec.scale, top_k=spec.top_k, delta=spec.delta)
         sess.decode(q, alpha=spec.alpha, scale=spec.scale, sparse=True)
 
@@ -193,7 +211,7 @@ def measure(spec, steps, warmup, torch, timer, do_dense=True, do_graph=True):
     lens = sess.seq_lens.cpu().numpy()
     sc = sess.support_count.cpu().numpy()
     union = support_union_sizes(spec, supp.cpu().numpy(), sc)
-    res["bytes"] = step_bytes(spec, sel, cnt, lens, union, sparse=True)
+    res["bytes"] = step_bytes(spec, sel, cnt, lens, union, sparse=True, appends=bool(toks))
     res["pages_selected"] = int(cnt.sum())
     res["pages_total"] = int(sum(-(-int(L) // spec.page_size) for L in lens) * spec.n_kv_heads)
     res["support_mean"] = float(sc.mean())
@@ -205,7 +223,7 @@ def measure(spec, steps, warmup, torch, timer, do_dense=True, do_graph=True):
     # one fp32 score per (page, KV head); Gaussian: (mean, sd) + estimate + float4 stats per (page, query head)
     out_b = 4 if pol == 0 else 28 * spec.group
     res["score_bytes"] = float(npages * (rec + out_b))
-    if do_graph:
+    if do_graph and not toks:  # (a captured append would advance the lengths on every replay)
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
