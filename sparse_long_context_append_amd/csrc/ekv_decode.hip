@@ -1114,17 +1114,34 @@ __global__ __launch_bounds__(kTauThreads) void tau_v_kernel(DecodeArgs a) {
   tau_v_block<DT, D, AK>(a, blockIdx.y, blockIdx.x, sm);
 }
 
+// The balanced gather's grid: as many blocks as can be resident at once
+// (blocks per compute unit from the runtime's occupancy query for this
+// instance), so that no block waits for a second round; at most `cap`.
+template <auto Kernel>  // one cached query per kernel instance
+static int resident_grid(int cus, int cap) {
+  static const int per_cu = [] {
+    int n = 0;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, Kernel, kDecThreads, 0) == hipSuccess ? n : 0;
+  }();
+  return per_cu > 0 ? (per_cu * cus < cap ? per_cu * cus : cap) : cap;
+}
+
 template <int DT, int D>
 static hipError_t decode_dispatch(const DecodeArgs& a, int slots, int bal_blocks, hipStream_t s) {
-  const dim3 g1(slots, a.batch * a.n_kv_heads), b1(kDecThreads), gb(bal_blocks);
+  const dim3 g1(slots, a.batch * a.n_kv_heads), b1(kDecThreads);
   const bool mfma = DT == EKV_BF16;
   if (mfma && bal_blocks > 0) {
+    const int cus = bal_blocks / 4;  // bal_blocks: four per compute unit
+#define EKV_BAL(GG)                                                                               \
+  hipLaunchKernelGGL((gather_mfma_kernel<D, GG, 4, true>),                                        \
+                     dim3(resident_grid<gather_mfma_kernel<D, GG, 4, true>>(cus, bal_blocks)), b1, 0, s, a, 0)
     switch (a.group) {
-      case 1: hipLaunchKernelGGL((gather_mfma_kernel<D, 1, 4, true>), gb, b1, 0, s, a, 0); break;
-      case 2: hipLaunchKernelGGL((gather_mfma_kernel<D, 2, 4, true>), gb, b1, 0, s, a, 0); break;
-      case 4: hipLaunchKernelGGL((gather_mfma_kernel<D, 4, 4, true>), gb, b1, 0, s, a, 0); break;
-      default: hipLaunchKernelGGL((gather_mfma_kernel<D, 8, 4, true>), gb, b1, 0, s, a, 0); break;
+      case 1: EKV_BAL(1); break;
+      case 2: EKV_BAL(2); break;
+      case 4: EKV_BAL(4); break;
+      default: EKV_BAL(8); break;
     }
+#undef EKV_BAL
   } else if (mfma) {
     switch (a.group) {
       case 1: hipLaunchKernelGGL((gather_mfma_kernel<D, 1, 4, false>), g1, b1, 0, s, a, slots); break;
