@@ -627,7 +627,7 @@ def main():
     ap.add_argument("--alpha", type=float, default=0.0, help="override the workload's entmax alpha")
     ap.add_argument("--q-heads", type=int, default=0,
                     help="override the workload's query-head count (query groups of other sizes)")
-    ap.add_argument("--cpu-units", type=int, default=2, help="(sequence, KV head) units the CPU oracle is timed on")
+    ap.add_argument("--cpu-units", type=int, default=4, help="(sequence, KV head) units the CPU oracle is timed on")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline line: context sweep 32K..1M of the top-2%% and Gaussian "
                          "million-token workloads (one JSON line with a 'sweep' list)")
@@ -684,20 +684,22 @@ def main():
         n_units = spec.batch * spec.n_kv_heads
         units = [(b, g) for b in range(spec.batch) for g in range(spec.n_kv_heads)][: args.cpu_units]
         t0 = time.perf_counter()
-        sparse_s, dense_s = cpu_baseline(spec, units, dense_units=[units[0]])
+        dense_units = units[:2]
+        sparse_s, dense_s = cpu_baseline(spec, units, dense_units=dense_units)
         log(f"cpu oracle: {time.perf_counter() - t0:.1f}s including input preparation")
         cpu_us = sparse_s / len(units) * n_units * 1e6
         cpu = {
             "value": round(r["bytes"] / (cpu_us * 1e-6) / 1e9, 3),
             "unit": "GB/s",
             "us_per_step": round(cpu_us, 1),
-            "dense_us_per_step": round(dense_s * n_units * 1e6, 1),
+            "dense_us_per_step": round(dense_s / len(dense_units) * n_units * 1e6, 1),
             "cores": int(os.environ.get("OMP_NUM_THREADS", _NCPU)),
             "kind": "oracle",
             "sample": (f"float64 numpy oracle on the host, inputs prepared outside the timing: sparse step "
                        f"({spec.policy} scoring from prebuilt page metadata, selection, exact entmax over the "
                        f"kept pages) on {len(units)} of {n_units} (sequence, KV head) units of {spec.name}, "
-                       f"median of 3 per unit, scaled to all units; full-cache entmax on 1 unit, scaled"),
+                       f"median of 3 per unit, scaled to all units; full-cache entmax on {len(dense_units)} "
+                       f"units, scaled"),
         }
     med_us = main_sum["us_per_step"]
     sm_us = main_sum["score_kernel_us"]
