@@ -903,8 +903,10 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
     int run = 0;
     auto read_rounds = [&](int n_ne, int raw_tot) {
       for (int r0 = 0; r0 < raw_tot; r0 += RPT * kTauThreads) {
+        // scores, token ids and rows in one round of loads (the ids and rows
+        // of the few that pass are then at hand for the stores)
         float xv[RPT];
-        size_t av[RPT];
+        int tv[RPT], rv[RPT];
         const int i0 = r0 + RPT * tid;
         int k = 0;
         if (i0 < raw_tot) {
@@ -919,11 +921,13 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
         for (int c = 0; c < RPT; ++c) {
           const int i = i0 + c;
           xv[c] = -INFINITY;
-          av[c] = 0;
+          tv[c] = rv[c] = 0;
           if (i < raw_tot) {
             while (s_pre[k + 1] <= i) ++k;
-            av[c] = (size_t)sm.s_item[k] * kItemTokens + (i - s_pre[k]);
-            xv[c] = cx[av[c]];
+            const size_t at = (size_t)sm.s_item[k] * kItemTokens + (i - s_pre[k]);
+            xv[c] = cx[at];
+            tv[c] = ct[at];
+            rv[c] = cr[at];
           }
         }
         int kc = 0;
@@ -933,7 +937,7 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
         int pos = run + block_exclusive_scan(kc, redi, &tot);
 #pragma unroll
         for (int c = 0; c < RPT; ++c)
-          if ((double)xv[c] > thr) { ox[pos] = xv[c]; ot[pos] = ct[av[c]]; orow[pos] = cr[av[c]]; ++pos; }
+          if ((double)xv[c] > thr) { ox[pos] = xv[c]; ot[pos] = tv[c]; orow[pos] = rv[c]; ++pos; }
         run += tot;
       }
     };
