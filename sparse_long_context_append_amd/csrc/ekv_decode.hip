@@ -25,6 +25,16 @@ namespace ekv {
 constexpr int kDecThreads = 256;
 constexpr int kTauThreads = 256;
 constexpr int kTauItemChunk = 1024;
+constexpr int kCollectU = 16;  // items per wave per on-chip collection round
+
+// p[i] for i < n, else `fill`, read from p[min(i, n - 1)] (p[0] when n is
+// 0, which must be readable) without a branch: guarded loads written this
+// way are issued back to back, where a branch around each load costs a
+// wait for it.
+template <typename T> __device__ __forceinline__ T load_or(const T* p, int i, int n, T fill) {
+  const T v = p[i < n ? i : (n > 0 ? n - 1 : 0)];
+  return i < n ? v : fill;
+}
 
 __device__ __forceinline__ int dec_len(const DecodeArgs& a, int b) {
   const int L = a.seq_lens[b];
@@ -696,6 +706,7 @@ struct TauSmem {
   int lr[kLdsCands];
   int s_pre[kTauItemChunk + 1];
   int s_item[kTauItemChunk];
+  int s_tab[2][65];  // per-item kept counts of one collection round, their offsets
   float vpart[2048];  // row-group partial outputs (RPB x D <= 2048)
   double redd[48];  // block reductions (up to three values per wave)
   int redi[17];
@@ -739,19 +750,19 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
 
   // ---- item counts and maxima (one round of loads) ----
   constexpr int IPT = 4;  // items per thread when n_items <= 1024
-  constexpr int RPT = 16;  // raw candidates per thread when they number <= 4096
+  constexpr int RPT = 16;  // raw candidates per thread per round of the workspace path
   const int tid_w = tid >> 6;
   const bool few_items = n_items <= IPT * kTauThreads;
-  int loc[IPT], lsum = 0;
+  int loc[IPT];
   float lmx[IPT];
   float lmax = -INFINITY, llb = -INFINITY;
   if (few_items) {
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
       const int jj = IPT * tid + i;
-      loc[i] = jj < n_items ? icnt[jj] : 0;
-      lmx[i] = jj < n_items ? imax[jj] : -INFINITY;
-      llb = fmaxf(llb, jj < n_items ? ilb[jj] : -INFINITY);
+      loc[i] = load_or(icnt, jj, n_items, 0);
+      lmx[i] = load_or(imax, jj, n_items, -INFINITY);
+      llb = fmaxf(llb, load_or(ilb, jj, n_items, -INFINITY));
       lmax = fmaxf(lmax, lmx[i]);
     }
   } else {
@@ -761,8 +772,8 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int j = j0 + u * kTauThreads;
-        vm[u] = j < n_items ? imax[j] : -INFINITY;
-        vl[u] = j < n_items ? ilb[j] : -INFINITY;
+        vm[u] = load_or(imax, j, n_items, -INFINITY);
+        vl[u] = load_or(ilb, j, n_items, -INFINITY);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -807,7 +818,7 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int j = j0 + u * kTauThreads;
-          vm[u] = j < n_items ? imax[j] : -INFINITY;
+          vm[u] = load_or(imax, j, n_items, -INFINITY);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
@@ -823,80 +834,93 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
     thr = fmax(thr, cb - 1e-6 * fmax(1.0, fabs(m)));
   }
 
-  // ---- collect candidates above m - 1, in item order (an item whose
-  // maximum is at most m - 1 holds none) ----
+  // Kept candidates (above thr) of the listed items s_item[0, n_list),
+  // appended in item and token order to the on-chip list from position N.
+  // One wave per item, lane r reading the item's candidate r, so a wave's
+  // loads are contiguous; kCollectU items per wave per round, and one wave
+  // scans the round's 4 kCollectU per-item counts.  False, with the list
+  // abandoned, once it would exceed kLdsCands.
+  auto collect_lds = [&](int n_list, int& N) -> bool {
+    constexpr int U = kCollectU;
+    const int lane = tid & 63;
+    for (int r0 = 0; r0 < n_list; r0 += 4 * U) {
+      float xv[U];
+      int tv[U], rv[U], cv[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int k = r0 + tid_w * U + j;
+        const int it = sm.s_item[k < n_list ? k : n_list - 1];
+        const size_t at = (size_t)it * kItemTokens + lane;  // within the unit's item slots
+        const int c = icnt[it];
+        cv[j] = k < n_list ? c : 0;
+        xv[j] = cx[at];
+        tv[j] = ct[at];
+        rv[j] = cr[at];
+      }
+      uint64_t mk[U];
+      int mine = 0;
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        mk[j] = __ballot(lane < cv[j] && (double)xv[j] > thr);
+        mine = lane == j ? __popcll(mk[j]) : mine;
+      }
+      if (lane < U) sm.s_tab[0][tid_w * U + lane] = mine;
+      __syncthreads();
+      if (tid_w == 0) {
+        const int v = sm.s_tab[0][lane];
+        const int inc = wave_incl_scan(v);
+        sm.s_tab[1][lane] = N + inc - v;
+        if (lane == 63) sm.s_tab[1][64] = N + inc;
+      }
+      __syncthreads();
+      const int n_end = sm.s_tab[1][64];
+      if (n_end > kLdsCands) return false;
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        if ((mk[j] >> lane) & 1ull) {
+          const int pos = sm.s_tab[1][tid_w * U + j] + __popcll(mk[j] & ((1ull << lane) - 1ull));
+          lx[pos] = xv[j];
+          lt[pos] = tv[j];
+          lr[pos] = rv[j];
+        }
+      }
+      N = n_end;
+    }
+    return true;
+  };
+
+  // ---- collect candidates above thr, in item order (an item whose
+  // maximum is at most thr holds none) ----
   int N = 0;
-  bool in_lds = true, done = false;
+  bool in_lds = true, done = false, lds_full = false;
   if (few_items) {
     int nz = 0;
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
       if (!((double)lmx[i] > thr)) loc[i] = 0;
-      lsum += loc[i];
       nz += loc[i] > 0;
     }
-    // the non-empty items, listed with their first candidate's rank: one
-    // scan of (items << 17 | candidates), at most 1024 items and 65536
-    // candidates, so the fields cannot carry into each other
-    int packed_tot;
-    const int packed = block_exclusive_scan((nz << 17) | lsum, redi, &packed_tot);
-    const int raw_tot = packed_tot & 0x1ffff, n_ne = packed_tot >> 17;
-    int base = packed & 0x1ffff, rank = packed >> 17;
+    // the non-empty items, in order: one scan
+    int n_ne;
+    int rank = block_exclusive_scan(nz, redi, &n_ne);
 #pragma unroll
-    for (int i = 0; i < IPT; ++i) {
-      if (loc[i] > 0) {
-        s_pre[rank] = base;
-        sm.s_item[rank] = IPT * tid + i;
-        ++rank;
-      }
-      base += loc[i];
-    }
-    if (tid == 0) s_pre[n_ne] = raw_tot;
+    for (int i = 0; i < IPT; ++i)
+      if (loc[i] > 0) sm.s_item[rank++] = IPT * tid + i;
     __syncthreads();
-    if (raw_tot <= RPT * kTauThreads) {
-      // thread t reads raw candidates [RPT t, RPT t + RPT): one round of loads
-      float xv[RPT];
-      int tv[RPT], rv[RPT];
-      const int i0 = RPT * tid;
-      int k = 0;  // index into the non-empty items
-      if (i0 < raw_tot) {
-        int lo = 0, hi = n_ne;  // s_pre[lo] <= i0 < s_pre[hi]
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (s_pre[mid] <= i0) lo = mid; else hi = mid;
-        }
-        k = lo;
-      }
-#pragma unroll
-      for (int c = 0; c < RPT; ++c) {
-        const int i = i0 + c;
-        xv[c] = -INFINITY;
-        tv[c] = rv[c] = 0;
-        if (i < raw_tot) {
-          while (s_pre[k + 1] <= i) ++k;
-          const size_t at = (size_t)sm.s_item[k] * kItemTokens + (i - s_pre[k]);
-          xv[c] = cx[at];
-          tv[c] = ct[at];
-          rv[c] = cr[at];
-        }
-      }
-      int kc = 0;
-#pragma unroll
-      for (int c = 0; c < RPT; ++c) kc += (double)xv[c] > thr;
-      int pos = block_exclusive_scan(kc, redi, &N);
-      if (N <= kLdsCands) {  // else the general path below lists them in the workspace
-#pragma unroll
-        for (int c = 0; c < RPT; ++c)
-          if ((double)xv[c] > thr) { lx[pos] = xv[c]; lt[pos] = tv[c]; lr[pos] = rv[c]; ++pos; }
-        done = true;
-      }
+    done = collect_lds(n_ne, N);
+    if (!done) {
+      lds_full = true;
+      N = 0;
     }
   }
   if (!done) {
-    // general case.  The raw candidates of the listed items (s_item, with
-    // their first candidate's rank in s_pre) are read RPT per thread per
-    // round (one round of loads, one scan), and the kept ones appended to
-    // the workspace list, which is copied on chip afterwards when it fits.
+    // general case.  The items above thr are listed (s_item) and collected
+    // on chip as above; when their kept candidates do not fit there, or the
+    // items are too many to list at once, the raw candidates of the listed
+    // items (with their first candidate's rank in s_pre) are read RPT per
+    // thread per round (one round of loads, one scan), and the kept ones
+    // appended to the workspace list, which is copied on chip afterwards
+    // when it fits.
     float* ox = a.ovf_x + bh * tok_per_bh;
     int32_t* ot = a.ovf_t + bh * tok_per_bh;
     int32_t* orow = a.ovf_r + bh * tok_per_bh;
@@ -907,29 +931,31 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
         // of the few that pass are then at hand for the stores)
         float xv[RPT];
         int tv[RPT], rv[RPT];
+        // addresses first (the last candidate stands in past the end), then
+        // the loads, unconditionally
         const int i0 = r0 + RPT * tid;
-        int k = 0;
-        if (i0 < raw_tot) {
-          int lo = 0, hi = n_ne;  // s_pre[lo] <= i0 < s_pre[hi]
-          while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (s_pre[mid] <= i0) lo = mid; else hi = mid;
-          }
-          k = lo;
+        int lo = 0, hi = n_ne;  // s_pre[lo] <= min(i0, raw_tot - 1) < s_pre[hi]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s_pre[mid] <= min(i0, raw_tot - 1)) lo = mid; else hi = mid;
+        }
+        int k = lo;
+        size_t at[RPT];
+#pragma unroll
+        for (int c = 0; c < RPT; ++c) {
+          const int i = min(i0 + c, raw_tot - 1);
+          while (s_pre[k + 1] <= i) ++k;
+          at[c] = (size_t)sm.s_item[k] * kItemTokens + (i - s_pre[k]);
         }
 #pragma unroll
         for (int c = 0; c < RPT; ++c) {
-          const int i = i0 + c;
-          xv[c] = -INFINITY;
-          tv[c] = rv[c] = 0;
-          if (i < raw_tot) {
-            while (s_pre[k + 1] <= i) ++k;
-            const size_t at = (size_t)sm.s_item[k] * kItemTokens + (i - s_pre[k]);
-            xv[c] = cx[at];
-            tv[c] = ct[at];
-            rv[c] = cr[at];
-          }
+          xv[c] = cx[at[c]];
+          tv[c] = ct[at[c]];
+          rv[c] = cr[at[c]];
         }
+#pragma unroll
+        for (int c = 0; c < RPT; ++c)
+          if (i0 + c >= raw_tot) xv[c] = -INFINITY;
         int kc = 0;
 #pragma unroll
         for (int c = 0; c < RPT; ++c) kc += (double)xv[c] > thr;
@@ -954,7 +980,7 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
       for (int i0 = e0; i0 < e1; i0 += 8) {
         float vm[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) vm[q] = i0 + q < e1 ? imax[i0 + q] : -INFINITY;
+        for (int q = 0; q < 8; ++q) vm[q] = load_or(imax, i0 + q, e1, -INFINITY);
 #pragma unroll
         for (int q = 0; q < 8; ++q)
           if ((double)vm[q] > thr) { smask |= 1ull << (i0 + q - e0); ++scount; }
@@ -969,12 +995,19 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
           sm.s_item[spos++] = e0 + k;
         }
         __syncthreads();
+        if (!lds_full) {
+          done = collect_lds(n_sv, N);
+          if (!done) N = 0;
+        }
+      }
+      if (listed && !done) {
         // their raw counts and first ranks: thread t takes listed items 4t .. 4t+3
         int lc[4], sum = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int k = 4 * tid + q;
-          lc[q] = k < n_sv ? icnt[sm.s_item[k]] : 0;
+          const int c = icnt[sm.s_item[k < n_sv ? k : (n_sv > 0 ? n_sv - 1 : 0)]];
+          lc[q] = k < n_sv ? c : 0;
           sum += lc[q];
         }
         int raw_tot;
@@ -998,7 +1031,9 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int jj = 4 * tid + i;
-        lc[i] = jj < nc && (double)imax[c0 + jj] > thr ? icnt[c0 + jj] : 0;
+        const float mx = load_or(imax + c0, jj, nc, -INFINITY);
+        const int c = load_or(icnt + c0, jj, nc, 0);
+        lc[i] = (double)mx > thr ? c : 0;
         sum += lc[i];
         nz += lc[i] > 0;
       }
@@ -1020,12 +1055,14 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
       read_rounds(n_ne, raw_tot);
       __syncthreads();  // s_pre / s_item are rewritten by the next chunk
     }
-    N = run;
-    in_lds = N <= kLdsCands;
-    wait_mem();  // this thread's list entries are written before others read them
-    __syncthreads();
-    if (in_lds)
-      for (int i = tid; i < N; i += kTauThreads) { lx[i] = ox[i]; lt[i] = ot[i]; lr[i] = orow[i]; }
+    if (!done) {
+      N = run;
+      in_lds = N <= kLdsCands;
+      wait_mem();  // this thread's list entries are written before others read them
+      __syncthreads();
+      if (in_lds)
+        for (int i = tid; i < N; i += kTauThreads) { lx[i] = ox[i]; lt[i] = ot[i]; lr[i] = orow[i]; }
+    }
   }
   __syncthreads();
   float* xs = in_lds ? lx : a.ovf_x + bh * tok_per_bh;

@@ -272,11 +272,11 @@ def test_topk_covering_every_page_equals_dense():
 @pytest.mark.parametrize("alpha", [1.5, 2.0])
 def test_all_keys_equal_large_support(alpha, L, kv):
     """Every key identical: every page ties (lowest ids win) and every token
-    is in the support.  1500 tokens overflow the on-chip candidate list from
-    the register path, 5000 from the listed-items path; at 70000 (1094 items
-    of 64 tokens, all at the maximum) the full-cache decode lists more items
-    than fit on chip and takes the chunked path.  bf16 runs the matrix-core
-    gather, fp32 the vector one."""
+    is in the support.  1500 tokens fit the on-chip candidate list; 5000
+    overflow it, so the listed items' candidates go through the workspace
+    list; at 70000 (1094 items of 64 tokens, all at the maximum) the
+    full-cache decode lists more items than fit on chip and takes the
+    chunked path.  bf16 runs the matrix-core gather, fp32 the vector one."""
     from sparse_long_context_append_amd.runtime import DecodeSession
     import sparse_long_context_append_amd as ekv
     P, d = 16, 64
