@@ -36,18 +36,31 @@ template <typename T> __device__ __forceinline__ T load_or(const T* p, int i, in
   return i < n ? v : fill;
 }
 
-__device__ __forceinline__ int dec_len(const DecodeArgs& a, int b) {
-  const int L = a.seq_lens[b];
+// A stored length clamped to [0, max_pages * P].
+__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int L) {
   if (L < 0 || (long long)L > (long long)a.max_pages * a.page_size) return L < 0 ? 0 : a.max_pages * a.page_size;
   return L;
 }
 
+__device__ __forceinline__ int dec_len(const DecodeArgs& a, int b) { return clamp_len(a, a.seq_lens[b]); }
+
+// Number of page-list entries of a unit from its sequence's stored length
+// and its list's stored count (ignored without lists).
+__device__ __forceinline__ int unit_pages_of(const DecodeArgs& a, int L, int cnt) {
+  const int n_b = pages_of(clamp_len(a, L), a.page_size);
+  return a.sel ? min(max(cnt, 0), min(a.cap, n_b)) : n_b;
+}
+
+// The stored list count of unit u, read without a branch (the length of
+// sequence 0 stands in without lists).
+__device__ __forceinline__ int unit_count_raw(const DecodeArgs& a, int u) {
+  const int32_t* p = a.sel ? a.sel_count : a.seq_lens;
+  return p[a.sel ? (u >> a.sel_shift) : 0];
+}
+
 // Number of page-list entries of unit u = b * Hkv + g.
 __device__ __forceinline__ int unit_pages(const DecodeArgs& a, int u) {
-  const int b = u / a.n_kv_heads;
-  const int n_b = pages_of(dec_len(a, b), a.page_size);
-  if (!a.sel) return n_b;
-  return min(max(a.sel_count[u >> a.sel_shift], 0), min(a.cap, n_b));
+  return unit_pages_of(a, a.seq_lens[u / a.n_kv_heads], unit_count_raw(a, u));
 }
 
 __device__ __forceinline__ int unit_items(const DecodeArgs& a, int u) {
@@ -206,11 +219,18 @@ struct UnitWalk {
 template <int SUB>
 __device__ __forceinline__ int unit_walk(const DecodeArgs& a, UnitWalk* uw) {
   const int lane = threadIdx.x & 63, units = a.batch * a.n_kv_heads;
+  int len[8], cnt[8];  // every load first (the last unit stands in past the end)
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int u = min(8 * lane + k, units - 1);
+    len[k] = a.seq_lens[u / a.n_kv_heads];
+    cnt[k] = unit_count_raw(a, u);
+  }
   int sum = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const int u = 8 * lane + k;
-    uw->sup[k] = u < units ? (unit_items(a, u) + SUB - 1) / SUB : 0;
+    const int items = (int)(((long long)unit_pages_of(a, len[k], cnt[k]) * a.page_size + kItemTokens - 1) / kItemTokens);
+    uw->sup[k] = 8 * lane + k < units ? (items + SUB - 1) / SUB : 0;
     sum += uw->sup[k];
   }
   uw->incl = wave_incl_scan(sum);
