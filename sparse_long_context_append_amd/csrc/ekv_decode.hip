@@ -26,6 +26,8 @@ constexpr int kDecThreads = 256;
 constexpr int kTauThreads = 256;
 constexpr int kTauItemChunk = 1024;
 constexpr int kCollectU = 16;  // items per wave per on-chip collection round
+constexpr int kVRows = 8;      // V rows in flight per thread in the weighted sum
+constexpr int kSolveBatch = 8; // scores loaded at once per thread in a threshold pass
 
 // p[i] for i < n, else `fill`, read from p[min(i, n - 1)] (p[0] when n is
 // 0, which must be readable) without a branch: guarded loads written this
@@ -570,17 +572,13 @@ template <int AK> __device__ __forceinline__ double entmax_pow(double d, double 
   return pow(d, beta);
 }
 
-template <bool WAVE, typename T> __device__ __forceinline__ T red_sum(T v, T* red) {
-  return WAVE ? wave_sum(v) : block_sum(v, red);
-}
-template <bool WAVE, typename T> __device__ __forceinline__ T red_min(T v, T* red) {
-  return WAVE ? wave_min(v) : block_min(v, red);
-}
-
 // Exact threshold of the N candidate scores xs (all threads of the calling
-// wave, or of the block, take part; every one gets the result).
+// wave, or of the block, take part; every one gets the result).  Other
+// alpha, whole block: when the fp32 steps end, the scores that can still
+// matter are copied to prune_buf (room for prune_cap) if they fit there.
 template <bool WAVE, int AK>
-__device__ double solve_threshold(const float* xs, int N, double m, double thr, float alpha_f, double* redd) {
+__device__ double solve_threshold(const float* xs, int N, double m, double thr, float alpha_f, double* redd,
+                                  float* prune_buf = nullptr, int prune_cap = 0) {
   const int idx = WAVE ? (threadIdx.x & 63) : threadIdx.x;
   const int stride = WAVE ? kWave : blockDim.x;
   constexpr bool sparsemax = AK == 0, ent15 = AK == 1;
@@ -593,24 +591,49 @@ __device__ double solve_threshold(const float* xs, int N, double m, double thr, 
   for (int it = 0; it < 4096; ++it) {
     tau = t;  // fallback if the iteration cap is ever reached
     double s1 = 0.0, s2 = 0.0, f = 0.0, fd = 0.0, xmin = INFINITY, cnt = 0.0;
-    for (int i = idx; i < N; i += stride) {
-      const double x = xs[i];
-      if (x > t) {
-        const double y = x - m, d = x - t;
-        cnt += 1.0; s1 += y; s2 += y * y; xmin = fmin(xmin, x);
-        const double pw = AK == 2 && coarse
-                              ? (double)__builtin_amdgcn_exp2f(beta_f * __builtin_amdgcn_logf((float)d))
-                              : entmax_pow<AK>(d, beta);
-        f += pw;
-        fd += sparsemax ? 1.0 : (ent15 ? 2.0 * d : beta * pw / d);
+    // kSolveBatch scores per thread loaded at once (the list may be in
+    // global memory), then taken in the same order as one at a time
+    for (int i0 = idx; i0 < N; i0 += kSolveBatch * stride) {
+      float xb[kSolveBatch];
+#pragma unroll
+      for (int u = 0; u < kSolveBatch; ++u) xb[u] = load_or(xs, i0 + u * stride, N, -INFINITY);
+#pragma unroll
+      for (int u = 0; u < kSolveBatch; ++u) {
+        const double x = xb[u];
+        if (x > t) {
+          const double y = x - m, d = x - t;
+          cnt += 1.0; s1 += y; s2 += y * y; xmin = fmin(xmin, x);
+          const double pw = AK == 2 && coarse
+                                ? (double)__builtin_amdgcn_exp2f(beta_f * __builtin_amdgcn_logf((float)d))
+                                : entmax_pow<AK>(d, beta);
+          f += pw;
+          fd += sparsemax ? 1.0 : (ent15 ? 2.0 * d : beta * pw / d);
+        }
       }
     }
-    cnt = red_sum<WAVE>(cnt, redd);
-    s1 = red_sum<WAVE>(s1, redd);
-    s2 = red_sum<WAVE>(s2, redd);
-    f = red_sum<WAVE>(f, redd);
-    fd = red_sum<WAVE>(fd, redd);
-    xmin = red_min<WAVE>(xmin, redd);
+    if (WAVE) {
+      cnt = wave_sum(cnt);
+      s1 = wave_sum(s1);
+      s2 = wave_sum(s2);
+      f = wave_sum(f);
+      fd = wave_sum(fd);
+      xmin = wave_min(xmin);
+    } else if (AK == 2) {  // (other alpha needs neither the moments nor xmin)
+      double v[3] = {cnt, f, fd};
+      block_sums<3>(v, redd);
+      cnt = v[0];
+      f = v[1];
+      fd = v[2];
+    } else {  // the sums in one reduction (same order as one at a time)
+      double v[5] = {cnt, s1, s2, f, fd};
+      block_sums<5>(v, redd);
+      cnt = v[0];
+      s1 = v[1];
+      s2 = v[2];
+      f = v[3];
+      fd = v[4];
+      xmin = block_min(xmin, redd);
+    }
     if (cnt == 0.0) { tau = t_prev; break; }  // only reachable through rounding
     t_prev = t;
     if (sparsemax || ent15) {
@@ -639,7 +662,41 @@ __device__ double solve_threshold(const float* xs, int N, double m, double thr, 
       tau = t;
       const double size = fabs(step), scale_t = fmax(1.0, fabs(t));
       if (coarse) {
-        if (size <= 1e-6 * scale_t) coarse = false;
+        if (size <= 1e-6 * scale_t) {
+          coarse = false;
+          if (!WAVE && AK == 2 && prune_buf) {
+            // t is now within about 1e-6 of tau and the fp64 steps stay
+            // there: a score at or below cut = t - 1e-4 max(1, |t|) adds
+            // nothing to any later pass, so the others are listed apart
+            // (in order: contiguous ranges, one scan), when they fit
+            const double cut = t - 1e-4 * scale_t;
+            const int E = (N + stride - 1) / stride;
+            const int e0 = min(idx * E, N), e1 = min(e0 + E, N);
+            int c = 0;
+            for (int i0 = e0; i0 < e1; i0 += kSolveBatch) {
+              float xb[kSolveBatch];
+#pragma unroll
+              for (int u = 0; u < kSolveBatch; ++u) xb[u] = load_or(xs, i0 + u, e1, -INFINITY);
+#pragma unroll
+              for (int u = 0; u < kSolveBatch; ++u) c += (double)xb[u] > cut;
+            }
+            int total;
+            int pos = block_exclusive_scan(c, reinterpret_cast<int*>(redd), &total);
+            if (total <= prune_cap) {
+              for (int i0 = e0; i0 < e1; i0 += kSolveBatch) {
+                float xb[kSolveBatch];
+#pragma unroll
+                for (int u = 0; u < kSolveBatch; ++u) xb[u] = load_or(xs, i0 + u, e1, -INFINITY);
+#pragma unroll
+                for (int u = 0; u < kSolveBatch; ++u)
+                  if ((double)xb[u] > cut) prune_buf[pos++] = xb[u];
+              }
+              __syncthreads();
+              xs = prune_buf;
+              N = total;
+            }
+          }
+        }
       } else if (size <= 1e-15 * scale_t || it > 4000) {
         break;
       }
@@ -719,11 +776,14 @@ __device__ double solve_pairwise(const float* xs, int N, double m, float alpha_f
   return t;
 }
 
-// On-chip scratch of the threshold stage (one instance per block).
-struct TauSmem {
-  float lx[kLdsCands];
-  int lt[kLdsCands];
-  int lr[kLdsCands];
+// On-chip scratch of the threshold stage (one instance per block), with room
+// for CAP candidates: kLdsCands, or kLdsCandsBig (about 115 KB) when every
+// block of the launch has a compute unit of its own anyway.
+constexpr int kLdsCandsBig = 8192;
+template <int CAP> struct TauSmem {
+  float lx[CAP];
+  int lt[CAP];
+  int lr[CAP];
   int s_pre[kTauItemChunk + 1];
   int s_item[kTauItemChunk];
   int s_tab[2][65];  // per-item kept counts of one collection round, their offsets
@@ -738,8 +798,8 @@ struct TauSmem {
 
 // Threshold, support and output of query head h of sequence b from the
 // candidate lists of its unit; the whole block takes part.
-template <int DT, int D, int AK>
-__device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
+template <int DT, int D, int AK, int CAP>
+__device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm) {
   using E = Elem<DT>;
   const int tid = threadIdx.x;
   const int G = a.group, g = h / G, Hkv = a.n_kv_heads, P = a.page_size;
@@ -759,30 +819,42 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
   float (*vpart)[D] = reinterpret_cast<float (*)[D]>(sm.vpart);
   __syncthreads();  // sm may still be in use by the caller
 
-  const int n_items = unit_items(a, u);
-  float* out = a.out + bh * D;
   const int32_t* icnt = a.item_cnt + bh * a.max_items;
   const float* imax = a.item_max + bh * a.max_items;
   const float* ilb = a.item_lb + bh * a.max_items;
+  // the first IPT * kTauThreads items' records are requested before the
+  // unit's size is known (indices clamped to the unit's item slots, the
+  // values past the unit's items masked once it is)
+  constexpr int IPT = 4;  // items per thread when n_items <= 1024
+  int loc[IPT];
+  float lmx[IPT], lbv[IPT];
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const int jj = min(IPT * threadIdx.x + i, a.max_items - 1);
+    loc[i] = icnt[jj];
+    lmx[i] = imax[jj];
+    lbv[i] = ilb[jj];
+  }
+  const int n_items = unit_items(a, u);
+  float* out = a.out + bh * D;
   const float* cx = a.cand_x + bh * tok_per_bh;
   const int32_t* ct = a.cand_t + bh * tok_per_bh;
   const int32_t* cr = a.cand_r + bh * tok_per_bh;
 
   // ---- item counts and maxima (one round of loads) ----
-  constexpr int IPT = 4;  // items per thread when n_items <= 1024
   constexpr int RPT = 16;  // raw candidates per thread per round of the workspace path
   const int tid_w = tid >> 6;
   const bool few_items = n_items <= IPT * kTauThreads;
-  int loc[IPT];
-  float lmx[IPT];
   float lmax = -INFINITY, llb = -INFINITY;
   if (few_items) {
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
-      const int jj = IPT * tid + i;
-      loc[i] = load_or(icnt, jj, n_items, 0);
-      lmx[i] = load_or(imax, jj, n_items, -INFINITY);
-      llb = fmaxf(llb, load_or(ilb, jj, n_items, -INFINITY));
+      if (IPT * tid + i >= n_items) {
+        loc[i] = 0;
+        lmx[i] = -INFINITY;
+        lbv[i] = -INFINITY;
+      }
+      llb = fmaxf(llb, lbv[i]);
       lmax = fmaxf(lmax, lmx[i]);
     }
   } else {
@@ -859,7 +931,7 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
   // One wave per item, lane r reading the item's candidate r, so a wave's
   // loads are contiguous; kCollectU items per wave per round, and one wave
   // scans the round's 4 kCollectU per-item counts.  False, with the list
-  // abandoned, once it would exceed kLdsCands.
+  // abandoned, once it would exceed CAP.
   auto collect_lds = [&](int n_list, int& N) -> bool {
     constexpr int U = kCollectU;
     const int lane = tid & 63;
@@ -894,7 +966,7 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
       }
       __syncthreads();
       const int n_end = sm.s_tab[1][64];
-      if (n_end > kLdsCands) return false;
+      if (n_end > CAP) return false;
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         if ((mk[j] >> lane) & 1ull) {
@@ -1077,7 +1149,7 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
     }
     if (!done) {
       N = run;
-      in_lds = N <= kLdsCands;
+      in_lds = N <= CAP;
       wait_mem();  // this thread's list entries are written before others read them
       __syncthreads();
       if (in_lds)
@@ -1104,36 +1176,106 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
     __syncthreads();
     tau = s_tau;
   } else {
-    tau = solve_threshold<false, AK>(xs, N, m, thr, a.alpha, redd);
+    tau = solve_threshold<false, AK>(xs, N, m, thr, a.alpha, redd, sm.vpart, 2048);  // vpart is free until the output
   }
   const double beta = 1.0 / ((double)a.alpha - 1.0);
 
   // ---- support, weights, compaction in place (p replaces x) ----
   double ps = 0.0;
   int nsup = 0;
-  for (int i0 = 0; i0 < N; i0 += kTauThreads) {
-    const int i = i0 + tid;
-    float x = 0.f;
-    int tok = 0, row = 0;
-    bool in = false;
-    if (i < N) { x = xs[i]; tok = ts[i]; row = rs[i]; in = (double)x > tau; }
-    double p = 0.0;
-    if (in) {
-      const double d = (double)x - tau;
-      p = entmax_pow<AK>(d, beta);
+  auto emit = [&](int pos, double p, int tok) {
+    if (a.support_idx && pos < a.support_cap) a.support_idx[bh * a.support_cap + pos] = tok;
+    if (a.support_p && pos < a.support_cap) a.support_p[bh * a.support_cap + pos] = (float)p;
+  };
+  if (in_lds) {
+    // on chip (N <= CAP, at most EW per thread): thread t holds the
+    // contiguous candidates [t E, t E + E) in registers, one scan places its
+    // kept ones
+    constexpr int EW = CAP / kTauThreads;
+    static_assert(CAP % kTauThreads == 0, "candidates per thread");
+    const int E = (N + kTauThreads - 1) / kTauThreads;
+    const int e0 = min(tid * E, N), e1 = min(e0 + E, N);
+    float xv[EW];
+    int tv[EW], rv[EW];
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < EW; ++k) {
+      const int i = min(e0 + k, CAP - 1);  // in the LDS list; masked below
+      xv[k] = xs[i];
+      tv[k] = ts[i];
+      rv[k] = rs[i];
+      if (!(e0 + k < e1)) xv[k] = -INFINITY;
+      c += (double)xv[k] > tau;
+    }
+    int pos = block_exclusive_scan(c, redi, &nsup);  // every read above is done
+#pragma unroll
+    for (int k = 0; k < EW; ++k) {
+      if ((double)xv[k] > tau) {
+        if (AK == 2) {
+          xs[pos] = xv[k];  // the power is taken below, over the support only
+        } else {
+          const double p = entmax_pow<AK>((double)xv[k] - tau, beta);
+          ps += p;
+          xs[pos] = (float)p;
+          emit(pos, p, tv[k]);
+        }
+        ts[pos] = tv[k];
+        rs[pos] = rv[k];
+        ++pos;
+      }
+    }
+    __syncthreads();
+  } else {
+    // in the workspace: rounds of kSolveBatch contiguous candidates per
+    // thread (loaded at once), one scan per round; a kept candidate moves to
+    // a position at or below its own, so no write reaches a later round's
+    constexpr int WB = kSolveBatch;
+    for (int i0 = 0; i0 < N; i0 += WB * kTauThreads) {
+      const int e0 = i0 + WB * tid;
+      float xv[WB];
+      int tv[WB], rv[WB];
+      int c = 0;
+#pragma unroll
+      for (int k = 0; k < WB; ++k) {
+        xv[k] = load_or(xs, e0 + k, N, -INFINITY);
+        tv[k] = load_or(ts, e0 + k, N, 0);
+        rv[k] = load_or(rs, e0 + k, N, 0);
+      }
+#pragma unroll
+      for (int k = 0; k < WB; ++k) c += (double)xv[k] > tau;
+      int tot;
+      int pos = nsup + block_exclusive_scan(c, redi, &tot);  // every read of the round is done
+#pragma unroll
+      for (int k = 0; k < WB; ++k) {
+        if ((double)xv[k] > tau) {
+          if (AK == 2) {
+            xs[pos] = xv[k];  // the power is taken below, over the support only
+          } else {
+            const double p = entmax_pow<AK>((double)xv[k] - tau, beta);
+            ps += p;
+            xs[pos] = (float)p;
+            emit(pos, p, tv[k]);
+          }
+          ts[pos] = tv[k];
+          rs[pos] = rv[k];
+          ++pos;
+        }
+      }
+      nsup += tot;
+      wait_mem();  // workspace list entries are read by other threads next
+      __syncthreads();
+    }
+  }
+  if (AK == 2) {
+    // other alpha: the fp64 powers over the compacted support, every lane
+    // busy (p replaces x)
+    for (int i = tid; i < nsup; i += kTauThreads) {
+      const double p = entmax_pow<AK>((double)xs[i] - tau, beta);
       ps += p;
+      xs[i] = (float)p;
+      emit(i, p, ts[i]);
     }
-    int tot;
-    const int pos = nsup + block_exclusive_scan(in ? 1 : 0, redi, &tot);  // syncs before writing
-    if (in) {
-      xs[pos] = (float)p;
-      ts[pos] = tok;
-      rs[pos] = row;
-      if (a.support_idx && pos < a.support_cap) a.support_idx[bh * a.support_cap + pos] = tok;
-      if (a.support_p && pos < a.support_cap) a.support_p[bh * a.support_cap + pos] = (float)p;
-    }
-    nsup += tot;
-    if (!in_lds) wait_mem();  // workspace list entries are read by other threads next
+    if (!in_lds) wait_mem();  // read by other threads next
     __syncthreads();
   }
   ps = block_sum(ps, redd);
@@ -1143,16 +1285,30 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  for (int s = rr; s < nsup; s += RPB) {
-    const int row = rs[s];
-    const float p = xs[s];
-    const int phys = row >> __builtin_ctz(P), slot = row & (P - 1);  // P is a power of two
-    const char* vrow = reinterpret_cast<const char*>(a.v) +
-                       ((((size_t)phys * a.hkv_mem + (g >> a.kv_shift)) * P + slot) * D + (size_t)sub * EPL) * E::kBytes;
-    float f[EPL];
-    E::unpack(ldg16(vrow), f);
+  // kVRows rows in flight per thread: every load of a round first (the last
+  // row stands in past the end), then the products in row order
+  for (int s0 = rr; s0 < nsup; s0 += kVRows * RPB) {
+    uint4 vv[kVRows];
+    float pv[kVRows];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, f[e], acc[e]);
+    for (int i = 0; i < kVRows; ++i) {
+      const int s = min(s0 + i * RPB, nsup - 1);
+      const int row = rs[s];
+      pv[i] = xs[s];
+      const int phys = row >> __builtin_ctz(P), slot = row & (P - 1);  // P is a power of two
+      const char* vrow = reinterpret_cast<const char*>(a.v) +
+                         ((((size_t)phys * a.hkv_mem + (g >> a.kv_shift)) * P + slot) * D + (size_t)sub * EPL) * E::kBytes;
+      vv[i] = ldg16(vrow);
+    }
+#pragma unroll
+    for (int i = 0; i < kVRows; ++i) {
+      if (s0 + i * RPB < nsup) {
+        float f[EPL];
+        E::unpack(vv[i], f);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pv[i], f[e], acc[e]);
+      }
+    }
   }
 #pragma unroll
   for (int e = 0; e < EPL; ++e) vpart[rr][sub * EPL + e] = acc[e];
@@ -1169,10 +1325,10 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem& sm) {
   }
 }
 
-template <int DT, int D, int AK>
+template <int DT, int D, int AK, int CAP>
 __global__ __launch_bounds__(kTauThreads) void tau_v_kernel(DecodeArgs a) {
-  __shared__ TauSmem sm;
-  tau_v_block<DT, D, AK>(a, blockIdx.y, blockIdx.x, sm);
+  __shared__ TauSmem<CAP> sm;
+  tau_v_block<DT, D, AK, CAP>(a, blockIdx.y, blockIdx.x, sm);
 }
 
 // The balanced gather's grid: as many blocks as can be resident at once
@@ -1187,12 +1343,12 @@ static int resident_grid(int cus, int cap) {
   return per_cu > 0 ? (per_cu * cus < cap ? per_cu * cus : cap) : cap;
 }
 
+
 template <int DT, int D>
-static hipError_t decode_dispatch(const DecodeArgs& a, int slots, int bal_blocks, hipStream_t s) {
+static hipError_t decode_dispatch(const DecodeArgs& a, int slots, int bal_blocks, int cus, hipStream_t s) {
   const dim3 g1(slots, a.batch * a.n_kv_heads), b1(kDecThreads);
   const bool mfma = DT == EKV_BF16;
   if (mfma && bal_blocks > 0) {
-    const int cus = bal_blocks / 4;  // bal_blocks: four per compute unit
 #define EKV_BAL(GG)                                                                               \
   hipLaunchKernelGGL((gather_mfma_kernel<D, GG, 4, true>),                                        \
                      dim3(resident_grid<gather_mfma_kernel<D, GG, 4, true>>(cus, bal_blocks)), b1, 0, s, a, 0)
@@ -1222,9 +1378,16 @@ static hipError_t decode_dispatch(const DecodeArgs& a, int slots, int bal_blocks
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 g2(a.n_q_heads, a.batch), b2(kTauThreads);
-  if (a.alpha == 2.0f) hipLaunchKernelGGL((tau_v_kernel<DT, D, 0>), g2, b2, 0, s, a);
-  else if (a.alpha == 1.5f) hipLaunchKernelGGL((tau_v_kernel<DT, D, 1>), g2, b2, 0, s, a);
-  else hipLaunchKernelGGL((tau_v_kernel<DT, D, 2>), g2, b2, 0, s, a);
+  if (a.alpha == 2.0f) hipLaunchKernelGGL((tau_v_kernel<DT, D, 0, kLdsCands>), g2, b2, 0, s, a);
+  else if (a.alpha == 1.5f) hipLaunchKernelGGL((tau_v_kernel<DT, D, 1, kLdsCands>), g2, b2, 0, s, a);
+  // other alpha (supports of hundreds of tokens, thousands of candidates):
+  // the larger list when every (sequence, query head) block has a compute
+  // unit of its own, where it costs no occupancy (it costs about 2 us per
+  // block in the weights and output phases, which the smaller supports of
+  // alpha 1.5 and 2 do not win back)
+  else if ((long long)a.batch * a.n_q_heads <= cus)
+    hipLaunchKernelGGL((tau_v_kernel<DT, D, 2, kLdsCandsBig>), g2, b2, 0, s, a);
+  else hipLaunchKernelGGL((tau_v_kernel<DT, D, 2, kLdsCands>), g2, b2, 0, s, a);
   return hipGetLastError();
 }
 
@@ -1248,11 +1411,12 @@ hipError_t launch_decode(const DecodeArgs& a, int target_blocks, hipStream_t s) 
   if (slots < 1) slots = 1;
   if (slots > 65535) slots = 65535;
   const int bal = mfma && units >= 64 && units <= 512 ? target_blocks : 0;
+  const int cus = target_blocks / 4;  // target_blocks: four per compute unit
   if (a.kv_dtype == EKV_BF16)
-    return a.head_dim == 128 ? decode_dispatch<EKV_BF16, 128>(a, (int)slots, bal, s)
-                             : decode_dispatch<EKV_BF16, 64>(a, (int)slots, bal, s);
-  return a.head_dim == 128 ? decode_dispatch<EKV_F32, 128>(a, (int)slots, 0, s)
-                           : decode_dispatch<EKV_F32, 64>(a, (int)slots, 0, s);
+    return a.head_dim == 128 ? decode_dispatch<EKV_BF16, 128>(a, (int)slots, bal, cus, s)
+                             : decode_dispatch<EKV_BF16, 64>(a, (int)slots, bal, cus, s);
+  return a.head_dim == 128 ? decode_dispatch<EKV_F32, 128>(a, (int)slots, 0, cus, s)
+                           : decode_dispatch<EKV_F32, 64>(a, (int)slots, 0, cus, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -267,45 +267,62 @@ def test_topk_covering_every_page_equals_dense():
     check_step(spec, rs, q, all_units(spec))
 
 
-@pytest.mark.parametrize("kv", ["f32", "bf16"])
-@pytest.mark.parametrize("L", [1500, 5000, 70000])
-@pytest.mark.parametrize("alpha", [1.5, 2.0])
-def test_all_keys_equal_large_support(alpha, L, kv):
-    """Every key identical: every page ties (lowest ids win) and every token
-    is in the support.  1500 tokens fit the on-chip candidate list; 5000
-    overflow it, so the listed items' candidates go through the workspace
-    list; at 70000 (1094 items of 64 tokens, all at the maximum) the
-    full-cache decode lists more items than fit on chip and takes the
-    chunked path.  bf16 runs the matrix-core gather, fp32 the vector one."""
+def _all_keys_equal_case(alpha, L, kv, batch=1, hq=2):
+    """Every key identical, in `batch` sequences of L tokens with hq query
+    heads on one KV head: every page ties (lowest ids win) and every token
+    is in the support, with uniform weights."""
     from sparse_long_context_append_amd.runtime import DecodeSession
     import sparse_long_context_append_amd as ekv
     P, d = 16, 64
     npg = -(-L // P)
-    table = np.arange(npg, dtype=np.int32)[None]
+    table = np.arange(batch * npg, dtype=np.int32).reshape(batch, npg)
     dt = ekv.EKV_F32 if kv == "f32" else ekv.EKV_BF16
     tdt = torch.float32 if kv == "f32" else torch.bfloat16
-    sess = DecodeSession(batch=1, n_kv_heads=1, n_q_heads=2, head_dim=d, page_size=P, kv_dtype=dt,
-                         n_phys_pages=npg, page_table=table, cap=npg)
+    sess = DecodeSession(batch=batch, n_kv_heads=1, n_q_heads=hq, head_dim=d, page_size=P, kv_dtype=dt,
+                         n_phys_pages=batch * npg, page_table=table, cap=npg)
     rng = np.random.default_rng(7)
     k = np.repeat(rng.standard_normal((1, d)).astype(np.float32), L, axis=0)
     v = rng.standard_normal((L, d)).astype(np.float32)
-    kd = torch.from_numpy(k[None, :, None]).cuda().to(tdt)
-    vd = torch.from_numpy(v[None, :, None]).cuda().to(tdt)
+    kd = torch.from_numpy(k[None, :, None]).cuda().to(tdt).expand(batch, L, 1, d).contiguous()
+    vd = torch.from_numpy(v[None, :, None]).cuda().to(tdt).expand(batch, L, 1, d).contiguous()
     sess.append(kd, vd)
-    q = torch.from_numpy(rng.standard_normal((1, 2, d)).astype(np.float32)).cuda()
+    q = torch.from_numpy(rng.standard_normal((batch, hq, d)).astype(np.float32)).cuda()
     sess.select(q, policy=ekv.EKV_SELECT_BBOX_TOPK, alpha=alpha, scale=0.125, top_k=5)
     torch.cuda.synchronize()
-    assert sess.sel_count.item() == 5
-    assert sess.sel[0, 0, :5].tolist() == [0, 1, 2, 3, 4]
+    assert np.all(sess.sel_count.cpu().numpy() == 5)
+    assert np.all(sess.sel[:, :, :5].cpu().numpy() == np.arange(5))
     v_stored = vd[0, :, 0].float().cpu().numpy().astype(np.float64)
     for sparse, n in ((True, 5 * P), (False, L)):
         sess.decode(q, alpha=alpha, scale=0.125, sparse=sparse)
         torch.cuda.synchronize()
         assert np.all(sess.support_count.cpu().numpy() == n)
         np.testing.assert_allclose(sess.psum.cpu().numpy(), 1.0, atol=1e-5)
-        np.testing.assert_allclose(sess.out.cpu().numpy()[0], np.tile(v_stored[:n].mean(axis=0), (2, 1)),
-                                   atol=2e-3)
+        want = np.broadcast_to(v_stored[:n].mean(axis=0), (batch, hq, d))
+        np.testing.assert_allclose(sess.out.cpu().numpy(), want, atol=2e-3)
     assert sess.device_status() == 0
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16"])
+@pytest.mark.parametrize("L", [1500, 5000, 9000, 70000])
+@pytest.mark.parametrize("alpha", [1.5, 2.0, 1.3])
+def test_all_keys_equal_large_support(alpha, L, kv):
+    """Two (sequence, query head) blocks.  At alpha 1.5 and 2 the threshold
+    stage keeps up to 4096 candidates on chip: 1500 tokens fit, 5000 and
+    9000 overflow the list, so the listed items' candidates go through the
+    workspace list.  At other alpha, with no more blocks than compute units,
+    the list holds 8192: 1500 and 5000 fit, 9000 overflow.  At 70000 (1094
+    items of 64 tokens, all at the maximum) the full-cache decode lists more
+    items than fit on chip and takes the chunked path.  bf16 runs the
+    matrix-core gather, fp32 the vector one."""
+    _all_keys_equal_case(alpha, L, kv)
+
+
+@pytest.mark.parametrize("alpha", [1.5, 1.3])
+def test_all_keys_equal_many_blocks(alpha):
+    """33 sequences of 8 query heads: 264 threshold blocks, more than the
+    device's 256 compute units, so the on-chip list holds 4096 candidates
+    at any alpha, which the full-cache decode of 5000 tokens overflows."""
+    _all_keys_equal_case(alpha, 5000, "bf16", batch=33, hq=8)
 
 
 def test_empty_and_single_token_sequences():
