@@ -217,9 +217,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_bbox_valu_kernel(SelectAr
 }
 
 // ---------------------------------------------------------------------------
-// Top-k.  One 1024-thread block per (KV head, sequence).  Thread t owns the
-// contiguous pages [t E, t E + E), E = ceil(n / 1024); keys stay in
-// registers when E <= 16 (up to 16384 pages), else are re-read from L2.
+// Top-k.  One 1024-thread block per (KV head, sequence).  With E > 0 thread
+// t owns the page slots [t E, t E + E) of the score row (E chosen on the host
+// from the table width, E * 1024 >= max_pages), and its keys stay in
+// registers; they are requested before the sequence length is known and the
+// slots at or past it are masked afterwards.  With E == 0 (more than 16384
+// pages) thread t owns ceil(n / 1024) pages and re-reads them from L2.
 // ---------------------------------------------------------------------------
 // Visit this thread's keys in page order: from registers (E > 0, loop fully
 // unrolled so the array stays in registers) or from memory (E == 0).
@@ -239,7 +242,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_bbox_valu_kernel(SelectAr
   }
 
 template <int E>  // keys per thread held in registers (0: read from memory)
-__device__ void topk_block(const SelectArgs& a, const float* s, int n_b, int k_eff, int32_t* out, int unit) {
+__device__ __forceinline__ void topk_block(const SelectArgs& a, const float* s, const uint32_t (&kin)[E > 0 ? E : 1], int n_b,
+                           int k_eff, int32_t* out, int unit) {
   constexpr int KE = E > 0 ? E : 1;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
   __shared__ uint32_t hist[2][256];
@@ -250,21 +254,8 @@ __device__ void topk_block(const SelectArgs& a, const float* s, int n_b, int k_e
   const int e0 = min(tid * per, n_b), e1 = min(e0 + per, n_b);
   const int cnt = e1 - e0;
   uint32_t keys[KE];
-  if (E > 0) {
-    // rows are 16-byte aligned and e0 is a multiple of 4: vector loads
 #pragma unroll
-    for (int i = 0; i < KE; i += 4) {
-      if (i + 4 <= cnt) {
-        const float4 v = *reinterpret_cast<const float4*>(s + e0 + i);
-        keys[i] = f2key(v.x); keys[(i + 1) % KE] = f2key(v.y);
-        keys[(i + 2) % KE] = f2key(v.z); keys[(i + 3) % KE] = f2key(v.w);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (i + q < KE) keys[i + q] = (i + q < cnt) ? f2key(s[e0 + i + q]) : 0u;
-      }
-    }
-  }
+  for (int i = 0; i < KE; ++i) keys[i] = kin[i];
   // bits shared by every key (AND and OR in one reduction) and cleared histograms
   uint32_t kand = 0xffffffffu, kor = 0u;
   EKV_FOR_KEYS(kand &= k; kor |= k;)
@@ -283,14 +274,18 @@ __device__ void topk_block(const SelectArgs& a, const float* s, int n_b, int k_e
     prefix = kand;  // every score equal: the k lowest page ids
     mask = 0xffffffffu;
   } else {
+    // Digits of up to 8 bits, the first one ending at the highest bit where
+    // the keys differ (the bits above it are common to all keys), so the
+    // first histogram spreads the keys over all its bins.
     const int top = 31 - __clz(diff);
-    const int start = (top / 8) * 8;
-    mask = (start + 8 >= 32) ? 0u : ~((1u << (start + 8)) - 1u);
+    mask = top >= 31 ? 0u : ~((2u << top) - 1u);
     prefix = kand & mask;
     int buf = 0;
-    for (int shift = start; shift >= 0; shift -= 8, buf ^= 1) {
+    for (int hi = top; hi >= 0; hi -= 8, buf ^= 1) {
+      const int shift = max(hi - 7, 0);
+      const uint32_t dmask = (2u << (hi - shift)) - 1u;  // hi - shift <= 7
       uint32_t* hb = hist[buf];
-      EKV_FOR_KEYS(if ((k & mask) == prefix) atomicAdd(&hb[(k >> shift) & 255u], 1u);)
+      EKV_FOR_KEYS(if ((k & mask) == prefix) atomicAdd(&hb[(k >> shift) & dmask], 1u);)
       __syncthreads();
       if (w == 0) {
         const uint32_t c0 = hb[4 * lane], c1 = hb[4 * lane + 1], c2 = hb[4 * lane + 2], c3 = hb[4 * lane + 3];
@@ -320,7 +315,7 @@ __device__ void topk_block(const SelectArgs& a, const float* s, int n_b, int k_e
       }
       __syncthreads();
       prefix |= sh_digit[buf] << shift;
-      mask |= 0xffu << shift;
+      mask |= dmask << shift;
       rem -= (int)sh_above[buf];
       // the chosen bucket holds exactly the keys still wanted: all of it is
       // taken, and its lower digits need not be resolved
@@ -344,30 +339,44 @@ __device__ void topk_block(const SelectArgs& a, const float* s, int n_b, int k_e
 }
 #undef EKV_FOR_KEYS
 
+template <int E>
 __global__ __launch_bounds__(kSelThreads) void topk_kernel(SelectArgs a) {
+  constexpr int KE = E > 0 ? E : 1;
   const int g = blockIdx.x, b = blockIdx.y;
   const int unit = b * a.n_kv_heads + g;
   const int tid = threadIdx.x;
   const int P = a.page_size;
+  const float* s = a.scores + (size_t)unit * a.score_stride;
+  // the score row's slots, requested with the length: the stride is a
+  // multiple of 4 and the row 16-byte aligned, so an index clamped to the
+  // row's last vector keeps every load inside the row
+  uint32_t keys[KE];
+  if (E > 0) {
+#pragma unroll
+    for (int i = 0; i < KE; i += 4) {
+      const int at = min(tid * KE + i, a.score_stride - 4);
+      const float4 v = *reinterpret_cast<const float4*>(s + at);
+      keys[i] = f2key(v.x); keys[(i + 1) % KE] = f2key(v.y);
+      keys[(i + 2) % KE] = f2key(v.z); keys[(i + 3) % KE] = f2key(v.w);
+    }
+  } else {
+    keys[0] = 0u;  // unused: the keys are read from memory
+  }
   const int L = clamp_len(a.seq_lens[b], a.max_pages, P, a.status);
   const int n_b = pages_of(L, P);
   const int k_eff = min(a.top_k, n_b);
-  const float* s = a.scores + (size_t)unit * a.score_stride;
   int32_t* out = a.sel + (size_t)unit * a.cap;
   if (k_eff >= n_b) {
     for (int p = tid; p < n_b; p += blockDim.x) out[p] = p;
     if (tid == 0) a.sel_count[unit] = n_b;
     return;
   }
-  const int per = (n_b + kSelThreads - 1) / kSelThreads;
   if (n_b > 65535) {  // packed 16-bit counts would overflow: the host rejects such shapes
     set_status(a.status, EKV_DEV_OVERFLOW);
     if (tid == 0) a.sel_count[unit] = 0;
     return;
   }
-  if (per <= 4) topk_block<4>(a, s, n_b, k_eff, out, unit);
-  else if (per <= 16) topk_block<16>(a, s, n_b, k_eff, out, unit);
-  else topk_block<0>(a, s, n_b, k_eff, out, unit);
+  topk_block<E>(a, s, keys, n_b, k_eff, out, unit);
 }
 
 // ---------------------------------------------------------------------------
@@ -1012,7 +1021,11 @@ hipError_t launch_score_bbox(const SelectArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_topk(const SelectArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3(a.n_kv_heads, a.batch), dim3(kSelThreads), 0, s, a);
+  const dim3 grid(a.n_kv_heads, a.batch);
+  const int per = (a.max_pages + kSelThreads - 1) / kSelThreads;
+  if (per <= 4) hipLaunchKernelGGL((topk_kernel<4>), grid, dim3(kSelThreads), 0, s, a);
+  else if (per <= 16) hipLaunchKernelGGL((topk_kernel<16>), grid, dim3(kSelThreads), 0, s, a);
+  else hipLaunchKernelGGL((topk_kernel<0>), grid, dim3(kSelThreads), 0, s, a);
   return hipGetLastError();
 }
 
