@@ -24,7 +24,8 @@ constexpr int kBboxPagesPerBlock = 64;   // 16 pages per wave
 constexpr int kGaussPagesPerBlock = 64;  // 8 lane groups per wave, 2 pages each
 constexpr int kSelThreads = 1024;
 constexpr int kTauHatThreads = 1024;
-constexpr int kTauHatPPT = 16;           // pages per thread held in registers (n_b <= 16384)
+// pages per thread held in registers: as many as the live list holds
+// (n_b <= LIVE), so the 8192-page instance stays within two blocks per CU
 constexpr int kTauHatLive = 8192;        // pages alive at the start point kept in LDS
 constexpr int kTauHatLiveBig = 16384;    // the same for sequences of more than 8192 pages (one block per CU)
 
@@ -754,9 +755,12 @@ __device__ void gauss_floor_unit(const SelectArgs& a, int b, int g, int n_b, int
 
 // GEN: alpha other than 1.5 and 2 (a separate instance, so that the
 // quadrature's registers do not weigh on the closed-form one)
+// The closed-form instance with the 8192-page list is held to 64 registers
+// so that two blocks share a compute unit (its LDS, 65 KB, allows two).
 template <int G, bool GEN, int LIVE>
-__global__ __launch_bounds__(kTauHatThreads) void tau_hat_kernel(SelectArgs a) {
-  constexpr int PPT = kTauHatPPT;
+__global__ __launch_bounds__(kTauHatThreads)
+__attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void tau_hat_kernel(SelectArgs a) {
+  constexpr int PPT = LIVE / kTauHatThreads;
   constexpr int NW = kTauHatThreads / kWave;
   const int h = blockIdx.x, b = blockIdx.y;
   const int g = h / G, unit = b * a.n_kv_heads + g;
