@@ -264,8 +264,10 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(BAL
   constexpr int KB = D / 32;
   constexpr int NH = (G + 3) / 4;  // 16-row operands (four heads each)
   __shared__ u32x4_t s_a[NH * KB][kWave];
-  __shared__ float s_max[NH][SUB][4][4];
-  __shared__ int s_cnt[NH][SUB][4][4];
+  // per-wave item maxima and kept counts, [head operand][item][head][wave]:
+  // a lane reads the four waves' values of its head in one 16-byte load
+  __shared__ float4 s_max[NH][SUB][4];
+  __shared__ int4 s_cnt[NH][SUB][4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int Hkv = a.n_kv_heads;
@@ -306,17 +308,19 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(BAL
   const int n_super = (ctx.n_items + SUB - 1) / SUB;
   RefPipe<SUB> nxt;  // the next super-item's references, in flight behind this one
   while (BAL || sj < n_super) {
+    // every lane loads (a lane without a token reads row 0 of the cache and
+    // zeroes the values), so the loads carry no branches and the first
+    // product waits only for its own item's keys
     u32x4_t bv[SUB][KB];
 #pragma unroll
     for (int s = 0; s < SUB; ++s) {
-      if (tr[s].phys >= 0) {
-        const uint16_t* row = reinterpret_cast<const uint16_t*>(a.k) +
-                              (((size_t)tr[s].phys * a.hkv_mem + (g >> a.kv_shift)) * a.page_size + tr[s].slot) * D + 8 * grp;
+      const bool has = tr[s].phys >= 0;
+      const size_t rowi = has ? ((size_t)tr[s].phys * a.hkv_mem + (g >> a.kv_shift)) * a.page_size + tr[s].slot : 0;
+      const uint16_t* row = reinterpret_cast<const uint16_t*>(a.k) + rowi * D + 8 * grp;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) bv[s][kb] = *reinterpret_cast<const u32x4_t*>(row + 32 * kb);
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) bv[s][kb] = u32x4_t{0u, 0u, 0u, 0u};
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + 32 * kb);
+        bv[s][kb] = has ? v : u32x4_t{0u, 0u, 0u, 0u};
       }
     }
     // the next super-item of this block, and its page-list round
@@ -347,7 +351,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(BAL
         x[hh][s] = tr[s].valid && 4 * hh + grp < G ? (c[0] + c[1]) + c[2] : -INFINITY;
         // per-head item maximum (the 16 lanes of one head share grp)
         const float m = group_reduce<16>(x[hh][s], [](float u, float v) { return fmaxf(u, v); });
-        if (col == 0) s_max[hh][s][w][grp] = m;
+        if (col == 0) reinterpret_cast<float*>(&s_max[hh][s][grp])[w] = m;
       }
     }
     // this super-item's token ids and rows, kept aside so that the next
@@ -379,8 +383,8 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(BAL
       msup[hh] = -INFINITY;
 #pragma unroll
       for (int s = 0; s < SUB; ++s) {
-        m[hh][s] = fmaxf(fmaxf(s_max[hh][s][0][grp], s_max[hh][s][1][grp]),
-                         fmaxf(s_max[hh][s][2][grp], s_max[hh][s][3][grp]));
+        const float4 mv = s_max[hh][s][grp];
+        m[hh][s] = fmaxf(fmaxf(mv.x, mv.y), fmaxf(mv.z, mv.w));
         msup[hh] = fmaxf(msup[hh], m[hh][s]);
       }
       lb[hh] = (double)msup[hh] - 1.0;
@@ -401,7 +405,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(BAL
         keep[hh][s] = hv && msup[hh] > -INFINITY && (double)x[hh][s] > lb[hh];
         const unsigned long long bal = __ballot(keep[hh][s]);
         bits[hh][s] = (uint32_t)(bal >> (16 * grp)) & 0xffffu;
-        if (col == 0) s_cnt[hh][s][w][grp] = __popc(bits[hh][s]);
+        if (col == 0) reinterpret_cast<int*>(&s_cnt[hh][s][grp])[w] = __popc(bits[hh][s]);
       }
     }
     if (has_next) refs_finish<SUB>(a, nxt, &ctx, tr);
@@ -415,12 +419,9 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(BAL
       for (int s = 0; s < SUB; ++s) {
         const int j = sj * SUB + s;
         if (j >= n_items_cur) break;
-        int off = 0, tot = 0;
-#pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
-          off += ww < w ? s_cnt[hh][s][ww][grp] : 0;
-          tot += s_cnt[hh][s][ww][grp];
-        }
+        const int4 cv = s_cnt[hh][s][grp];
+        const int off = (w > 0 ? cv.x : 0) + (w > 1 ? cv.y : 0) + (w > 2 ? cv.z : 0);
+        const int tot = (cv.x + cv.y) + (cv.z + cv.w);
         if (keep[hh][s]) {
           const int pos = off + __popc(bits[hh][s] & ((1u << col) - 1u));
           const size_t at = bh * tok_per_bh + (size_t)j * kItemTokens + pos;
