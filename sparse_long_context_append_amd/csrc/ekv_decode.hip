@@ -132,7 +132,9 @@ __device__ __forceinline__ void refs_list(const DecodeArgs& a, int u, int b, int
   for (int s = 0; s < SUB; ++s) {
     const long long T = (long long)(j0 + s) * kItemTokens + r;
     const int k = (int)(T >> __builtin_ctz(P));  // P is a power of two
-    rp.lp[s] = k < capk ? (a.sel ? a.sel[(size_t)(u >> a.sel_shift) * a.cap + k] : k) : -1;
+    // read from a clamped index and masked afterwards (no branch per load)
+    const int v = a.sel ? a.sel[(size_t)(u >> a.sel_shift) * a.cap + min(k, capk - 1)] : k;
+    rp.lp[s] = k < capk ? v : -1;
   }
   if (first) {
     rp.L = a.seq_lens[b];
@@ -143,8 +145,11 @@ __device__ __forceinline__ void refs_list(const DecodeArgs& a, int u, int b, int
 template <int SUB>
 __device__ __forceinline__ void refs_table(const DecodeArgs& a, RefPipe<SUB>& rp) {
 #pragma unroll
-  for (int s = 0; s < SUB; ++s)
-    rp.ph[s] = (rp.lp[s] >= 0 && rp.lp[s] < a.max_pages) ? a.page_table[(size_t)rp.b * a.max_pages + rp.lp[s]] : -1;
+  for (int s = 0; s < SUB; ++s) {
+    const bool in = rp.lp[s] >= 0 && rp.lp[s] < a.max_pages;
+    const int v = a.page_table[(size_t)rp.b * a.max_pages + (in ? rp.lp[s] : 0)];
+    rp.ph[s] = in ? v : -1;
+  }
 }
 
 template <int SUB>
