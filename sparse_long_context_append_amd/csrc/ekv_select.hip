@@ -24,8 +24,6 @@ constexpr int kBboxPagesPerBlock = 64;   // 16 pages per wave
 constexpr int kGaussPagesPerBlock = 64;  // 8 lane groups per wave, 2 pages each
 constexpr int kSelThreads = 1024;
 constexpr int kTauHatThreads = 1024;
-// pages per thread held in registers: as many as the live list holds
-// (n_b <= LIVE), so the 8192-page instance stays within two blocks per CU
 constexpr int kTauHatLive = 8192;        // pages alive at the start point kept in LDS
 constexpr int kTauHatLiveBig = 16384;    // the same for sequences of more than 8192 pages (one block per CU)
 
@@ -760,6 +758,8 @@ __device__ void gauss_floor_unit(const SelectArgs& a, int b, int g, int n_b, int
 template <int G, bool GEN, int LIVE>
 __global__ __launch_bounds__(kTauHatThreads)
 __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void tau_hat_kernel(SelectArgs a) {
+  // pages per thread held in registers: as many as the live list holds
+  // (n_b <= LIVE), which keeps the 8192-page instance within 64 registers
   constexpr int PPT = LIVE / kTauHatThreads;
   constexpr int NW = kTauHatThreads / kWave;
   const int h = blockIdx.x, b = blockIdx.y;
