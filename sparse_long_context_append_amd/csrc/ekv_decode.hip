@@ -880,8 +880,27 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
       }
     }
   }
-  const float mf = block_max(lmax, reinterpret_cast<float*>(redd));
-  const float lbf = block_max(llb, reinterpret_cast<float*>(redd));
+  // the largest item maximum and the largest item bound in one block
+  // reduction (one pair of barriers)
+  float mf, lbf;
+  {
+    constexpr int NWV = kTauThreads / kWave;
+    float* rf = reinterpret_cast<float*>(redd);  // 2 NWV floats
+    const float wm = wave_max(lmax), wl = wave_max(llb);
+    __syncthreads();
+    if ((tid & 63) == 0) {
+      rf[tid_w] = wm;
+      rf[NWV + tid_w] = wl;
+    }
+    __syncthreads();
+    mf = rf[0];
+    lbf = rf[NWV];
+#pragma unroll
+    for (int i = 1; i < NWV; ++i) {
+      mf = max(mf, rf[i]);
+      lbf = max(lbf, rf[NWV + i]);
+    }
+  }
   if (!(mf > -INFINITY)) {  // no pages, or every page invalid (flagged): empty result
     for (int e = tid; e < D; e += blockDim.x) out[e] = 0.f;
     if (tid == 0) {
