@@ -343,6 +343,18 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+// The same scan on unsigned words (sums wrap modulo 2^32, so several small
+// counts can share one word in disjoint bit fields).
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);
+  return v;
+}
+
 // Exclusive prefix sum over the block (blockDim.x multiple of 64, <= 1024);
 // `red` holds >= 17 ints.  Returns the exclusive prefix, *total the sum.
 __device__ inline int block_exclusive_scan(int v, int* red, int* total) {
@@ -352,6 +364,22 @@ __device__ inline int block_exclusive_scan(int v, int* red, int* total) {
   if (lane == 63) red[w] = inc;
   __syncthreads();
   int before = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    if (i < w) before += red[i];
+    tot += red[i];
+  }
+  *total = tot;
+  return before + inc - v;
+}
+
+// block_exclusive_scan on unsigned words (modulo 2^32); `red` holds >= 16.
+__device__ inline uint32_t block_exclusive_scan_u32(uint32_t v, uint32_t* red, uint32_t* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const uint32_t inc = wave_incl_scan_u32(v);
+  __syncthreads();
+  if (lane == 63) red[w] = inc;
+  __syncthreads();
+  uint32_t before = 0u, tot = 0u;
   for (int i = 0; i < nw; ++i) {
     if (i < w) before += red[i];
     tot += red[i];

@@ -247,7 +247,7 @@ __device__ __forceinline__ void topk_block(const SelectArgs& a, const float* s, 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
   __shared__ uint32_t hist[2][256];
   __shared__ uint32_t red[2][16];
-  __shared__ int redi[17];
+  __shared__ uint32_t redu[16];
   __shared__ uint32_t sh_digit[2], sh_above[2], sh_bucket[2];
   const int per = E > 0 ? E : (n_b + blockDim.x - 1) / blockDim.x;
   const int e0 = min(tid * per, n_b), e1 = min(e0 + per, n_b);
@@ -324,12 +324,14 @@ __device__ __forceinline__ void topk_block(const SelectArgs& a, const float* s, 
   // keys compared on the resolved digits: above kstar are taken, and `rem`
   // of those equal to it, lowest page id first
   const uint32_t kstar = prefix;
-  // one scan of (greater, equal) counts packed in 16 bits each (n <= 65535)
-  int c_gt = 0, c_eq = 0;
+  // one scan of (greater, equal) counts packed in the low and high 16 bits
+  // of an unsigned word: each prefix is at most n <= 65535, so neither field
+  // carries into the other, and the high field is read without sign extension
+  uint32_t c_gt = 0u, c_eq = 0u;
   EKV_FOR_KEYS(const uint32_t km = k & mask; c_gt += (km > kstar); c_eq += (km == kstar);)
-  int tot;
-  const int packed = block_exclusive_scan(c_gt | (c_eq << 16), redi, &tot);
-  const int gt_before = packed & 0xffff, eq_before = packed >> 16;
+  uint32_t tot;
+  const uint32_t packed = block_exclusive_scan_u32(c_gt | (c_eq << 16), redu, &tot);
+  const int gt_before = (int)(packed & 0xffffu), eq_before = (int)(packed >> 16);
   int pos = gt_before + min(eq_before, rem);
   int r = eq_before;
   EKV_FOR_KEYS(const uint32_t km = k & mask; bool take = km > kstar;
@@ -946,7 +948,12 @@ __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void t
   }
   wait_mem();  // every wave's device-scope stores have completed
   __syncthreads();
-  if (tid == 0) s_last = atomicAdd(a.done + unit, 1u) == (uint32_t)(G - 1);
+  if (tid == 0) {
+    // release: the bitmaps and tau_hat above are visible at agent scope
+    // before the arrival is; the last block's acquire below pairs with it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    s_last = atomicAdd(a.done + unit, 1u) == (uint32_t)(G - 1);
+  }
   __syncthreads();
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");

@@ -36,6 +36,15 @@ CASES = {
          "kmin": [-1.0, 0.25], "kmax": [0.5, 1.0], "bound": 0.0, "token_scores": [-1.5, -1.5],
          "derivation": "box [-1,0.5]x[0.25,1]; q1>0 takes kmax_1=0.5, q2<0 takes kmin_2=0.25: 0.5-0.5=0"},
     ],
+    "gauss_page": [
+        {"alpha": 1.5, "scale": 0.5, "q": [2.0, 1.0], "keys": [[1.0, 3.0], [-1.0, 3.0]],
+         "mean_y": 0.75, "sd_y": 0.5, "e_hat": 0.75 + 0.5 * math.sqrt(2 * math.log(2)),
+         "token_scores": [1.25, 0.25],
+         "derivation": "page mean (0,3), population variance (1,0); (alpha-1) scale = 0.25; "
+                       "mean_Y = 0.25 (2*0 + 1*3) = 0.75; var_Y = 0.25^2 (2^2*1 + 1^2*0) = 0.25, sd_Y = 0.5; "
+                       "e_hat = mean_Y + sd_Y sqrt(2 ln 2); the two token scores 0.25(2+3) = 1.25 and "
+                       "0.25(-2+3) = 0.25 have mean 0.75 and population variance 0.25"},
+    ],
     "gauss": [
         {"alpha": 2.0, "mu": 0.0, "sd": 1.0, "t": 0.0, "E": 1.0 / math.sqrt(2 * math.pi),
          "derivation": "E[Y_+] for a standard normal is phi(0)"},

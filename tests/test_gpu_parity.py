@@ -251,6 +251,37 @@ def test_topk_at_max_pages():
     assert sess.device_status() == 0
 
 
+@pytest.mark.parametrize("top_k", [5, 33000])
+def test_topk_more_than_32768_equal_scores(top_k):
+    """40000 one-token pages scored against q = 0: every box bound is exactly
+    0, so all pages tie and the lowest ids win.  More than 32768 equal keys
+    precede the last threads' slots, the case where a sign-extended 16-bit
+    count field would have produced negative output positions."""
+    from sparse_long_context_append_amd.runtime import DecodeSession
+    import sparse_long_context_append_amd as ekv
+    n, d = 40000, 64
+    print(f"[case] topk ties n={n} top_k={top_k}", flush=True)
+    table = np.arange(n, dtype=np.int32)[None, :]
+    sess = DecodeSession(batch=1, n_kv_heads=1, n_q_heads=1, head_dim=d, page_size=1, kv_dtype=ekv.EKV_F32,
+                         n_phys_pages=n, page_table=table, cap=top_k)
+    rng = np.random.default_rng(11)
+    k = torch.from_numpy(rng.standard_normal((1, n, 1, d)).astype(np.float32)).cuda()
+    v = torch.from_numpy(rng.standard_normal((1, n, 1, d)).astype(np.float32)).cuda()
+    sess.append(k, v)
+    q = torch.zeros((1, 1, d), dtype=torch.float32, device="cuda")
+    sess.select(q, policy=ekv.EKV_SELECT_BBOX_TOPK, alpha=1.5, scale=0.125, top_k=top_k)
+    sess.decode(q, alpha=1.5, scale=0.125)
+    torch.cuda.synchronize()
+    assert int(sess.sel_count[0, 0]) == top_k
+    np.testing.assert_array_equal(sess.sel[0, 0, :top_k].cpu().numpy(), np.arange(top_k))
+    # every selected token scores 0: uniform weights over all of them
+    assert int(sess.support_count[0, 0]) == top_k
+    assert abs(float(sess.psum[0, 0]) - 1.0) <= 1e-5
+    want = v[0, :top_k, 0].double().mean(dim=0).cpu().numpy()
+    np.testing.assert_allclose(sess.out[0, 0].cpu().numpy(), want, atol=2e-3)
+    assert sess.device_status() == 0
+
+
 def test_topk_covering_every_page_equals_dense():
     spec = W.make_spec("c2", context=1000, n_q_heads=8, n_kv_heads=2, n_needles=8, top_k=10 ** 6)
     sess, _ = _session(spec)

@@ -4,6 +4,7 @@ bound on every token score of the page (and the tightest one the box allows,
 checked against all box vertices), and top-k keeps the k best pages (brute
 force over all k-subsets)."""
 import itertools
+import math
 import json
 import os
 
@@ -110,3 +111,74 @@ def test_topk_brute_force():
                 best = (s, sub)
         assert list(got) == list(best[1])
         assert list(got) == sorted(got)
+
+
+# ------------------------------------------------- Gaussian page model ---
+# The summary (sec. 2.A) models a page's token scores as a Gaussian built
+# from the page's first and second key moments.  With the diagonal reading,
+# the model's mean and variance are exactly the mean and population variance
+# of the page's true scaled token scores whenever the keys' covariance is
+# diagonal; the pins below build such pages and compare against the token
+# scores themselves (computed one product at a time, not through the model).
+
+def _token_scores(q, blk, alpha, scale):
+    return [(alpha - 1.0) * scale * sum(float(q[i]) * float(t[i]) for i in range(len(q))) for t in blk]
+
+
+def test_golden_gauss_page():
+    c = GOLD["gauss_page"][0]
+    k = np.array(c["keys"])
+    md = metadata.page_metadata(k, len(k), len(k))
+    mu, sd, eh = scoring.gauss_page_stats(np.array(c["q"]), md["mean"], md["var"], md["count"], c["alpha"],
+                                          c["scale"])
+    assert mu[0] == pytest.approx(c["mean_y"], abs=1e-15)
+    assert sd[0] == pytest.approx(c["sd_y"], abs=1e-15)
+    assert eh[0] == pytest.approx(c["e_hat"], abs=1e-15)
+    np.testing.assert_allclose(_token_scores(c["q"], k, c["alpha"], c["scale"]), c["token_scores"], atol=1e-15)
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0, 1.3])
+def test_gauss_stats_one_token_pages(alpha):
+    """A page of one token: the model's mean is that token's scaled score,
+    its spread is zero, and the estimated maximum is the score itself."""
+    rng = np.random.default_rng(15)
+    d, L = 7, 13
+    k = rng.standard_normal((L, d)) * 2
+    q = rng.standard_normal(d) * 2
+    md = metadata.page_metadata(k, L, 1)
+    mu, sd, eh = scoring.gauss_page_stats(q, md["mean"], md["var"], md["count"], alpha, 0.3)
+    x = _token_scores(q, k, alpha, 0.3)
+    np.testing.assert_allclose(mu, x, rtol=0, atol=1e-13)
+    assert np.all(sd == 0.0)
+    np.testing.assert_allclose(eh, x, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("alpha,scale", [(1.5, 0.125), (1.3, 0.37), (2.0, 0.7)])
+def test_gauss_stats_match_token_scores_with_diagonal_covariance(alpha, scale):
+    """Pages whose keys are a centre plus sign-balanced offsets along the
+    coordinate axes (c + a_i e_i and c - a_i e_i), and pages whose keys
+    differ in one coordinate only: the key covariance is diagonal, so the
+    model's mean_Y and sd_Y^2 equal the mean and population variance of the
+    page's exact scores (alpha-1) scale q.k_t.  A dropped (alpha-1), a
+    missing square on the scale or on q_i, or a sample variance fails."""
+    rng = np.random.default_rng(16)
+    d = 6
+    for _ in range(25):
+        q = rng.standard_normal(d) * 2
+        c = rng.standard_normal(d)
+        axes = rng.choice(d, size=int(rng.integers(1, d + 1)), replace=False)
+        offs = rng.uniform(0.2, 2.0, axes.size)
+        balanced = [c + a * np.eye(d)[i] for i, a in zip(axes, offs)] + [c - a * np.eye(d)[i]
+                                                                         for i, a in zip(axes, offs)]
+        j = int(rng.integers(d))
+        one_coord = [c + s * np.eye(d)[j] for s in rng.standard_normal(int(rng.integers(2, 9))) * 1.5]
+        for blk in (np.array(balanced), np.array(one_coord)):
+            n = len(blk)
+            md = metadata.page_metadata(blk, n, n)
+            mu, sd, eh = scoring.gauss_page_stats(q, md["mean"], md["var"], md["count"], alpha, scale)
+            x = _token_scores(q, blk, alpha, scale)
+            m = sum(x) / n
+            var = sum((v - m) ** 2 for v in x) / n
+            assert mu[0] == pytest.approx(m, abs=1e-12)
+            assert sd[0] ** 2 == pytest.approx(var, abs=1e-12, rel=1e-12)
+            assert eh[0] == pytest.approx(m + math.sqrt(var) * math.sqrt(2 * math.log(n)), abs=1e-12)
