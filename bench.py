@@ -159,6 +159,40 @@ def score_kernel_ms(sess, spec, q, pol, scores, torch, timer, reps, copies=8):
     return out
 
 
+def read_ceiling(nbytes, torch, timer, reps=5):
+    """Best plain streaming-read rate (GB/s) over a buffer of the step's
+    size, after the same eviction as the timed steps: the library's read
+    probe at 4, 8 and 16 blocks per compute unit, best of `reps` each."""
+    import sparse_long_context_append_amd as ekv
+    n = max(16, (int(nbytes) + 15) // 16 * 16)
+    buf = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    best = 0.0
+    for per_cu in (4, 8, 16):
+        for _ in range(reps):
+            timer.evict()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            ekv.stream_read(buf, sink, blocks=per_cu * cus)
+            e1.record()
+            torch.cuda.synchronize()
+            best = max(best, n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf
+    return best
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def pct(xs, q):
     xs = sorted(xs)
     return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
@@ -252,6 +286,7 @@ def measure(spec, steps, warmup, torch, timer, do_dense=True, do_graph=True):
     assert status == 0, f"device status {status:#x}"
     del sess
     torch.cuda.empty_cache()
+    res["read_ceiling_gbs"] = read_ceiling(res["bytes"], torch, timer)
     return res
 
 
@@ -326,6 +361,8 @@ def summarize(spec, r):
         "bytes_per_step": int(r["bytes"]),
         "effective_gbs": round(r["bytes"] / (med * 1e-6) / 1e9, 1),
         "hbm_fraction": round(r["bytes"] / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "read_ceiling_gbs": round(r["read_ceiling_gbs"], 1),
+        "fraction_of_read_ceiling": round(r["bytes"] / (med * 1e-6) / 1e9 / r["read_ceiling_gbs"], 4),
         "pages_selected": r["pages_selected"],
         "pages_total": r["pages_total"],
         "support_mean": round(r["support_mean"], 2),
@@ -619,7 +656,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c4", help="workload the headline value is measured on")
-    ap.add_argument("--also", default="c3", help="second workload reported in the same line ('' for none)")
+    ap.add_argument("--also", default="c3,c5,c2,c1",
+                    help="comma-separated workloads reported beside the headline one in the same line ('' for none)")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -674,11 +712,12 @@ def main():
     log(f"device {torch.cuda.get_device_name(0)}; workload {spec.name}")
     r = measure(spec, args.steps, args.warmup, torch, timer, not args.no_dense, not args.no_graph)
     main_sum = summarize(spec, r)
-    extra = None
-    if args.also:
-        spec2 = W.make_spec(args.also)
+    extra = []
+    for name in [n for n in args.also.split(",") if n]:
+        spec2 = W.make_spec(name)
         r2 = measure(spec2, args.steps, args.warmup, torch, timer, not args.no_dense, not args.no_graph)
-        extra = summarize(spec2, r2)
+        extra.append(summarize(spec2, r2))
+        log(f"{name}: {extra[-1]['us_per_step']} us/step")
     cpu = None
     if not args.no_cpu:
         n_units = spec.batch * spec.n_kv_heads
@@ -694,6 +733,7 @@ def main():
             "us_per_step": round(cpu_us, 1),
             "dense_us_per_step": round(dense_s / len(dense_units) * n_units * 1e6, 1),
             "cores": int(os.environ.get("OMP_NUM_THREADS", _NCPU)),
+            "cpu_model": cpu_model(),
             "kind": "oracle",
             "sample": (f"float64 numpy oracle on the host, inputs prepared outside the timing: sparse step "
                        f"({spec.policy} scoring from prebuilt page metadata, selection, exact entmax over the "
@@ -723,8 +763,11 @@ def main():
                    "global_batch": spec.batch, "seq_len": spec.context, "parallelism": "none"},
         "us_per_step": med_us,
         "hbm_fraction": main_sum["hbm_fraction"],
+        "read_ceiling_gbs": main_sum["read_ceiling_gbs"],
+        "fraction_of_read_ceiling": main_sum["fraction_of_read_ceiling"],
         "detail": main_sum,
         "roofline": {
+            "scope": "dominant kernel of the step, per launch (the step-level fraction is hbm_fraction)",
             "bound": "hbm",
             "kernel": "score_bbox" if spec.policy == "bbox" else "score_gauss",
             "achieved": main_sum["score_kernel_gbs"],
@@ -737,7 +780,7 @@ def main():
         },
         "cpu_baseline": cpu,
     }
-    if extra is not None:
+    if extra:
         line["also"] = extra
     print(json.dumps(line), flush=True)
 

@@ -31,7 +31,7 @@
  *   - Conditions only the device can see (a page-table entry outside
  *     [0, n_phys_pages), a sequence longer than max_pages*page_size) set bits
  *     of a status word in the workspace; the offending page is skipped.  Read
- *     it with ekv_read_device_status after the caller synchronises.
+ *     it with ekv_read_device_status on the stream of the calls.
  *   - Calls that share one workspace must be ordered (same stream or
  *     explicit dependencies); concurrent calls on one workspace race.
  *   - No exception crosses this boundary.
@@ -131,6 +131,13 @@ typedef struct {
  *              1: one page set per (sequence, query head), each head scored
  *              and selected on its own.  The summary does not say how
  *              grouped-query heads share a selection; both are offered.
+ *   min_pages  EKV_SELECT_GAUSS: the fewest pages kept per selection unit
+ *              (>= 1; entmax over an empty set is undefined).  When the keep
+ *              rule keeps fewer than min(min_pages, n_b) pages, the unit keeps
+ *              the min(min_pages, n_b) pages of largest margin
+ *              max_h (e_hat - tau_hat) instead, lower page id first on equal
+ *              margins.  Values above 1 need max_pages <= 65535.  Not used by
+ *              EKV_SELECT_BBOX_TOPK, which always keeps min(top_k, n_b) pages.
  */
 typedef struct {
   int32_t policy;
@@ -139,13 +146,22 @@ typedef struct {
   float scale;
   float delta;
   int32_t per_head;
+  int32_t min_pages;
 } ekv_select_params;
 
 /*
- * Workspace bytes needed by every call on this cache/batch shape with up to
- * n_q_heads query heads.  Returns 0 if the shape is invalid.
+ * Workspace bytes for the calls on this cache/batch shape with n_q_heads
+ * query heads.  Returns 0 if the shape is invalid.
+ *   cap  the largest page-list capacity of the sparse ekv_entmax_decode
+ *        calls the workspace will serve; its per-item candidate regions
+ *        (four bytes per token of a list, six arrays per query head) are
+ *        sized for lists of min(cap, max_pages) pages.  cap <= 0 sizes them
+ *        for the whole cache, which a full-cache decode (sel == NULL) needs.
+ * Selection, scoring and softmax decode use only the part before those
+ * regions, which does not depend on cap.  Every call checks ws_bytes against
+ * what it needs and returns EKV_ERR_WORKSPACE when it is short.
  */
-size_t ekv_workspace_size(const ekv_cache* cache, const ekv_seqs* seqs, int32_t n_q_heads);
+size_t ekv_workspace_size(const ekv_cache* cache, const ekv_seqs* seqs, int32_t n_q_heads, int32_t cap);
 
 /*
  * Prepare a fresh workspace (clears its control words with a fill kernel on
@@ -185,6 +201,7 @@ ekv_status ekv_append_kv(const ekv_cache* cache, const ekv_seqs* seqs, const voi
  *   sel_count  [batch][H] int32: number of valid entries in sel
  *   tau_hat    optional [batch][n_q_heads] float32 (EKV_SELECT_GAUSS only):
  *              the estimated threshold per query head
+ *   workspace  at least the cap-independent part (ekv_workspace_size)
  * BBOX_TOPK: page score = max over the group's heads of
  *   scale * sum_i max(q_i k_min_i, q_i k_max_i), the tightest upper bound
  *   the box gives on q.k (summary sec. 2.A); keeps the min(top_k, n_b)
@@ -263,10 +280,22 @@ ekv_status ekv_score_pages(const ekv_cache* cache, const ekv_seqs* seqs, const f
                            void* workspace, size_t ws_bytes, void* stream);
 
 /*
- * Copy the device status word (EKV_DEV_* bits) to *host_flags and clear it.
- * Synchronous: waits for all work on the device.
+ * Copy the device status word (EKV_DEV_* bits) to *host_flags and clear it,
+ * in order after the work already enqueued on `stream`.  Synchronous: waits
+ * for `stream` (only) before returning.  Work on other streams that shares
+ * the workspace must be ordered before it by the caller.
  */
-ekv_status ekv_read_device_status(void* workspace, size_t ws_bytes, int32_t* host_flags);
+ekv_status ekv_read_device_status(void* workspace, size_t ws_bytes, int32_t* host_flags, void* stream);
+
+/*
+ * Measurement helper, not part of the decode path: one plain streaming read
+ * of `bytes` (a multiple of 16) from the 16-byte aligned device buffer src,
+ * with `blocks` blocks of 256 threads (<= 0: eight per compute unit), on
+ * `stream`.  Timing it after the caches are evicted gives the read-stream
+ * ceiling the decode kernels are compared with at the same size.  sink:
+ * one device uint32 the kernel may set (its value is meaningless).
+ */
+ekv_status ekv_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, void* stream);
 
 /* Static description of a status code. */
 const char* ekv_status_string(int32_t status);

@@ -25,7 +25,9 @@ EntmaxKV summary section 2.B names two policies:
        it: max_h (e_hat[h,p] - tau_hat[h]) > -Delta (strict);
      * if that keeps nothing, the single page maximising that quantity is
        kept (lowest page id on ties), since entmax over an empty set is
-       undefined.
+       undefined.  More generally, with a floor of m pages, a unit that
+       keeps fewer than min(m, n) pages keeps the min(m, n) pages of largest
+       margin instead (lowest page id on ties); m = 1 is the rule above.
 """
 from __future__ import annotations
 
@@ -144,12 +146,18 @@ def gauss_tau_hat(mu: np.ndarray, sd: np.ndarray, count: np.ndarray, alpha: floa
     return 0.5 * (lo + hi)
 
 
-def gauss_keep_pages(e_hat: np.ndarray, tau_hat: np.ndarray, delta: float) -> np.ndarray:
-    """e_hat: [G][n] estimated maxima of the group's heads, tau_hat: [G].
-    Ascending ids of kept pages (at least one)."""
+def gauss_margin(e_hat: np.ndarray, tau_hat: np.ndarray) -> np.ndarray:
+    """max over the group's heads of e_hat[h, p] - tau_hat[h], per page."""
     e_hat = np.asarray(e_hat, dtype=np.float64)
-    margin = np.max(e_hat - np.asarray(tau_hat, dtype=np.float64)[:, None], axis=0)
+    return np.max(e_hat - np.asarray(tau_hat, dtype=np.float64)[:, None], axis=0)
+
+
+def gauss_keep_pages(e_hat: np.ndarray, tau_hat: np.ndarray, delta: float, min_pages: int = 1) -> np.ndarray:
+    """e_hat: [G][n] estimated maxima of the group's heads, tau_hat: [G].
+    Ascending ids of kept pages (at least min(min_pages, n))."""
+    margin = gauss_margin(e_hat, tau_hat)
     keep = np.nonzero(margin > -delta)[0]
-    if keep.size == 0:
-        keep = np.array([int(np.argmax(margin))])  # argmax returns the first (lowest id)
+    m = min(int(min_pages), margin.size)
+    if keep.size < m:
+        keep = topk_pages(margin, m)  # the m largest margins, lower id first on ties
     return keep

@@ -10,5 +10,5 @@ from .binding import (  # noqa: F401
     EKV_F32, EKV_BF16, EKV_SELECT_BBOX_TOPK, EKV_SELECT_GAUSS,
     EntmaxKVError, PagedCache, Sequences, lib, lib_path,
     workspace_size, workspace_init, append_kv, select_pages, entmax_decode, softmax_decode, score_pages,
-    read_device_status, status_string, last_error,
+    read_device_status, status_string, last_error, stream_read,
 )

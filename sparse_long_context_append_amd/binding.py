@@ -49,6 +49,7 @@ class _SelectParams(ctypes.Structure):
         ("policy", ctypes.c_int32), ("top_k", ctypes.c_int32),
         ("alpha", ctypes.c_float), ("scale", ctypes.c_float),
         ("delta", ctypes.c_float), ("per_head", ctypes.c_int32),
+        ("min_pages", ctypes.c_int32),
     ]
 
 
@@ -56,7 +57,7 @@ _LIB = None
 _vp, _sz, _i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
 _PC, _PS, _PP = ctypes.POINTER(_Cache), ctypes.POINTER(_Seqs), ctypes.POINTER(_SelectParams)
 _SIGS = {
-    "ekv_workspace_size": (_sz, [_PC, _PS, _i32]),
+    "ekv_workspace_size": (_sz, [_PC, _PS, _i32, _i32]),
     "ekv_workspace_init": (_i32, [_vp, _sz, _vp]),
     "ekv_append_kv": (_i32, [_PC, _PS, _vp, _vp, _i32, _vp, _sz, _vp]),
     "ekv_select_pages": (_i32, [_PC, _PS, _vp, _i32, _PP, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
@@ -65,7 +66,8 @@ _SIGS = {
     "ekv_softmax_decode": (_i32, [_PC, _PS, _vp, _i32, ctypes.c_float, _vp, _vp, _i32, _i32, _vp, _vp, _vp,
                                   _sz, _vp]),
     "ekv_score_pages": (_i32, [_PC, _PS, _vp, _i32, _PP, _vp, _vp, _sz, _vp]),
-    "ekv_read_device_status": (_i32, [_vp, _sz, ctypes.POINTER(_i32)]),
+    "ekv_read_device_status": (_i32, [_vp, _sz, ctypes.POINTER(_i32), _vp]),
+    "ekv_stream_read": (_i32, [_vp, _sz, _vp, _i32, _vp]),
     "ekv_status_string": (ctypes.c_char_p, [_i32]),
     "ekv_last_error": (ctypes.c_char_p, []),
 }
@@ -154,8 +156,10 @@ class Sequences:
         return _Seqs(self.batch, self.max_pages, _ptr(self.page_table), _ptr(self.seq_lens))
 
 
-def workspace_size(cache: PagedCache, seqs: Sequences, n_q_heads: int) -> int:
-    return int(lib().ekv_workspace_size(ctypes.byref(cache.c()), ctypes.byref(seqs.c()), n_q_heads))
+def workspace_size(cache: PagedCache, seqs: Sequences, n_q_heads: int, cap: int = 0) -> int:
+    """cap: largest page-list capacity of the sparse decodes served (0: the
+    whole cache, as full-cache decodes need)."""
+    return int(lib().ekv_workspace_size(ctypes.byref(cache.c()), ctypes.byref(seqs.c()), n_q_heads, int(cap)))
 
 
 def workspace_init(ws, stream=None):
@@ -167,8 +171,9 @@ def append_kv(cache: PagedCache, seqs: Sequences, k_new, v_new, n_new: int, ws, 
                                n_new, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "append_kv")
 
 
-def _params(policy, top_k, alpha, scale, delta, per_head=False) -> _SelectParams:
-    return _SelectParams(int(policy), int(top_k), float(alpha), float(scale), float(delta), int(bool(per_head)))
+def _params(policy, top_k, alpha, scale, delta, per_head=False, min_pages=1) -> _SelectParams:
+    return _SelectParams(int(policy), int(top_k), float(alpha), float(scale), float(delta), int(bool(per_head)),
+                         int(min_pages))
 
 
 def _sel_heads(cache: PagedCache, sel, sel_heads):
@@ -181,9 +186,9 @@ def _sel_heads(cache: PagedCache, sel, sel_heads):
 
 
 def select_pages(cache: PagedCache, seqs: Sequences, q, n_q_heads: int, *, policy: int, top_k: int = 0,
-                 alpha: float, scale: float, delta: float = 0.0, per_head: bool = False, sel, sel_count,
-                 cap: int, tau_hat=None, ws, stream=None):
-    p = _params(policy, top_k, alpha, scale, delta, per_head)
+                 alpha: float, scale: float, delta: float = 0.0, per_head: bool = False, min_pages: int = 1,
+                 sel, sel_count, cap: int, tau_hat=None, ws, stream=None):
+    p = _params(policy, top_k, alpha, scale, delta, per_head, min_pages)
     _check(lib().ekv_select_pages(ctypes.byref(cache.c()), ctypes.byref(seqs.c()), _ptr(q), n_q_heads,
                                   ctypes.byref(p), _ptr(sel), _ptr(sel_count), cap, _ptr(tau_hat), _ptr(ws),
                                   ws.numel() * ws.element_size(), _stream(stream)), "select_pages")
@@ -216,8 +221,17 @@ def softmax_decode(cache: PagedCache, seqs: Sequences, q, n_q_heads: int, *, sca
                                     _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "softmax_decode")
 
 
-def read_device_status(ws) -> int:
+def read_device_status(ws, stream=None) -> int:
+    """Status bits of the work enqueued so far on `stream` (default: torch's
+    current stream), cleared afterwards; waits for that stream."""
     flags = ctypes.c_int32(0)
-    _check(lib().ekv_read_device_status(_ptr(ws), ws.numel() * ws.element_size(), ctypes.byref(flags)),
-           "read_device_status")
+    _check(lib().ekv_read_device_status(_ptr(ws), ws.numel() * ws.element_size(), ctypes.byref(flags),
+                                        _stream(stream)), "read_device_status")
     return flags.value
+
+
+def stream_read(src, sink, blocks: int = 0, nbytes: int | None = None, stream=None):
+    """Plain streaming read of `src` (measurement helper: the read-stream
+    ceiling at a given size)."""
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    _check(lib().ekv_stream_read(_ptr(src), n, _ptr(sink), int(blocks), _stream(stream)), "stream_read")

@@ -58,14 +58,23 @@ ekv_status check_heads(const ekv_cache* c, int32_t n_q_heads, int* group) {
   return EKV_OK;
 }
 
+// Pages of the longest list a decode with capacity `cap` reads (cap <= 0:
+// the whole cache).
+int list_pages(const ekv_seqs* s, int32_t cap) { return cap > 0 && cap < s->max_pages ? cap : s->max_pages; }
+
+// Workspace layout for decodes of lists of up to item_pages pages; a call
+// that uses no per-item region (selection, scoring, softmax decode) needs
+// only the part before them.
 ekv_status check_ws(const ekv_cache* c, const ekv_seqs* s, int32_t n_q_heads, void* ws, size_t ws_bytes,
-                    ekv::Layout* L) {
-  *L = ekv::make_layout(s->batch, c->n_kv_heads, n_q_heads, s->max_pages, c->page_size, c->head_dim);
+                    int item_pages, bool items, ekv::Layout* L) {
+  *L = ekv::make_layout(s->batch, c->n_kv_heads, n_q_heads, s->max_pages, c->page_size, c->head_dim, item_pages);
   if (!ws) return fail(EKV_ERR_WORKSPACE, "workspace is NULL");
   if (!aligned16(ws)) return fail(EKV_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-  if (ws_bytes < L->total)
+  const size_t need = items ? L->total : L->item_cnt;
+  if (ws_bytes < need)
     return fail(EKV_ERR_WORKSPACE, "workspace holds " + std::to_string(ws_bytes) + " bytes, needs " +
-                                       std::to_string(L->total));
+                                       std::to_string(need) +
+                                       (items ? " (size it with this call's cap, or 0 for full-cache decodes)" : ""));
   return EKV_OK;
 }
 
@@ -101,13 +110,13 @@ template <typename Args> Args per_query_head_view(const Args& a) {
 
 extern "C" {
 
-size_t ekv_workspace_size(const ekv_cache* cache, const ekv_seqs* seqs, int32_t n_q_heads) {
+size_t ekv_workspace_size(const ekv_cache* cache, const ekv_seqs* seqs, int32_t n_q_heads, int32_t cap) {
   int G = 0;
   if (check_cache(cache) != EKV_OK || check_seqs(cache, seqs) != EKV_OK ||
       check_heads(cache, n_q_heads, &G) != EKV_OK)
     return 0;
   return ekv::make_layout(seqs->batch, cache->n_kv_heads, n_q_heads, seqs->max_pages, cache->page_size,
-                          cache->head_dim).total;
+                          cache->head_dim, list_pages(seqs, cap)).total;
 }
 
 ekv_status ekv_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
@@ -163,6 +172,9 @@ static ekv_status prepare_select(const ekv_cache* cache, const ekv_seqs* seqs, c
     if (!(p->alpha >= 1.1f && p->alpha <= 2.0f))
       return fail(EKV_ERR_UNSUPPORTED, "Gaussian selection supports alpha in [1.1, 2]");
     if (!(p->delta >= 0.f) || !isfinite(p->delta)) return fail(EKV_ERR_INVALID_ARG, "delta must be finite and >= 0");
+    if (p->min_pages < 1) return fail(EKV_ERR_INVALID_ARG, "min_pages must be >= 1");
+    if (p->min_pages > 1 && seqs->max_pages > 65535)
+      return fail(EKV_ERR_UNSUPPORTED, "min_pages > 1 supports up to 65535 pages per sequence");
   } else {
     return fail(EKV_ERR_INVALID_ARG, "unknown selection policy");
   }
@@ -170,7 +182,7 @@ static ekv_status prepare_select(const ekv_cache* cache, const ekv_seqs* seqs, c
   if (p->per_head != 0 && p->per_head != 1) return fail(EKV_ERR_INVALID_ARG, "per_head must be 0 or 1");
   if (p->per_head && (long long)seqs->batch * n_q_heads > ekv::kMaxUnits)
     return fail(EKV_ERR_UNSUPPORTED, "per-query-head selection needs batch * n_q_heads <= 4096");
-  if ((st = check_ws(cache, seqs, n_q_heads, workspace, ws_bytes, L)) != EKV_OK) return st;
+  if ((st = check_ws(cache, seqs, n_q_heads, workspace, ws_bytes, 1, false, L)) != EKV_OK) return st;
   *a = ekv::SelectArgs{};
   a->batch = seqs->batch; a->n_kv_heads = cache->n_kv_heads; a->n_q_heads = n_q_heads; a->group = G;
   a->hkv_mem = cache->n_kv_heads; a->kv_shift = 0; a->per_head_scores = 0;
@@ -178,7 +190,8 @@ static ekv_status prepare_select(const ekv_cache* cache, const ekv_seqs* seqs, c
   a->max_pages = seqs->max_pages; a->n_phys = cache->n_phys_pages;
   a->page_table = seqs->page_table; a->seq_lens = seqs->seq_lens;
   a->k_box = cache->k_box; a->k_moments = cache->k_moments; a->q = q;
-  a->policy = p->policy; a->top_k = p->top_k; a->alpha = p->alpha; a->scale = p->scale; a->delta = p->delta;
+  a->policy = p->policy; a->top_k = p->top_k; a->min_pages = p->min_pages;
+  a->alpha = p->alpha; a->scale = p->scale; a->delta = p->delta;
   a->scores = at<float>(workspace, L->scores);
   a->score_stride = ekv::score_stride(seqs->max_pages);
   a->musd = at<float2>(workspace, L->musd);
@@ -218,7 +231,9 @@ ekv_status ekv_select_pages(const ekv_cache* cache, const ekv_seqs* seqs, const 
     return hip_status(ekv::launch_topk(u, s), "topk launch");
   }
   if ((st = hip_status(ekv::launch_score_gauss(a, s), "score_gauss launch")) != EKV_OK) return st;
-  return hip_status(ekv::launch_tau_hat(u, s), "tau_hat launch");
+  if ((st = hip_status(ekv::launch_tau_hat(u, s), "tau_hat launch")) != EKV_OK) return st;
+  if (params->min_pages > 1) return hip_status(ekv::launch_gauss_floor(u, s), "gauss_floor launch");
+  return EKV_OK;
 }
 
 ekv_status ekv_score_pages(const ekv_cache* cache, const ekv_seqs* seqs, const float* q, int32_t n_q_heads,
@@ -243,8 +258,8 @@ ekv_status ekv_score_pages(const ekv_cache* cache, const ekv_seqs* seqs, const f
 // Validation and argument packing shared by the two decode entry points.
 ekv_status prepare_decode(const ekv_cache* cache, const ekv_seqs* seqs, const float* q, int32_t n_q_heads,
                           float alpha, float scale, const int32_t* sel, const int32_t* sel_count, int32_t cap,
-                          int32_t sel_heads, float* out, void* workspace, size_t ws_bytes, ekv::DecodeArgs* a,
-                          ekv::Layout* L) {
+                          int32_t sel_heads, float* out, void* workspace, size_t ws_bytes, bool items,
+                          ekv::DecodeArgs* a, ekv::Layout* L) {
   ekv_status st;
   int G = 0;
   if ((st = check_cache(cache)) != EKV_OK) return st;
@@ -260,7 +275,9 @@ ekv_status prepare_decode(const ekv_cache* cache, const ekv_seqs* seqs, const fl
   const bool per_head = sel && sel_heads == n_q_heads && G > 1;
   if (per_head && (long long)seqs->batch * n_q_heads > ekv::kMaxUnits)
     return fail(EKV_ERR_UNSUPPORTED, "per-query-head page lists need batch * n_q_heads <= 4096");
-  if ((st = check_ws(cache, seqs, n_q_heads, workspace, ws_bytes, L)) != EKV_OK) return st;
+  if ((st = check_ws(cache, seqs, n_q_heads, workspace, ws_bytes, list_pages(seqs, sel ? cap : 0), items, L)) !=
+      EKV_OK)
+    return st;
   *a = ekv::DecodeArgs{};
   a->batch = seqs->batch; a->n_kv_heads = cache->n_kv_heads; a->n_q_heads = n_q_heads; a->group = G;
   a->hkv_mem = cache->n_kv_heads; a->kv_shift = 0; a->sel_shift = 0;
@@ -284,7 +301,7 @@ ekv_status ekv_entmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const
   ekv::DecodeArgs a;
   ekv::Layout L;
   ekv_status st = prepare_decode(cache, seqs, q, n_q_heads, alpha, scale, sel, sel_count, cap, sel_heads, out,
-                                 workspace, ws_bytes, &a, &L);
+                                 workspace, ws_bytes, true, &a, &L);
   if (st != EKV_OK) return st;
   if ((support_idx || support_p) && support_cap < 1)
     return fail(EKV_ERR_INVALID_ARG, "support_idx/support_p need support_cap >= 1");
@@ -310,7 +327,7 @@ ekv_status ekv_softmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, cons
   ekv::DecodeArgs a;
   ekv::Layout L;
   ekv_status st = prepare_decode(cache, seqs, q, n_q_heads, 2.0f, scale, sel, sel_count, cap, sel_heads, out,
-                                 workspace, ws_bytes, &a, &L);
+                                 workspace, ws_bytes, false, &a, &L);
   if (st != EKV_OK) return st;
   if (cache->kv_dtype != EKV_BF16) return fail(EKV_ERR_UNSUPPORTED, "softmax decode needs bf16 keys/values");
   if (a.group == 8) {
@@ -326,19 +343,28 @@ ekv_status ekv_softmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, cons
                     "softmax_decode launch");
 }
 
-ekv_status ekv_read_device_status(void* workspace, size_t ws_bytes, int32_t* host_flags) {
+ekv_status ekv_read_device_status(void* workspace, size_t ws_bytes, int32_t* host_flags, void* stream) {
   if (!workspace || ws_bytes < 256) return fail(EKV_ERR_WORKSPACE, "workspace is NULL or too small");
   if (!host_flags) return fail(EKV_ERR_INVALID_ARG, "host_flags is NULL");
+  hipStream_t s = (hipStream_t)stream;
   uint32_t v = 0;
-  hipError_t e = hipDeviceSynchronize();
-  if (e == hipSuccess) e = hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost);
-  if (e == hipSuccess) {
-    const uint32_t zero = 0;
-    e = hipMemcpy(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice);
-  }
+  // ordered after the stream's earlier work; the word is cleared by a fill
+  // kernel on the same stream, then the stream (only) is waited for
+  hipError_t e = hipMemcpyAsync(&v, workspace, sizeof(v), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = ekv::launch_fill_zero(workspace, 16, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_status(e, "read device status");
   *host_flags = (int32_t)v;
   return EKV_OK;
+}
+
+ekv_status ekv_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, void* stream) {
+  if (!src || !aligned16(src) || bytes % 16 != 0)
+    return fail(EKV_ERR_INVALID_ARG, "src must be a 16-byte aligned buffer of a multiple of 16 bytes");
+  if (!sink) return fail(EKV_ERR_INVALID_ARG, "sink is NULL");
+  if (blocks > 65535) return fail(EKV_ERR_INVALID_ARG, "blocks must be <= 65535");
+  const int nb = blocks > 0 ? blocks : 8 * device_cus();
+  return hip_status(ekv::launch_stream_read(src, bytes, sink, nb, (hipStream_t)stream), "stream_read launch");
 }
 
 const char* ekv_status_string(int32_t status) {

@@ -19,6 +19,7 @@ constexpr int kWave = 64;
 constexpr int kItemTokens = 64;  // tokens of one decode work item
 
 struct Layout {
+  // regions every call may touch, at offsets that depend only on the shape
   size_t status;    // u32 device status bits
   size_t sel_done;  // u32 [B*Hq] per-unit arrival counters of the selection stage (zero between calls)
   size_t scores;    // f32 [B*Hq][score_stride] bounding-box page scores (unit rows)
@@ -26,6 +27,8 @@ struct Layout {
   size_t ehat;      // f32 [B*Hq*max_pages] estimated page maximum
   size_t tau_hat;   // f64 [B*Hq]
   size_t keep_bits; // u64 [B*Hq][keep_words(max_pages)] Gaussian keep bitmaps
+  size_t smx_part;  // f32 [B*Hq][kSmxMaxSlots][head_dim + 2] softmax block partials
+  // the entmax decode's per-item regions, sized for lists of item_pages pages
   size_t item_cnt;  // i32 [B*Hq*max_items] candidates kept by each decode work item
   size_t item_max;  // f32 [B*Hq*max_items] per item maximum score
   size_t item_lb;   // f32 [B*Hq*max_items] per item lower bound on the head's threshold
@@ -35,7 +38,6 @@ struct Layout {
   size_t ovf_x;     // f32 [B*Hq*max_items*64] compacted candidates (large sets)
   size_t ovf_t;     // i32 [...]
   size_t ovf_r;     // i32 [...]
-  size_t smx_part;  // f32 [B*Hq][kSmxMaxSlots][head_dim + 2] softmax block partials
   size_t total;
   size_t max_items; // per (sequence, query head)
 };
@@ -48,12 +50,15 @@ inline int score_stride(int max_pages) { return (max_pages + 3) & ~3; }
 
 constexpr int kSmxMaxSlots = 256;  // softmax decode blocks per (sequence, KV head), at most
 
-inline Layout make_layout(int B, int Hkv, int Hq, int max_pages, int P, int D = 128) {
+// item_pages: the longest page list an entmax decode on this workspace
+// reads (the list capacity of sparse calls; max_pages for the full cache).
+// Everything before item_cnt is independent of it.
+inline Layout make_layout(int B, int Hkv, int Hq, int max_pages, int P, int D, int item_pages) {
   (void)Hkv;  // every per-unit array is sized for B * Hq units
   Layout L{};
   size_t off = 0;
   const size_t bh = size_t(B) * Hq;
-  L.max_items = (size_t(max_pages) * P + kItemTokens - 1) / kItemTokens;
+  L.max_items = (size_t(item_pages) * P + kItemTokens - 1) / kItemTokens;
   const size_t tok = L.max_items * kItemTokens;
   L.status = off;   off = align256(off + 4);
   // selection units are (sequence, KV head), or (sequence, query head) in
@@ -64,6 +69,7 @@ inline Layout make_layout(int B, int Hkv, int Hq, int max_pages, int P, int D = 
   L.ehat = off;     off = align256(off + 4 * bh * max_pages);
   L.tau_hat = off;  off = align256(off + 8 * bh);
   L.keep_bits = off; off = align256(off + 8 * bh * keep_words(max_pages));
+  L.smx_part = off; off = align256(off + 4 * bh * kSmxMaxSlots * size_t(D + 2));
   L.item_cnt = off; off = align256(off + 4 * bh * L.max_items);
   L.item_max = off; off = align256(off + 4 * bh * L.max_items);
   L.item_lb = off;  off = align256(off + 4 * bh * L.max_items);
@@ -73,7 +79,6 @@ inline Layout make_layout(int B, int Hkv, int Hq, int max_pages, int P, int D = 
   L.ovf_x = off;    off = align256(off + 4 * bh * tok);
   L.ovf_t = off;    off = align256(off + 4 * bh * tok);
   L.ovf_r = off;    off = align256(off + 4 * bh * tok);
-  L.smx_part = off; off = align256(off + 4 * bh * kSmxMaxSlots * size_t(D + 2));
   L.total = off;
   return L;
 }

@@ -36,7 +36,7 @@ struct SelectArgs {
   const void* k_box;
   const float* k_moments;
   const float* q;
-  int policy, top_k;
+  int policy, top_k, min_pages;
   float alpha, scale, delta;
   int32_t* sel;
   int32_t* sel_count;
@@ -89,11 +89,13 @@ struct DecodeArgs {
 };
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_score_bbox(const SelectArgs& a, hipStream_t s);
 hipError_t launch_topk(const SelectArgs& a, hipStream_t s);
 hipError_t launch_score_gauss(const SelectArgs& a, hipStream_t s);
 hipError_t launch_tau_hat(const SelectArgs& a, hipStream_t s);
+hipError_t launch_gauss_floor(const SelectArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int target_blocks, hipStream_t s);
 // softmax decode over the same page list; `part` holds max_slots * (D + 2)
 // floats per query head

@@ -991,6 +991,61 @@ __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void t
 }
 
 // ---------------------------------------------------------------------------
+// At least min_pages pages per unit (min_pages > 1; the threshold kernel's
+// last block already guarantees one).  When the keep rule kept fewer than
+// m = min(min_pages, n_b) pages, the unit's list becomes the m pages of
+// largest margin max_h (e_hat_h - tau_hat_h), lower page id first on equal
+// margins, in ascending order: a superset of the kept pages, whose margins
+// are above -delta while every other page's is not.  One 1024-thread block
+// per unit; the margins (rounded to float) go through the top-k block.
+// ---------------------------------------------------------------------------
+template <int G, int E>
+__global__ __launch_bounds__(kSelThreads) void gauss_floor_kernel(SelectArgs a) {
+  constexpr int KE = E > 0 ? E : 1;
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int unit = b * a.n_kv_heads + g;
+  const int tid = threadIdx.x;
+  const int L = clamp_len(a.seq_lens[b], a.max_pages, a.page_size, a.status);
+  const int n_b = pages_of(L, a.page_size);
+  const int m = min(a.min_pages, n_b);
+  if (a.sel_count[unit] >= m) return;  // block-uniform
+  int32_t* out = a.sel + (size_t)unit * a.cap;
+  if (m == n_b) {  // every page
+    for (int p = tid; p < n_b; p += blockDim.x) out[p] = p;
+    if (tid == 0) a.sel_count[unit] = n_b;
+    return;
+  }
+  double tau[G];
+  const float* eh[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const size_t bh = (size_t)b * a.n_q_heads + (size_t)g * G + h;
+    tau[h] = a.tau_hat[bh];
+    eh[h] = a.ehat + bh * a.max_pages;
+  }
+  auto margin = [&](int p) {
+    double mg = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < G; ++h) mg = fmax(mg, (double)eh[h][p] - tau[h]);
+    return (float)mg;
+  };
+  uint32_t keys[KE];
+  float* s = a.scores + (size_t)unit * a.score_stride;
+  if (E > 0) {
+#pragma unroll
+    for (int i = 0; i < KE; ++i) {
+      const int p = tid * KE + i;
+      keys[i] = p < n_b ? f2key(margin(p)) : 0u;
+    }
+  } else {
+    keys[0] = 0u;  // unused: the keys are read back from the score row
+    for (int p = tid; p < n_b; p += blockDim.x) s[p] = margin(p);
+    __syncthreads();  // the row is read by other threads of the block next
+  }
+  topk_block<E>(a, s, keys, n_b, m, out, unit);
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 template <int DT, int D>
@@ -1073,6 +1128,27 @@ static hipError_t tau_hat_dispatch(const SelectArgs& a, hipStream_t s) {
 // The live-page list holds 8192 pages (two blocks per compute unit) unless a
 // sequence can have more pages; then 16384 (128 KB of LDS, one block per
 // unit), so that long sequences keep iterating on chip.
+template <int E>
+static hipError_t gauss_floor_dispatch(const SelectArgs& a, hipStream_t s) {
+  const dim3 grid(a.n_kv_heads, a.batch), block(kSelThreads);
+  switch (a.group) {
+    case 1: hipLaunchKernelGGL((gauss_floor_kernel<1, E>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gauss_floor_kernel<2, E>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((gauss_floor_kernel<4, E>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((gauss_floor_kernel<8, E>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Needs max_pages <= 65535 (the top-k block's limit, checked on the host).
+hipError_t launch_gauss_floor(const SelectArgs& a, hipStream_t s) {
+  const int per = (a.max_pages + kSelThreads - 1) / kSelThreads;
+  if (per <= 4) return gauss_floor_dispatch<4>(a, s);
+  if (per <= 16) return gauss_floor_dispatch<16>(a, s);
+  return gauss_floor_dispatch<0>(a, s);
+}
+
 hipError_t launch_tau_hat(const SelectArgs& a, hipStream_t s) {
   const bool gen = !(a.alpha == 1.5f || a.alpha == 2.0f);
   if (a.max_pages > kTauHatLive)

@@ -20,10 +20,12 @@ class DecodeSession:
 
     page_table: int32 [batch][max_pages] (host array or device tensor),
     seq_lens: int32 [batch] initial lengths (the cache starts empty: append
-    fills it and advances the lengths)."""
+    fills it and advances the lengths).
+    full_decode: size the workspace for full-cache decodes too (otherwise
+    only for sparse decodes of lists of up to `cap` pages)."""
 
     def __init__(self, *, batch, n_kv_heads, n_q_heads, head_dim, page_size, kv_dtype, n_phys_pages,
-                 page_table, device="cuda", with_box=True, with_moments=True, cap=None):
+                 page_table, device="cuda", with_box=True, with_moments=True, cap=None, full_decode=True):
         torch = _torch()
         self.torch = torch
         self.device = torch.device(device)
@@ -44,12 +46,12 @@ class DecodeSession:
         self.cache = B.PagedCache(self.k, self.v, self.k_box, self.k_moments, n_phys_pages, n_kv_heads,
                                   page_size, head_dim, kv_dtype)
         self.seqs = B.Sequences(self.page_table, self.seq_lens, batch, self.max_pages)
-        nbytes = B.workspace_size(self.cache, self.seqs, n_q_heads)
+        self.cap = int(cap if cap is not None else self.max_pages)
+        nbytes = B.workspace_size(self.cache, self.seqs, n_q_heads, 0 if full_decode else self.cap)
         if nbytes == 0:
             raise ValueError("invalid cache/sequence shape: " + B.last_error())
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         B.workspace_init(self.ws)
-        self.cap = int(cap if cap is not None else self.max_pages)
         # room for one page list per query head; the last selection decides
         # whether the rows are KV heads (shared lists) or query heads
         self._sel_buf = torch.zeros(batch * n_q_heads * self.cap, dtype=torch.int32, device=self.device)
@@ -89,13 +91,13 @@ class DecodeSession:
     def sel_count(self):
         return self._cnt_buf[: self.batch * self.sel_heads].view(self.batch, self.sel_heads)
 
-    def select(self, q, *, policy, alpha, scale, top_k=0, delta=0.0, per_head=False):
+    def select(self, q, *, policy, alpha, scale, top_k=0, delta=0.0, per_head=False, min_pages=1):
         """Page selection shared by each KV head's query group, or one
         selection per query head (per_head=True)."""
         self.sel_heads = self.n_q_heads if per_head else self.n_kv_heads
         B.select_pages(self.cache, self.seqs, q, self.n_q_heads, policy=policy, top_k=top_k, alpha=alpha,
-                       scale=scale, delta=delta, per_head=per_head, sel=self.sel, sel_count=self.sel_count,
-                       cap=self.cap, tau_hat=self.tau_hat, ws=self.ws)
+                       scale=scale, delta=delta, per_head=per_head, min_pages=min_pages, sel=self.sel,
+                       sel_count=self.sel_count, cap=self.cap, tau_hat=self.tau_hat, ws=self.ws)
 
     def decode(self, q, *, alpha, scale, sparse=True, support_idx=None, support_p=None, support_cap=0):
         B.entmax_decode(self.cache, self.seqs, q, self.n_q_heads, alpha=alpha, scale=scale,

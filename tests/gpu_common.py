@@ -24,7 +24,7 @@ def run_step(sess, spec, q_np, sparse=True, per_head=False):
     supp = torch.full((spec.batch, spec.n_q_heads, SUPPORT_CAP), -1, dtype=torch.int32, device=sess.device)
     if sparse:
         sess.select(q, policy=policy_of(spec), alpha=spec.alpha, scale=spec.scale, top_k=spec.top_k,
-                    delta=spec.delta, per_head=per_head)
+                    delta=spec.delta, per_head=per_head, min_pages=spec.min_pages)
     sess.decode(q, alpha=spec.alpha, scale=spec.scale, sparse=sparse, support_idx=supp, support_cap=SUPPORT_CAP)
     torch.cuda.synchronize()
     res = {
@@ -66,7 +66,7 @@ def check_step(spec, res, q_np, units, sparse=True, kv_cache=None, heads_per_uni
             else:
                 uo.gauss()
                 check_tau_hat(res["tau_hat"][b, uo.heads], uo.tau_hat)
-                check_gauss_sel(gsel, uo.margin, spec.delta, uo.tau_hat)
+                check_gauss_sel(gsel, uo.margin, spec.delta, uo.tau_hat, spec.min_pages)
             tokens = odecode.pages_to_tokens(gsel, L, spec.page_size)
         else:
             tokens = np.arange(L)

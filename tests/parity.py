@@ -91,21 +91,35 @@ def check_tau_hat(gpu_tau_hat, tau_hat):
         assert abs(a - b) <= 1e-5 * max(1.0, abs(b)), f"tau_hat {a} vs {b}"
 
 
-def check_gauss_sel(gpu_sel, margin, delta, tau_hat):
+def check_gauss_sel(gpu_sel, margin, delta, tau_hat, min_pages=1):
+    """Keep rule max_h(e_hat - tau_hat) > -delta with a floor of
+    min(min_pages, n) pages (the largest margins), decisions compared
+    outside the band |margin + delta| <= 1e-5 max(1, |tau_hat|) and, for the
+    floor, outside the same band around the oracle's m-th margin."""
     gpu_sel = np.asarray(gpu_sel)
     assert np.all(np.diff(gpu_sel) > 0), "selection not strictly ascending"
     band = 1e-5 * max(1.0, max(abs(t) for t in tau_hat))
-    keep = margin > -delta
-    if not np.any(keep):
-        # floor: one page, the best margin (ties within the band allowed)
-        assert gpu_sel.size == 1
-        assert margin[gpu_sel[0]] >= margin.max() - band
-        return
-    clear_in = np.nonzero(margin + delta > band)[0]
-    clear_out = np.nonzero(margin + delta < -band)[0]
+    m = min(int(min_pages), margin.size)
     s = set(gpu_sel.tolist())
-    assert all(int(p) in s for p in clear_in), "a page clearly above tau_hat - delta is missing"
-    assert not any(int(p) in s for p in clear_out), "a page clearly below tau_hat - delta was kept"
+    sure_in = np.nonzero(margin + delta > band)[0]
+    maybe_in = np.nonzero(margin + delta >= -band)[0]
+    Mm = np.sort(margin)[::-1][m - 1] if m > 0 else np.inf
+    if sure_in.size >= m:  # the rule alone decides
+        clear_out = np.nonzero(margin + delta < -band)[0]
+        assert all(int(p) in s for p in sure_in), "a page clearly above tau_hat - delta is missing"
+        assert not any(int(p) in s for p in clear_out), "a page clearly below tau_hat - delta was kept"
+        return
+    if maybe_in.size < m:  # the floor decides: the m best margins
+        assert gpu_sel.size == m, f"floor kept {gpu_sel.size} pages, expected {m}"
+        assert all(int(p) in s for p in np.nonzero(margin > Mm + band)[0]), "a page clearly above the floor is missing"
+        assert not any(int(p) in s for p in np.nonzero(margin < Mm - band)[0]), "a page clearly below the floor kept"
+        return
+    # rule and floor meet inside the band: at least m pages, every sure page,
+    # nothing clearly below both the rule and the floor
+    assert gpu_sel.size >= m
+    assert all(int(p) in s for p in sure_in), "a page clearly above tau_hat - delta is missing"
+    low = min(-delta, Mm) - band
+    assert not any(int(p) in s for p in np.nonzero(margin < low)[0]), "a page clearly below rule and floor kept"
 
 
 def check_decode(r, q_h, keys, alpha, scale, d, gpu_out, gpu_tau, gpu_psum, gpu_count, gpu_support=None):

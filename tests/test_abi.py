@@ -47,19 +47,29 @@ def seqs(**kw):
     return B._Seqs(**s)
 
 
+def ws_size(L, c=None, s=None, hq=32, cap=0):
+    return L.ekv_workspace_size(ctypes.byref(c or cache()), ctypes.byref(s or seqs()), hq, cap)
+
+
 def test_workspace_size(L):
-    n = L.ekv_workspace_size(ctypes.byref(cache()), ctypes.byref(seqs()), 32)
-    # candidate lists dominate: 4 lists of B*Hq*max_pages*P 4-byte entries
-    assert n >= 4 * 4 * 32 * 256 * 16
-    assert L.ekv_workspace_size(ctypes.byref(cache()), ctypes.byref(seqs()), 12) == 0  # not a multiple of 8
-    assert L.ekv_workspace_size(ctypes.byref(cache(head_dim=96)), ctypes.byref(seqs()), 32) == 0
-    assert L.ekv_workspace_size(ctypes.byref(cache(page_size=24)), ctypes.byref(seqs()), 32) == 0
-    assert L.ekv_workspace_size(ctypes.byref(cache(n_kv_heads=2)), ctypes.byref(seqs()), 64) == 0  # group 32
-    assert L.ekv_workspace_size(None, ctypes.byref(seqs()), 32) == 0
+    n = ws_size(L)
+    # candidate lists dominate: 6 lists of B*Hq*max_pages*P 4-byte entries
+    assert n >= 6 * 4 * 32 * 256 * 16
+    assert ws_size(L, hq=12) == 0  # not a multiple of 8
+    assert ws_size(L, c=cache(head_dim=96)) == 0
+    assert ws_size(L, c=cache(page_size=24)) == 0
+    assert ws_size(L, c=cache(n_kv_heads=2), hq=64) == 0  # group 32
+    assert L.ekv_workspace_size(None, ctypes.byref(seqs()), 32, 0) == 0
+    # sized for lists of 16 pages: the per-item regions shrink 16-fold, the
+    # rest does not depend on cap; cap <= 0 or >= max_pages is the full size
+    small = ws_size(L, cap=16)
+    assert small < n and n - small >= 6 * 4 * 32 * (256 - 16) * 16
+    assert ws_size(L, cap=-1) == n and ws_size(L, cap=256) == n and ws_size(L, cap=10 ** 6) == n
+    assert ws_size(L, cap=8) < small
 
 
 def sp(**kw):
-    p = dict(policy=B.EKV_SELECT_BBOX_TOPK, top_k=8, alpha=1.5, scale=0.125, delta=0.5, per_head=0)
+    p = dict(policy=B.EKV_SELECT_BBOX_TOPK, top_k=8, alpha=1.5, scale=0.125, delta=0.5, per_head=0, min_pages=1)
     p.update(kw)
     return B._SelectParams(**p)
 
@@ -92,6 +102,18 @@ def test_select_validation(L):
     assert call_select(L, p=sp(per_head=2)) == B.EKV_ERR_INVALID_ARG
     # per query head the units are batch * n_q_heads: 200 * 32 = 6400 > 4096
     assert call_select(L, s=seqs(batch=200), p=sp(per_head=1)) == B.EKV_ERR_UNSUPPORTED
+    # the Gaussian floor: at least one page; more than one needs the top-k block's page limit
+    g = dict(policy=B.EKV_SELECT_GAUSS)
+    assert call_select(L, cap=256, p=sp(min_pages=0, **g)) == B.EKV_ERR_INVALID_ARG
+    big = seqs(max_pages=70000)
+    assert call_select(L, s=big, cap=70000, p=sp(min_pages=2, **g)) == B.EKV_ERR_UNSUPPORTED
+    # selection needs only the cap-independent part of the workspace: the
+    # size for one-page lists less its per-item regions (one 64-token item
+    # per query head: three per-item arrays, six per-token arrays, 256-byte
+    # aligned), one byte short
+    a256 = lambda x: (x + 255) // 256 * 256
+    items1 = 3 * a256(4 * 32) + 6 * a256(4 * 32 * 64)
+    assert call_select(L, wsb=ws_size(L, cap=1) - items1 - 1) == B.EKV_ERR_WORKSPACE
 
 
 def call_decode(L, q=FAKE, alpha=1.5, scale=0.125, sel=FAKE, cnt=FAKE, cap=64, sel_heads=8, out=FAKE, sidx=None,
@@ -113,6 +135,12 @@ def test_decode_validation(L):
     assert call_decode(L, c=cache(kv_dtype=5)) == B.EKV_ERR_INVALID_ARG
     assert call_decode(L, sel_heads=5) == B.EKV_ERR_INVALID_ARG  # neither n_kv_heads nor n_q_heads
     assert call_decode(L, sel_heads=32, s=seqs(batch=200)) == B.EKV_ERR_UNSUPPORTED
+    # a workspace sized for 64-page lists serves sparse calls of cap <= 64 only,
+    # and no full-cache decode
+    w64 = ws_size(L, cap=64)
+    assert call_decode(L, cap=65, wsb=w64) == B.EKV_ERR_WORKSPACE
+    assert call_decode(L, sel=None, cnt=None, cap=0, wsb=w64) == B.EKV_ERR_WORKSPACE
+    assert "cap" in ekv.last_error()
 
 
 def test_softmax_validation(L):
@@ -144,4 +172,5 @@ def test_misc(L):
     assert L.ekv_workspace_init(None, 0, None) == B.EKV_ERR_WORKSPACE
     assert L.ekv_workspace_init(FAKE, 17, None) == B.EKV_ERR_WORKSPACE
     flags = ctypes.c_int32(0)
-    assert L.ekv_read_device_status(None, 0, ctypes.byref(flags)) == B.EKV_ERR_WORKSPACE
+    assert L.ekv_read_device_status(None, 0, ctypes.byref(flags), None) == B.EKV_ERR_WORKSPACE
+    assert L.ekv_read_device_status(FAKE, 1 << 20, None, None) == B.EKV_ERR_INVALID_ARG

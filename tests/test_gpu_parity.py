@@ -282,6 +282,23 @@ def test_topk_more_than_32768_equal_scores(top_k):
     assert sess.device_status() == 0
 
 
+@pytest.mark.parametrize("per_head", [False, True])
+@pytest.mark.parametrize("min_pages", [1, 8, 1000])
+def test_gauss_floor_of_several_pages(min_pages, per_head):
+    """Isotropic keys with margin 0: the keep rule keeps no page, so the
+    floor decides (the min_pages largest margins; 1000 is more than the 701
+    pages, which keeps them all), per KV-head group and per query head."""
+    spec = W.make_spec("c2", context=16 * 700 + 5, n_q_heads=8, n_kv_heads=2, n_needles=0, policy="gauss",
+                       delta=0.0, min_pages=min_pages)
+    sess, _ = _session(spec)
+    q = W.queries(spec)
+    res = run_step(sess, spec, q, per_head=per_head)
+    assert np.all(res["cnt"] == min(min_pages, 701))
+    units = [(0, h) for h in range(spec.n_q_heads)] if per_head else all_units(spec)
+    check_step(spec, res, q, units, per_head=per_head)
+    assert sess.device_status() == 0
+
+
 def test_topk_covering_every_page_equals_dense():
     spec = W.make_spec("c2", context=1000, n_q_heads=8, n_kv_heads=2, n_needles=8, top_k=10 ** 6)
     sess, _ = _session(spec)

@@ -161,3 +161,42 @@ def test_alpha_limits_of_the_general_branch():
         np.testing.assert_allclose(near, ref, rtol=1e-7)
     with pytest.raises(ValueError):
         select.gauss_tau_hat(mu, sd, np.array([1, 1, 1]), 2.5)
+
+
+def test_keep_floor_of_several_pages_brute_force():
+    """With a floor of m pages: the kept set when it holds at least
+    min(m, n) pages, else the min(m, n)-subset of largest margin sum, the
+    lexicographically first on ties (brute force over all subsets)."""
+    import itertools
+    rng = np.random.default_rng(23)
+    for _ in range(200):
+        n, G = int(rng.integers(1, 9)), int(rng.integers(1, 4))
+        e = rng.integers(-4, 3, (G, n)).astype(float) * 0.5  # coarse values force ties
+        tau = rng.integers(-2, 3, G).astype(float) * 0.5
+        delta, m = 0.5, int(rng.integers(1, n + 3))
+        got = select.gauss_keep_pages(e, tau, delta, m)
+        margin = np.max(e - tau[:, None], axis=0)
+        kept = [p for p in range(n) if margin[p] > -delta]
+        mm = min(m, n)
+        if len(kept) >= mm:
+            assert list(got) == kept
+            continue
+        best = None
+        for sub in itertools.combinations(range(n), mm):
+            sc = margin[list(sub)].sum()
+            if best is None or sc > best[0]:
+                best = (sc, sub)
+        assert list(got) == list(best[1])
+        assert set(kept) <= set(got.tolist())
+
+
+def test_keep_floor_hand_case():
+    # margins (one head, tau 0): [-1, -3, -0.5, -2]; delta 0.25 keeps nothing
+    e = np.array([[-1.0, -3.0, -0.5, -2.0]])
+    np.testing.assert_array_equal(select.gauss_keep_pages(e, np.array([0.0]), 0.25, 1), [2])
+    np.testing.assert_array_equal(select.gauss_keep_pages(e, np.array([0.0]), 0.25, 2), [0, 2])
+    np.testing.assert_array_equal(select.gauss_keep_pages(e, np.array([0.0]), 0.25, 3), [0, 2, 3])
+    np.testing.assert_array_equal(select.gauss_keep_pages(e, np.array([0.0]), 0.25, 9), [0, 1, 2, 3])
+    # delta 1.5 keeps pages 0 and 2: a floor of 2 changes nothing, 3 adds page 3
+    np.testing.assert_array_equal(select.gauss_keep_pages(e, np.array([0.0]), 1.5, 2), [0, 2])
+    np.testing.assert_array_equal(select.gauss_keep_pages(e, np.array([0.0]), 1.5, 3), [0, 2, 3])

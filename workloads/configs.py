@@ -53,6 +53,7 @@ class WorkloadSpec:
     policy: str              # "bbox" or "gauss"
     top_k: int = 0
     delta: float = 0.5
+    min_pages: int = 1       # Gaussian selector: fewest pages kept per unit
     key_kind: str = "needles"  # "needles" or "clusters"
     n_needles: int = 0       # per KV head
     needle_amp: float = 3.0
