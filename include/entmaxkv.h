@@ -250,6 +250,30 @@ ekv_status ekv_entmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const
                              void* stream);
 
 /*
+ * ekv_entmax_decode without a workspace, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, kernels and results as
+ * ekv_entmax_decode, except:
+ *   - scratch: a fixed 64 MiB device array inside the library, one per
+ *     device, held from the library's load until the process ends.  Its
+ *     per-item regions take 6 * 64 * 4 + 12 = 1548 bytes per (sequence, query
+ *     head, 64-token item of the longest list): a call whose lists (cap pages,
+ *     or the whole cache when sel == NULL) need more returns
+ *     EKV_ERR_WORKSPACE before launching anything.  The call allocates
+ *     nothing.
+ *   - dev_status: optional device uint32; the EKV_DEV_* bits of this call are
+ *     OR-ed into it (the caller clears it).  With NULL they are not reported.
+ * Every call on a device shares that device's scratch, which keeps the last
+ * call's contents: calls that overlap on one device (other streams, other
+ * threads) race and must be ordered by the caller.
+ */
+ekv_status ekv_entmax_decode_noalloc(const ekv_cache* cache, const ekv_seqs* seqs, const float* q,
+                                     int32_t n_q_heads, float alpha, float scale, const int32_t* sel,
+                                     const int32_t* sel_count, int32_t cap, int32_t sel_heads, float* out,
+                                     float* tau, int32_t* support_count, float* psum, int32_t* support_idx,
+                                     float* support_p, int32_t support_cap, uint32_t* dev_status, void* stream);
+
+/*
  * Softmax attention decode over the same page list, the baseline the
  * EntmaxKV summary compares against (sec. 1 and 3: softmax gives every
  * token a positive weight, so a dropped page always leaves some error):

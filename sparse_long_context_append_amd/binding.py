@@ -63,6 +63,8 @@ _SIGS = {
     "ekv_select_pages": (_i32, [_PC, _PS, _vp, _i32, _PP, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
     "ekv_entmax_decode": (_i32, [_PC, _PS, _vp, _i32, ctypes.c_float, ctypes.c_float, _vp, _vp, _i32, _i32,
                                  _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
+    "ekv_entmax_decode_noalloc": (_i32, [_PC, _PS, _vp, _i32, ctypes.c_float, ctypes.c_float, _vp, _vp, _i32,
+                                         _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp]),
     "ekv_softmax_decode": (_i32, [_PC, _PS, _vp, _i32, ctypes.c_float, _vp, _vp, _i32, _i32, _vp, _vp, _vp,
                                   _sz, _vp]),
     "ekv_score_pages": (_i32, [_PC, _PS, _vp, _i32, _PP, _vp, _vp, _sz, _vp]),
@@ -211,6 +213,19 @@ def entmax_decode(cache: PagedCache, seqs: Sequences, q, n_q_heads: int, *, alph
                                    _ptr(tau), _ptr(support_count), _ptr(psum), _ptr(support_idx),
                                    _ptr(support_p), support_cap, _ptr(ws), ws.numel() * ws.element_size(),
                                    _stream(stream)), "entmax_decode")
+
+
+def entmax_decode_noalloc(cache: PagedCache, seqs: Sequences, q, n_q_heads: int, *, alpha: float, scale: float,
+                          sel=None, sel_count=None, cap: int = 0, sel_heads=None, out, tau=None,
+                          support_count=None, psum=None, support_idx=None, support_p=None, support_cap: int = 0,
+                          dev_status=None, stream=None):
+    """entmax_decode on the library's fixed device scratch (no workspace)."""
+    _check(lib().ekv_entmax_decode_noalloc(ctypes.byref(cache.c()), ctypes.byref(seqs.c()), _ptr(q), n_q_heads,
+                                           float(alpha), float(scale), _ptr(sel), _ptr(sel_count), cap,
+                                           _sel_heads(cache, sel, sel_heads), _ptr(out), _ptr(tau),
+                                           _ptr(support_count), _ptr(psum), _ptr(support_idx), _ptr(support_p),
+                                           support_cap, _ptr(dev_status), _stream(stream)),
+           "entmax_decode_noalloc")
 
 
 def softmax_decode(cache: PagedCache, seqs: Sequences, q, n_q_heads: int, *, scale: float, sel=None,

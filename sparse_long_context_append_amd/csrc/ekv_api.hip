@@ -4,9 +4,17 @@
 #include <math.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "ekv_kernels.h"
+
+// Fixed device scratch of ekv_entmax_decode_noalloc: every device the
+// library runs on holds one copy, for the life of the process.  Host code
+// never uses the name as an address: the per-device address comes from
+// hipGetSymbolAddress (static_scratch below).
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -104,6 +112,28 @@ template <typename Args> Args per_query_head_view(const Args& a) {
   u.group = 1;
   u.kv_shift = shift;
   return u;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+ekv_status static_scratch(void** addr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(EKV_ERR_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol, "scratch address");
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return EKV_OK;
 }
 
 }  // namespace
@@ -255,11 +285,11 @@ ekv_status ekv_score_pages(const ekv_cache* cache, const ekv_seqs* seqs, const f
   return hip_status(ekv::launch_score_gauss(a, s), "score_gauss launch");
 }
 
-// Validation and argument packing shared by the two decode entry points.
+// Validation and argument packing shared by the decode entry points (the
+// workspace-dependent fields are filled in by the caller).
 ekv_status prepare_decode(const ekv_cache* cache, const ekv_seqs* seqs, const float* q, int32_t n_q_heads,
                           float alpha, float scale, const int32_t* sel, const int32_t* sel_count, int32_t cap,
-                          int32_t sel_heads, float* out, void* workspace, size_t ws_bytes, bool items,
-                          ekv::DecodeArgs* a, ekv::Layout* L) {
+                          int32_t sel_heads, float* out, ekv::DecodeArgs* a) {
   ekv_status st;
   int G = 0;
   if ((st = check_cache(cache)) != EKV_OK) return st;
@@ -275,9 +305,6 @@ ekv_status prepare_decode(const ekv_cache* cache, const ekv_seqs* seqs, const fl
   const bool per_head = sel && sel_heads == n_q_heads && G > 1;
   if (per_head && (long long)seqs->batch * n_q_heads > ekv::kMaxUnits)
     return fail(EKV_ERR_UNSUPPORTED, "per-query-head page lists need batch * n_q_heads <= 4096");
-  if ((st = check_ws(cache, seqs, n_q_heads, workspace, ws_bytes, list_pages(seqs, sel ? cap : 0), items, L)) !=
-      EKV_OK)
-    return st;
   *a = ekv::DecodeArgs{};
   a->batch = seqs->batch; a->n_kv_heads = cache->n_kv_heads; a->n_q_heads = n_q_heads; a->group = G;
   a->hkv_mem = cache->n_kv_heads; a->kv_shift = 0; a->sel_shift = 0;
@@ -287,10 +314,32 @@ ekv_status prepare_decode(const ekv_cache* cache, const ekv_seqs* seqs, const fl
   a->k = cache->k; a->v = cache->v; a->q = q; a->alpha = alpha; a->scale = scale;
   a->sel = sel; a->sel_count = sel_count; a->cap = sel ? cap : 0;
   a->out = out;
-  a->max_items = (int)L->max_items;
-  a->status = at<uint32_t>(workspace, L->status);
   if (per_head) *a = per_query_head_view(*a);
   return EKV_OK;
+}
+
+// The optional outputs of an entmax decode.
+ekv_status decode_outputs(ekv::DecodeArgs* a, float* tau, int32_t* support_count, float* psum, int32_t* support_idx,
+                          float* support_p, int32_t support_cap) {
+  if ((support_idx || support_p) && support_cap < 1)
+    return fail(EKV_ERR_INVALID_ARG, "support_idx/support_p need support_cap >= 1");
+  a->tau = tau; a->support_count = support_count; a->psum = psum;
+  a->support_idx = support_idx; a->support_p = support_p; a->support_cap = support_cap;
+  return EKV_OK;
+}
+
+// The per-item regions of layout L inside the buffer at `base`.
+void decode_regions(ekv::DecodeArgs* a, void* base, const ekv::Layout& L) {
+  a->max_items = (int)L.max_items;
+  a->item_cnt = at<int32_t>(base, L.item_cnt);
+  a->item_max = at<float>(base, L.item_max);
+  a->item_lb = at<float>(base, L.item_lb);
+  a->cand_x = at<float>(base, L.cand_x);
+  a->cand_t = at<int32_t>(base, L.cand_t);
+  a->cand_r = at<int32_t>(base, L.cand_r);
+  a->ovf_x = at<float>(base, L.ovf_x);
+  a->ovf_t = at<int32_t>(base, L.ovf_t);
+  a->ovf_r = at<int32_t>(base, L.ovf_r);
 }
 
 ekv_status ekv_entmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const float* q, int32_t n_q_heads,
@@ -300,24 +349,45 @@ ekv_status ekv_entmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const
                              size_t ws_bytes, void* stream) {
   ekv::DecodeArgs a;
   ekv::Layout L;
-  ekv_status st = prepare_decode(cache, seqs, q, n_q_heads, alpha, scale, sel, sel_count, cap, sel_heads, out,
-                                 workspace, ws_bytes, true, &a, &L);
+  ekv_status st = prepare_decode(cache, seqs, q, n_q_heads, alpha, scale, sel, sel_count, cap, sel_heads, out, &a);
   if (st != EKV_OK) return st;
-  if ((support_idx || support_p) && support_cap < 1)
-    return fail(EKV_ERR_INVALID_ARG, "support_idx/support_p need support_cap >= 1");
-  a.tau = tau; a.support_count = support_count; a.psum = psum;
-  a.support_idx = support_idx; a.support_p = support_p; a.support_cap = support_cap;
-  a.item_cnt = at<int32_t>(workspace, L.item_cnt);
-  a.item_max = at<float>(workspace, L.item_max);
-  a.item_lb = at<float>(workspace, L.item_lb);
-  a.cand_x = at<float>(workspace, L.cand_x);
-  a.cand_t = at<int32_t>(workspace, L.cand_t);
-  a.cand_r = at<int32_t>(workspace, L.cand_r);
-  a.ovf_x = at<float>(workspace, L.ovf_x);
-  a.ovf_t = at<int32_t>(workspace, L.ovf_t);
-  a.ovf_r = at<int32_t>(workspace, L.ovf_r);
+  if ((st = decode_outputs(&a, tau, support_count, psum, support_idx, support_p, support_cap)) != EKV_OK) return st;
+  if ((st = check_ws(cache, seqs, n_q_heads, workspace, ws_bytes, list_pages(seqs, sel ? cap : 0), true, &L)) !=
+      EKV_OK)
+    return st;
+  a.status = at<uint32_t>(workspace, L.status);
+  decode_regions(&a, workspace, L);
   // about 4 gather blocks per compute unit (one resident wave of blocks)
   return hip_status(ekv::launch_decode(a, 4 * device_cus(), (hipStream_t)stream), "entmax_decode launch");
+}
+
+ekv_status ekv_entmax_decode_noalloc(const ekv_cache* cache, const ekv_seqs* seqs, const float* q,
+                                     int32_t n_q_heads, float alpha, float scale, const int32_t* sel,
+                                     const int32_t* sel_count, int32_t cap, int32_t sel_heads, float* out, float* tau,
+                                     int32_t* support_count, float* psum, int32_t* support_idx, float* support_p,
+                                     int32_t support_cap, uint32_t* dev_status, void* stream) {
+  ekv::DecodeArgs a;
+  ekv_status st = prepare_decode(cache, seqs, q, n_q_heads, alpha, scale, sel, sel_count, cap, sel_heads, out, &a);
+  if (st != EKV_OK) return st;
+  if ((st = decode_outputs(&a, tau, support_count, psum, support_idx, support_p, support_cap)) != EKV_OK) return st;
+  const ekv::Layout L = ekv::make_decode_layout(seqs->batch, n_q_heads, cache->page_size,
+                                                list_pages(seqs, sel ? cap : 0));
+  if (L.total > kStaticScratchBytes)
+    return fail(EKV_ERR_WORKSPACE, "entmax_decode_noalloc: this call needs " + std::to_string(L.total) +
+                                       " bytes of scratch, above its fixed " + std::to_string(kStaticScratchBytes) +
+                                       " (fewer query heads or sequences, or a smaller cap)");
+  void* base = nullptr;
+  if ((st = static_scratch(&base)) != EKV_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (dev_status) {
+    a.status = dev_status;
+  } else {
+    // the status word of the scratch, cleared for this call (no report)
+    a.status = at<uint32_t>(base, L.status);
+    if ((st = hip_status(ekv::launch_fill_zero(a.status, 16, s), "scratch status clear")) != EKV_OK) return st;
+  }
+  decode_regions(&a, base, L);
+  return hip_status(ekv::launch_decode(a, 4 * device_cus(), s), "entmax_decode_noalloc launch");
 }
 
 ekv_status ekv_softmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const float* q, int32_t n_q_heads,
@@ -326,9 +396,10 @@ ekv_status ekv_softmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, cons
                               void* stream) {
   ekv::DecodeArgs a;
   ekv::Layout L;
-  ekv_status st = prepare_decode(cache, seqs, q, n_q_heads, 2.0f, scale, sel, sel_count, cap, sel_heads, out,
-                                 workspace, ws_bytes, false, &a, &L);
+  ekv_status st = prepare_decode(cache, seqs, q, n_q_heads, 2.0f, scale, sel, sel_count, cap, sel_heads, out, &a);
   if (st != EKV_OK) return st;
+  if ((st = check_ws(cache, seqs, n_q_heads, workspace, ws_bytes, 1, false, &L)) != EKV_OK) return st;
+  a.status = at<uint32_t>(workspace, L.status);
   if (cache->kv_dtype != EKV_BF16) return fail(EKV_ERR_UNSUPPORTED, "softmax decode needs bf16 keys/values");
   if (a.group == 8) {
     // the kernels hold four heads per unit: split each query group in two

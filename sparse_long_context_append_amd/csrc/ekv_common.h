@@ -50,6 +50,23 @@ inline int score_stride(int max_pages) { return (max_pages + 3) & ~3; }
 
 constexpr int kSmxMaxSlots = 256;  // softmax decode blocks per (sequence, KV head), at most
 
+// The entmax decode's per-item regions for B * Hq query heads and lists of
+// up to item_pages pages, carved from offset `off` on.
+inline size_t carve_items(Layout& L, size_t off, size_t bh, int P, int item_pages) {
+  L.max_items = (size_t(item_pages) * P + kItemTokens - 1) / kItemTokens;
+  const size_t tok = L.max_items * kItemTokens;
+  L.item_cnt = off; off = align256(off + 4 * bh * L.max_items);
+  L.item_max = off; off = align256(off + 4 * bh * L.max_items);
+  L.item_lb = off;  off = align256(off + 4 * bh * L.max_items);
+  L.cand_x = off;   off = align256(off + 4 * bh * tok);
+  L.cand_t = off;   off = align256(off + 4 * bh * tok);
+  L.cand_r = off;   off = align256(off + 4 * bh * tok);
+  L.ovf_x = off;    off = align256(off + 4 * bh * tok);
+  L.ovf_t = off;    off = align256(off + 4 * bh * tok);
+  L.ovf_r = off;    off = align256(off + 4 * bh * tok);
+  return off;
+}
+
 // item_pages: the longest page list an entmax decode on this workspace
 // reads (the list capacity of sparse calls; max_pages for the full cache).
 // Everything before item_cnt is independent of it.
@@ -58,8 +75,6 @@ inline Layout make_layout(int B, int Hkv, int Hq, int max_pages, int P, int D, i
   Layout L{};
   size_t off = 0;
   const size_t bh = size_t(B) * Hq;
-  L.max_items = (size_t(item_pages) * P + kItemTokens - 1) / kItemTokens;
-  const size_t tok = L.max_items * kItemTokens;
   L.status = off;   off = align256(off + 4);
   // selection units are (sequence, KV head), or (sequence, query head) in
   // per-query-head mode: size the per-unit arrays for the larger count
@@ -70,16 +85,16 @@ inline Layout make_layout(int B, int Hkv, int Hq, int max_pages, int P, int D, i
   L.tau_hat = off;  off = align256(off + 8 * bh);
   L.keep_bits = off; off = align256(off + 8 * bh * keep_words(max_pages));
   L.smx_part = off; off = align256(off + 4 * bh * kSmxMaxSlots * size_t(D + 2));
-  L.item_cnt = off; off = align256(off + 4 * bh * L.max_items);
-  L.item_max = off; off = align256(off + 4 * bh * L.max_items);
-  L.item_lb = off;  off = align256(off + 4 * bh * L.max_items);
-  L.cand_x = off;   off = align256(off + 4 * bh * tok);
-  L.cand_t = off;   off = align256(off + 4 * bh * tok);
-  L.cand_r = off;   off = align256(off + 4 * bh * tok);
-  L.ovf_x = off;    off = align256(off + 4 * bh * tok);
-  L.ovf_t = off;    off = align256(off + 4 * bh * tok);
-  L.ovf_r = off;    off = align256(off + 4 * bh * tok);
-  L.total = off;
+  L.total = carve_items(L, off, bh, P, item_pages);
+  return L;
+}
+
+// Only what the entmax decode uses: the status word, then the per-item
+// regions (the selection and softmax regions are left out).
+inline Layout make_decode_layout(int B, int Hq, int P, int item_pages) {
+  Layout L{};
+  L.status = 0;
+  L.total = carve_items(L, 256, size_t(B) * Hq, P, item_pages);
   return L;
 }
 

@@ -174,3 +174,18 @@ def test_misc(L):
     flags = ctypes.c_int32(0)
     assert L.ekv_read_device_status(None, 0, ctypes.byref(flags), None) == B.EKV_ERR_WORKSPACE
     assert L.ekv_read_device_status(FAKE, 1 << 20, None, None) == B.EKV_ERR_INVALID_ARG
+
+
+def test_noalloc_decode_validation(L):
+    f = L.ekv_entmax_decode_noalloc
+    call = lambda s=None, sel=FAKE, cnt=FAKE, cap=64, out=FAKE, alpha=1.5: f(
+        ctypes.byref(cache()), ctypes.byref(s or seqs()), FAKE, 32, alpha, 0.125, sel, cnt, cap, 8, out, None, None,
+        None, None, None, 0, None, None)
+    assert call(out=None) == B.EKV_ERR_INVALID_ARG
+    assert call(alpha=1.0) == B.EKV_ERR_INVALID_ARG
+    assert call(cnt=None) == B.EKV_ERR_INVALID_ARG
+    # 32 query heads x lists of 65536 pages of 16 tokens: far above the fixed scratch
+    big = seqs(max_pages=65536)
+    assert call(s=big, cap=65536) == B.EKV_ERR_WORKSPACE
+    assert call(s=big, sel=None, cnt=None, cap=0) == B.EKV_ERR_WORKSPACE
+    assert "scratch" in ekv.last_error()
