@@ -26,7 +26,6 @@ struct Layout {
   size_t musd;      // float2 [B*Hq*max_pages] Gaussian page score (mean_Y, sd_Y)
   size_t ehat;      // f32 [B*Hq*max_pages] estimated page maximum
   size_t tau_hat;   // f64 [B*Hq]
-  size_t keep_bits; // u64 [B*Hq][keep_words(max_pages)] Gaussian keep bitmaps
   size_t smx_part;  // f32 [B*Hq][kSmxMaxSlots][head_dim + 2] softmax block partials
   // the entmax decode's per-item regions, sized for lists of item_pages pages
   size_t item_cnt;  // i32 [B*Hq*max_items] candidates kept by each decode work item
@@ -43,8 +42,6 @@ struct Layout {
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-// 64-bit words of a per-page bitmap
-inline int keep_words(int max_pages) { return (max_pages + 63) / 64; }
 // row stride of the internal page-score buffer: 16-byte aligned rows
 inline int score_stride(int max_pages) { return (max_pages + 3) & ~3; }
 
@@ -83,7 +80,6 @@ inline Layout make_layout(int B, int Hkv, int Hq, int max_pages, int P, int D, i
   L.musd = off;     off = align256(off + 8 * bh * max_pages);
   L.ehat = off;     off = align256(off + 4 * bh * max_pages);
   L.tau_hat = off;  off = align256(off + 8 * bh);
-  L.keep_bits = off; off = align256(off + 8 * bh * keep_words(max_pages));
   L.smx_part = off; off = align256(off + 4 * bh * kSmxMaxSlots * size_t(D + 2));
   L.total = carve_items(L, off, bh, P, item_pages);
   return L;
@@ -406,6 +402,15 @@ __device__ inline uint32_t block_exclusive_scan_u32(uint32_t v, uint32_t* red, u
   }
   *total = tot;
   return before + inc - v;
+}
+
+// p[i] for i < n, else `fill`, read from p[min(i, n - 1)] (p[0] when n is
+// 0, which must be readable) without a branch: guarded loads written this
+// way are issued back to back, where a branch around each load costs a
+// wait for it.
+template <typename T> __device__ __forceinline__ T load_or(const T* p, int i, int n, T fill) {
+  const T v = p[i < n ? i : (n > 0 ? n - 1 : 0)];
+  return i < n ? v : fill;
 }
 
 // Number of pages of a sequence of length L.

@@ -29,15 +29,6 @@ constexpr int kCollectU = 16;  // items per wave per on-chip collection round
 constexpr int kVRows = 8;      // V rows in flight per thread in the weighted sum
 constexpr int kSolveBatch = 8; // scores loaded at once per thread in a threshold pass
 
-// p[i] for i < n, else `fill`, read from p[min(i, n - 1)] (p[0] when n is
-// 0, which must be readable) without a branch: guarded loads written this
-// way are issued back to back, where a branch around each load costs a
-// wait for it.
-template <typename T> __device__ __forceinline__ T load_or(const T* p, int i, int n, T fill) {
-  const T v = p[i < n ? i : (n > 0 ? n - 1 : 0)];
-  return i < n ? v : fill;
-}
-
 // A stored length clamped to [0, max_pages * P].
 __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int L) {
   if (L < 0 || (long long)L > (long long)a.max_pages * a.page_size) return L < 0 ? 0 : a.max_pages * a.page_size;

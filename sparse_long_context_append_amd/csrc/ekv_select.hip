@@ -728,7 +728,7 @@ __device__ void gauss_floor_unit(const SelectArgs& a, int b, int g, int n_b, int
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const size_t bh = (size_t)b * a.n_q_heads + (size_t)g * G + h;
-    tau[h] = a.tau_hat[bh];
+    tau[h] = __hip_atomic_load(a.tau_hat + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // written by the group's other blocks
     eh[h] = a.ehat + bh * a.max_pages;
   }
   double best = -INFINITY;
@@ -772,8 +772,6 @@ __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void t
   const int n_b = pages_of(L, P);
   const size_t bh = (size_t)b * a.n_q_heads + h;
   const float2* st = a.musd + bh * a.max_pages;
-  const float* eh = a.ehat + bh * a.max_pages;
-  uint64_t* kbits = a.keep_bits + bh * a.keep_words;
   __shared__ float2 live[LIVE];
   __shared__ MomTable<GEN> mom;
   __shared__ double part[2][NW][3];
@@ -782,13 +780,6 @@ __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void t
   __shared__ int s_last;
   double t = 0.0;
   const bool in_regs = n_b <= PPT * kTauHatThreads;
-  // the general-alpha instance re-reads the estimated maxima for the keep
-  // test instead of holding them through the iteration: its quadrature
-  // needs the registers
-  const bool er_regs = !GEN && in_regs;
-  float er[PPT];  // this thread's estimated maxima (pages tid + 1024 i)
-#pragma unroll
-  for (int i = 0; i < PPT; ++i) er[i] = -INFINITY;
   if (n_b > 0) {
     const int mode = GEN ? 2 : (a.alpha == 1.5f ? 1 : 0);
     const float beta = 1.f / (a.alpha - 1.f);
@@ -810,7 +801,6 @@ __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void t
       for (int i = 0; i < PPT; ++i) {
         const int p = i * kTauHatThreads + tid;
         ms[i] = p < n_b ? st[p] : make_float2(-INFINITY, 0.f);
-        if (!GEN) er[i] = p < n_b ? eh[p] : -INFINITY;
         if (p < n_b) lb = fmax(lb, bound(ms[i], p));
       }
     } else {
@@ -923,25 +913,6 @@ __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void t
       if (stop) break;
     }
   }
-  // this head's keep decisions as a bitmap (bit p: e_hat_p - tau_hat > -delta)
-  const double ndelta = -(double)a.delta;
-  const int nwords = (n_b + 63) / 64;
-  if (er_regs) {
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int p0 = i * kTauHatThreads + w * kWave;  // this wave's 64 pages
-      if (p0 < n_b) {
-        const unsigned long long bal = __ballot(p0 + lane < n_b && (double)er[i] - t > ndelta);
-        if (lane == 0) st_dev(kbits + p0 / 64, (uint64_t)bal);
-      }
-    }
-  } else {
-    for (int p0 = w * kWave; p0 < n_b; p0 += kTauHatThreads) {
-      const int p = p0 + lane;
-      const unsigned long long bal = __ballot(p < n_b && (double)eh[p] - t > ndelta);
-      if (lane == 0) st_dev(kbits + p0 / 64, (uint64_t)bal);
-    }
-  }
   if (tid == 0) {
     st_dev(a.tau_hat + bh, t);  // read by the group's last block
     if (a.tau_hat_out) a.tau_hat_out[bh] = (float)t;
@@ -949,39 +920,78 @@ __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void t
   wait_mem();  // every wave's device-scope stores have completed
   __syncthreads();
   if (tid == 0) {
-    // release: the bitmaps and tau_hat above are visible at agent scope
-    // before the arrival is; the last block's acquire below pairs with it
+    // release: tau_hat above is visible at agent scope before the arrival is
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     s_last = atomicAdd(a.done + unit, 1u) == (uint32_t)(G - 1);
   }
   __syncthreads();
   if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // The last block reads the other heads' tau_hat with agent-scope atomic
+  // loads, which return the coherent value: each writer's store completed
+  // before its release and arrival, and this block saw every arrival.  (An
+  // acquire fence here would invalidate this compute unit's caches and
+  // slow the loads below by microseconds.)  The estimated maxima come from
+  // the scoring kernel, which finished before this one started.
   if (tid == 0) st_dev(a.done + unit, 0u);  // ready for the next call
 
-  // ---- the group's last block: union of the heads' bitmaps, ascending ids ----
+  // ---- the group's last block: the pages some head keeps, ascending ids.
+  // Pages go in chunks of 64 (chunk c: pages 64 c .. 64 c + 63), wave w
+  // taking chunks w, w + NW, ...: lane l reads page 64 c + l of each head
+  // (one coalesced row per load), the keep decisions of a chunk are one
+  // ballot, and one scan over the chunks' counts places every kept page.
+  // Sequences of more than 64 Ki pages go in passes of 1024 chunks. ----
   int32_t* out = a.sel + (size_t)unit * a.cap;
   if (n_b == 0) {
     if (tid == 0) a.sel_count[unit] = 0;
     return;
   }
-  const uint64_t* kb0 = a.keep_bits + ((size_t)b * a.n_q_heads + (size_t)g * G) * a.keep_words;
-  int run = 0;
-  for (int w0 = 0; w0 < nwords; w0 += kTauHatThreads) {
-    const int wi = w0 + tid;
-    uint64_t word = 0;
-    if (wi < nwords) {
+  double tg[G];
+  const float* ehg[G];
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) word |= kb0[(size_t)hh * a.keep_words + wi];
+  for (int hh = 0; hh < G; ++hh) {
+    const size_t bhh = (size_t)b * a.n_q_heads + (size_t)g * G + hh;
+    tg[hh] = __hip_atomic_load(a.tau_hat + bhh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ehg[hh] = a.ehat + bhh * a.max_pages;
+  }
+  const double ndelta = -(double)a.delta;
+  uint64_t* s_mask = reinterpret_cast<uint64_t*>(live);  // the live list is no longer needed
+  int* s_off = reinterpret_cast<int*>(s_mask + kTauHatThreads);
+  static_assert(LIVE * sizeof(float2) >= kTauHatThreads * (sizeof(uint64_t) + sizeof(int)), "union scratch");
+  __syncthreads();  // every wave is done with the live list
+  int run = 0;
+  for (int base = 0; base < n_b; base += 64 * kTauHatThreads) {  // block-uniform
+    const int nch = min(kTauHatThreads, (n_b - base + 63) / 64);
+    constexpr int CU = G <= 4 ? 4 : 2;  // chunks per wave whose loads travel together
+    for (int c0 = w; c0 < nch; c0 += CU * NW) {
+      float ev[CU][G];
+#pragma unroll
+      for (int j = 0; j < CU; ++j) {
+        const int p = base + 64 * (c0 + j * NW) + lane;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) ev[j][hh] = load_or(ehg[hh], p, n_b, -INFINITY);
+      }
+#pragma unroll
+      for (int j = 0; j < CU; ++j) {
+        const int c = c0 + j * NW;
+        double mg = -INFINITY;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) mg = fmax(mg, (double)ev[j][hh] - tg[hh]);
+        const uint64_t m = __ballot(mg > ndelta);  // pages past n_b read -inf: never kept
+        if (lane == 0 && c < nch) s_mask[c] = m;
+      }
     }
+    __syncthreads();
+    const int cnt = tid < nch ? __popcll(s_mask[tid]) : 0;
     int tot;
-    int pos = run + block_exclusive_scan(__popcll(word), redi, &tot);
-    while (word) {
-      const int j = __ffsll((unsigned long long)word) - 1;
-      out[pos++] = wi * 64 + j;
-      word &= word - 1;
+    const int off = block_exclusive_scan(cnt, redi, &tot);
+    if (tid < nch) s_off[tid] = run + off;
+    __syncthreads();
+    for (int c = w; c < nch; c += NW) {
+      const uint64_t m = s_mask[c];
+      if ((m >> lane) & 1ull) out[s_off[c] + __popcll(m & ((1ull << lane) - 1ull))] = base + 64 * c + lane;
     }
     run += tot;
+    __syncthreads();  // s_mask / s_off are rewritten by the next pass
   }
   if (run > 0) {
     if (tid == 0) a.sel_count[unit] = run;
