@@ -499,9 +499,42 @@ __global__ __launch_bounds__(kScoreThreads) void score_gauss_kernel(SelectArgs a
 // the group, in ascending order, at least one page (the best margin, lowest
 // id on ties).
 // ---------------------------------------------------------------------------
+// The standard normal density and distribution function at u from one
+// exponential.  erfc is the Chebyshev fit of Press, Teukolsky, Vetterling
+// and Flannery, Numerical Recipes (2nd ed.) sec. 6.2: erfc(z) = t exp(-z^2 +
+// P(t)), t = 1 / (1 + z/2), fractional error below 1.2e-7.  Here z^2 = u^2/2
+// is carried as an exact two-float sum, and exp(-z^2) comes from a
+// Cody-Waite reduction onto the hardware exp2 (about 1e-7 relative), which
+// the density exp(-u^2/2) / sqrt(2 pi) shares.  In fp32 the density and
+// Phi(u <= 0) come out within about 5e-7 relative, Phi(u > 0) within 2e-7
+// absolute, against 50 + 20 instructions for erfcf and expf.
+__device__ __forceinline__ void normal_pdf_cdf(float u, float& pdf, float& cdf) {
+  const float kInvSqrt2 = 0.70710678118654752440f, kInvSqrt2Pi = 0.39894228040143267794f;
+  const float kLog2e = 1.4426950408889634f, kLog2eHi = 1.44269502162933349609375f, kLog2eLo = 1.925963033500011e-08f;
+  const float z = fabsf(u) * kInvSqrt2;
+  const float t = __builtin_amdgcn_rcpf(1.f + 0.5f * z);
+  float p = 0.17087277f;
+  p = fmaf(t, p, -0.82215223f);
+  p = fmaf(t, p, 1.48851587f);
+  p = fmaf(t, p, -1.13520398f);
+  p = fmaf(t, p, 0.27886807f);
+  p = fmaf(t, p, -0.18628806f);
+  p = fmaf(t, p, 0.09678418f);
+  p = fmaf(t, p, 0.37409196f);
+  p = fmaf(t, p, 1.00002368f);
+  p = fmaf(t, p, -1.26551223f);
+  const float u2h = u * u, u2l = fmaf(u, u, -u2h);  // u^2 = u2h + u2l exactly
+  const float z2h = 0.5f * u2h, z2l = 0.5f * u2l;
+  const float n = __builtin_rintf(-z2h * kLog2eHi);
+  const float fr = fmaf(-z2h, kLog2eHi, -n) - z2h * kLog2eLo;
+  const float e1 = __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(fr), (int)n);  // exp(-z2h)
+  const float erfc = t * e1 * __builtin_amdgcn_exp2f((p - z2l) * kLog2e);
+  pdf = e1 * (1.f - z2l) * kInvSqrt2Pi;
+  cdf = u <= 0.f ? 0.5f * erfc : 1.f - 0.5f * erfc;
+}
+
 __device__ __forceinline__ void gauss_mass(float mu, float sd, float tf, bool quad, float& e, float& de,
                                            float& dde) {
-  const float kInvSqrt2 = 0.70710678118654752440f, kInvSqrt2Pi = 0.39894228040143267794f;
   const float am = mu - tf;
   if (sd <= 0.f) {
     const float pos = fmaxf(am, 0.f);
@@ -516,8 +549,8 @@ __device__ __forceinline__ void gauss_mass(float mu, float sd, float tf, bool qu
     e = de = dde = 0.f;
     return;
   }
-  const float Phi = 0.5f * erfcf(-u * kInvSqrt2);
-  const float phi = expf(-0.5f * u * u) * kInvSqrt2Pi;
+  float phi, Phi;
+  normal_pdf_cdf(u, phi, Phi);
   const float e1 = am * Phi + sd * phi;
   if (quad) {
     e = (am * am + sd * sd) * Phi + am * sd * phi;
