@@ -193,12 +193,15 @@ __device__ __forceinline__ void resolve_refs(const DecodeArgs& a, int u, int b, 
 // which their weights alone reach 1.
 // Evaluated in float and rounded up by a relative 1e-5, so the bound
 // stays below the exact one.
+// The hardware reciprocal, reciprocal square root, exp2 and log2 are within
+// a few ulp (about 1e-6 relative for the exp2/log2 pair), well inside the
+// 1e-5 rounding up.
 __device__ __forceinline__ double count_pow(int n, float alpha) {
   const float nf = (float)n;
   float v;
-  if (alpha == 2.0f) v = 1.f / nf;
-  else if (alpha == 1.5f) v = 1.f / sqrtf(nf);
-  else v = exp2f(-(alpha - 1.f) * log2f(nf));
+  if (alpha == 2.0f) v = __builtin_amdgcn_rcpf(nf);
+  else if (alpha == 1.5f) v = __builtin_amdgcn_rsqf(nf);
+  else v = __builtin_amdgcn_exp2f(-(alpha - 1.f) * __builtin_amdgcn_logf(nf));
   return (double)v * (1.0 + 1e-5);
 }
 
@@ -812,8 +815,6 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
   constexpr int EPL = E::kPerVec;
   constexpr int LPR = D / EPL;
   constexpr int RPB = kTauThreads / LPR;
-  static_assert(RPB * D <= 2048, "vpart");
-  float (*vpart)[D] = reinterpret_cast<float (*)[D]>(sm.vpart);
   __syncthreads();  // sm may still be in use by the caller
 
   const int32_t* icnt = a.item_cnt + bh * a.max_items;
@@ -909,17 +910,17 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
   double thr = fmax(m - 1.0, (double)lbf);
   {
     float lvl[4];
-    double nk[4];
+    int nk[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       lvl[k] = mf - 0.03125f * (float)(1 << k);
-      nk[k] = 0.0;
+      nk[k] = 0;
     }
     if (few_items) {
 #pragma unroll
       for (int i = 0; i < IPT; ++i)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) nk[k] += lmx[i] >= lvl[k] ? 1.0 : 0.0;
+        for (int k = 0; k < 4; ++k) nk[k] += lmx[i] >= lvl[k];
     } else {
       for (int j0 = tid; j0 < n_items; j0 += 8 * kTauThreads) {
         float vm[8];
@@ -931,14 +932,32 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
 #pragma unroll
         for (int u = 0; u < 8; ++u)
 #pragma unroll
-          for (int k = 0; k < 4; ++k) nk[k] += vm[u] >= lvl[k] ? 1.0 : 0.0;
+          for (int k = 0; k < 4; ++k) nk[k] += vm[u] >= lvl[k];
       }
     }
-    block_sums<4>(nk, redd);
+    // integer block sums of the four counts (one pair of barriers)
+    {
+      constexpr int NWV = kTauThreads / kWave;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) nk[k] = wave_sum(nk[k]);
+      __syncthreads();
+      if ((tid & 63) == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) redi[4 * tid_w + k] = nk[k];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        int t = 0;
+#pragma unroll
+        for (int i = 0; i < NWV; ++i) t += redi[4 * i + k];
+        nk[k] = t;
+      }
+    }
     double cb = -INFINITY;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      if (nk[k] > 0.0) cb = fmax(cb, (double)lvl[k] - count_pow((int)nk[k], a.alpha));
+      if (nk[k] > 0) cb = fmax(cb, (double)lvl[k] - count_pow(nk[k], a.alpha));
     thr = fmax(thr, cb - 1e-6 * fmax(1.0, fabs(m)));
   }
 
@@ -1216,11 +1235,15 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
     int c = 0;
 #pragma unroll
     for (int k = 0; k < EW; ++k) {
-      const int i = min(e0 + k, CAP - 1);  // in the LDS list; masked below
-      xv[k] = xs[i];
-      tv[k] = ts[i];
-      rv[k] = rs[i];
-      if (!(e0 + k < e1)) xv[k] = -INFINITY;
+      xv[k] = -INFINITY;
+      tv[k] = rv[k] = 0;
+      if (k < E) {  // block-uniform: no read past the slots in use
+        const int i = min(e0 + k, CAP - 1);  // in the LDS list; masked below
+        xv[k] = xs[i];
+        tv[k] = ts[i];
+        rv[k] = rs[i];
+        if (!(e0 + k < e1)) xv[k] = -INFINITY;
+      }
       c += (double)xv[k] > tau;
     }
     int pos = block_exclusive_scan(c, redi, &nsup);  // every read above is done
@@ -1326,12 +1349,23 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
       }
     }
   }
+  // the wave's row groups (lanes sub, sub + LPR, ...) by lane exchanges,
+  // then the four waves' partials in order
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) vpart[rr][sub * EPL + e] = acc[e];
+  for (int mask = LPR; mask < kWave; mask <<= 1)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], mask, kWave);
+  constexpr int NWV = kTauThreads / kWave;
+  static_assert(NWV * D <= 2048, "vpart");
+  if ((tid & 63) < LPR) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) sm.vpart[tid_w * D + sub * EPL + e] = acc[e];
+  }
   __syncthreads();
   for (int e = tid; e < D; e += blockDim.x) {
-    float o = 0.f;
-    for (int r = 0; r < RPB; ++r) o += vpart[r][e];
+    float o = sm.vpart[e];
+#pragma unroll
+    for (int w2 = 1; w2 < NWV; ++w2) o += sm.vpart[w2 * D + e];
     out[e] = o;
   }
   if (tid == 0) {
