@@ -409,6 +409,63 @@ def run_sweep(args, torch, timer):
                       "data": "synthetic", "sweep": rows}), flush=True)
 
 
+def run_selectors(args, torch, timer):
+    """Both selectors on the same clustered keys: one sequence of c4g's
+    clustered keys (32/8 heads, d=128, pages of 64, alpha 1.5) at contexts
+    32K..1M; the Gaussian selector (margin 0.5), and bounding-box top-k with
+    a budget of 2% of the pages and with the Gaussian selector's mean kept
+    page count per KV head.  Per variant: step time (select + decode), pages
+    kept, the full-cache entmax mass outside the kept pages (dropped mass)
+    and the share of the full-cache support kept."""
+    import math
+    import sparse_long_context_append_amd as ekv
+    from workloads.upload import build_session, queries_device
+    rows = []
+    SC = 1 << 14
+    for ctx in (1 << 15, 1 << 16, 1 << 17, 1 << 18, 1 << 19, 1 << 20):
+        spec = W.make_spec("c4g", context=ctx)
+        sess, _ = build_session(spec)
+        q = queries_device(spec)
+        B, Hq, G = spec.batch, spec.n_q_heads, spec.group
+        n_pages = -(-ctx // spec.page_size)
+        sidx = torch.full((B, Hq, SC), -1, dtype=torch.int32, device="cuda")
+        sp = torch.zeros((B, Hq, SC), dtype=torch.float32, device="cuda")
+        dense_ms, _ = timer.run(lambda: sess.decode(q, alpha=spec.alpha, scale=spec.scale, sparse=False), 3, 1)
+        sess.decode(q, alpha=spec.alpha, scale=spec.scale, sparse=False, support_idx=sidx, support_p=sp,
+                    support_cap=SC)
+        torch.cuda.synchronize()
+        cnt, ids, ps = sess.support_count.cpu().numpy(), sidx.cpu().numpy(), sp.cpu().numpy()
+
+        def variant(label, policy, k):
+            def step():
+                sess.select(q, policy=policy, alpha=spec.alpha, scale=spec.scale, top_k=k, delta=spec.delta)
+                sess.decode(q, alpha=spec.alpha, scale=spec.scale, sparse=True)
+            ms, _ = timer.run(step, args.steps, args.warmup)
+            step()
+            torch.cuda.synchronize()
+            sel, scnt = sess.sel.cpu().numpy(), sess.sel_count.cpu().numpy()
+            d_ent, keep = _selection_quality(spec, sel, scnt, False, ids, ps, cnt, SC)
+            row = {"context": ctx, "selector": label, "top_k": k if policy == ekv.EKV_SELECT_BBOX_TOPK else None,
+                   "us_per_step": round(statistics.median(ms) * 1e3, 2),
+                   "pages_per_kv_head_mean": round(float(scnt.mean()), 1), "pages_per_kv_head": n_pages,
+                   "dropped_mass_mean": float(d_ent.mean()), "dropped_mass_max": float(d_ent.max()),
+                   "support_retention_mean": float(keep.mean()),
+                   "heads_with_full_support": int((keep == 1.0).sum()), "heads": int(keep.size),
+                   "dense_us": round(statistics.median(dense_ms) * 1e3, 2)}
+            log(f"selectors {ctx} {label}: {row['us_per_step']} us, {row['pages_per_kv_head_mean']} pages, "
+                f"dropped {row['dropped_mass_mean']:.4f}, retention {row['support_retention_mean']:.3f}")
+            return row, scnt
+        r_g, scnt_g = variant("gaussian", ekv.EKV_SELECT_GAUSS, 0)
+        rows.append(r_g)
+        rows.append(variant("topk_2pct", ekv.EKV_SELECT_BBOX_TOPK, math.ceil(0.02 * n_pages))[0])
+        rows.append(variant("topk_matched", ekv.EKV_SELECT_BBOX_TOPK, max(1, int(round(float(scnt_g.mean())))))[0])
+        del sess
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "bounding-box top-k vs the Gaussian selector on the same clustered keys",
+                      "n_gpus": 1, "data": "synthetic", "steps": args.steps, "warmup": args.warmup,
+                      "selectors": rows}), flush=True)
+
+
 def compare_one(spec, args, torch, timer):
     """Entmax and softmax decode over the same selected pages and over the
     whole cache: per query head, the full-cache mass outside the selection
@@ -675,6 +732,10 @@ def main():
     ap.add_argument("--gqa", action="store_true",
                     help="instead of the headline line: shared vs per-query-head selection (dropped mass, "
                          "support retention, output error, pages read, step time) on c2, c3, c4")
+    ap.add_argument("--selectors", action="store_true",
+                    help="instead of the headline line: bounding-box top-k (2%% of pages, and the Gaussian "
+                         "selector's kept-page count) beside the Gaussian selector on the same clustered "
+                         "million-token keys, contexts 32K..1M")
     ap.add_argument("--prefill", action="store_true",
                     help="instead of the headline line: bulk prefill throughput of append_kv (one call per "
                          "sequence: K/V rows and page metadata) at the c4 and c3 shapes")
@@ -702,6 +763,9 @@ def main():
         return
     if args.prefill:
         run_prefill(args, torch, timer)
+        return
+    if args.selectors:
+        run_selectors(args, torch, timer)
         return
     over = {"context": args.context} if args.context else {}
     if args.q_heads:

@@ -251,6 +251,23 @@ def test_topk_at_max_pages():
     assert sess.device_status() == 0
 
 
+@pytest.mark.parametrize("P,top_k", [(32, 40), (64, 12)])
+def test_topk_on_clustered_keys(P, top_k):
+    """Bounding-box top-k on clustered keys (runs of 256 tokens around 64
+    centres, as the Gaussian workloads), with ragged tails; sparse and
+    full-cache decode on every unit."""
+    spec = W.make_spec("c3", batch=2, context=P * 700 + 9, page_size=P, n_q_heads=8, n_kv_heads=2, policy="bbox",
+                       top_k=top_k, alpha=1.5)
+    sess, _ = _session(spec)
+    q = W.queries(spec)
+    cache = {}
+    res = run_step(sess, spec, q)
+    assert np.all(res["cnt"] == top_k)
+    check_step(spec, res, q, all_units(spec), kv_cache=cache)
+    check_step(spec, run_step(sess, spec, q, sparse=False), q, all_units(spec), sparse=False, kv_cache=cache)
+    assert sess.device_status() == 0
+
+
 @pytest.mark.parametrize("top_k", [5, 33000])
 def test_topk_more_than_32768_equal_scores(top_k):
     """40000 one-token pages scored against q = 0: every box bound is exactly
