@@ -1192,6 +1192,63 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
     }
   }
   __syncthreads();
+  if (in_lds && N > kTauThreads) {
+    // Count bound on the candidates themselves.  Bin j holds the candidates
+    // with (m - x) 64 in [j, j + 1) (the last bin everything lower); the
+    // n_j candidates in bins 0..j lie above m - (j + 1)/64, so, one bin of
+    // slack covering the rounding of the bin index, above L_j = m - (j + 2)/64,
+    // and tau >= L_j - n_j^-(alpha-1).  The candidates above the best of
+    // these bounds are kept, in order; usually few enough for the pairwise
+    // test below, where the iterative solve would take a pass per step.
+    int* hist = sm.s_pre;  // (free here)
+    for (int i = tid; i < 256; i += kTauThreads) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < N; i += kTauThreads) {
+      const float d = (mf - lx[i]) * 64.f;
+      atomicAdd(&hist[d < 255.f ? (int)d : 255], 1);
+    }
+    __syncthreads();
+    const int c = tid < 256 ? hist[tid] : 0;
+    int tot;
+    const int excl = block_exclusive_scan(c, redi, &tot);
+    double bnd = -INFINITY;
+    if (tid < 255 && excl + c > 0)
+      bnd = (double)(mf - (float)(tid + 2) * (1.f / 64.f)) - count_pow(excl + c, a.alpha);
+    bnd = block_max(bnd, redd) - 1e-6 * fmax(1.0, fabs(m));
+    if (bnd > thr) {  // block-uniform
+      thr = bnd;
+      constexpr int EW = CAP / kTauThreads;
+      const int E = (N + kTauThreads - 1) / kTauThreads;
+      const int e0 = min(tid * E, N), e1 = min(e0 + E, N);
+      float xv[EW];
+      int tv[EW], rv[EW];
+      int kept = 0;
+#pragma unroll
+      for (int k = 0; k < EW; ++k) {
+        xv[k] = -INFINITY;
+        tv[k] = rv[k] = 0;
+        if (k < E && e0 + k < e1) {
+          xv[k] = lx[e0 + k];
+          tv[k] = lt[e0 + k];
+          rv[k] = lr[e0 + k];
+        }
+        kept += (double)xv[k] > thr;
+      }
+      int n2;
+      int pos = block_exclusive_scan(kept, redi, &n2);  // every read above is done
+#pragma unroll
+      for (int k = 0; k < EW; ++k) {
+        if ((double)xv[k] > thr) {
+          lx[pos] = xv[k];
+          lt[pos] = tv[k];
+          lr[pos] = rv[k];
+          ++pos;
+        }
+      }
+      N = n2;
+      __syncthreads();
+    }
+  }
   float* xs = in_lds ? lx : a.ovf_x + bh * tok_per_bh;
   int32_t* ts = in_lds ? lt : a.ovf_t + bh * tok_per_bh;
   int32_t* rs = in_lds ? lr : a.ovf_r + bh * tok_per_bh;
