@@ -491,8 +491,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_gauss_kernel(SelectArgs a
 // The iteration is Halley's method on log F (alpha 1.5 and 2, where F'' is
 // at hand) or Newton's (other alpha), kept inside a bracket [lo, hi] with
 // F(lo) >= 1 > F(hi) and replaced by bisection whenever it would leave it.
-// Per-page terms are evaluated in fp32 and summed in fp64; the step stops
-// below 2e-7 max(1, |t|).
+// Per-page terms are evaluated in fp32 and summed in fp64; the iteration
+// stops once a step moves t by at most 2e-7 max(1, |t|).  Near the root
+// Halley's method converges cubically (each step about the cube of the one
+// before, in units of the root's scale): a Halley step of at most
+// 1e-4 max(1, |t|) that is also at most 1/100 of the step before it (the
+// iteration is in that regime, not crossing the kink of a page with zero
+// variance) leaves an error far below the tolerance, so it is taken as the
+// last step, without one more evaluation of F to confirm it.
 //
 // The last block of a (sequence, KV head) to finish (arrival counter) keeps
 // the pages whose estimated maximum beats tau_hat - delta for some head of
@@ -865,6 +871,7 @@ __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void t
       __syncthreads();
     }
     double lo = -INFINITY, hi = INFINITY;
+    double prev_step = 0.0;  // the last step's size (wave 0)
     t = t0;
     for (int it = 0; it < 200; ++it) {
       const float tf = (float)t;
@@ -910,7 +917,7 @@ __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void t
           // on g, else bisection of the bracket.  Near the root g comes from
           // its series in F - 1; farther away a float logarithm suffices.
           double cand = t;
-          bool ok = false;
+          bool ok = false, halley = false;
           if (F > 0.0 && dF < 0.0) {
             const double x = F - 1.0;
             const double gl = fabs(x) < 1e-3 ? x * (1.0 - x * (0.5 - x * (1.0 / 3.0 - 0.25 * x)))
@@ -921,11 +928,12 @@ __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void t
             const float r = mode == 2 ? 0.f : (float)(gl * g2 / (g1 * g1));  // 0: Newton
             const float den = 1.f - 0.5f * r;
             const double ch = den > 0.f ? t + (cn - t) * (double)(1.f / den) : cn;  // Halley = Newton / (1 - r/2)
-            if (den > 0.f && ch > lo && ch < hi) { cand = ch; ok = true; }
+            if (den > 0.f && ch > lo && ch < hi) { cand = ch; ok = true; halley = mode != 2; }
             else if (cn > lo && cn < hi) { cand = cn; ok = true; }
             else if (fabs(cn - t) <= tol) { cand = cn; ok = true; }
           }
-          if (ok && fabs(cand - t) <= tol) {
+          const double step = fabs(cand - t);
+          if (ok && (step <= tol || (halley && step <= 1e-4 * fmax(1.0, fabs(t)) && step <= 0.01 * prev_step))) {
             stop = 1;
           } else if (!ok) {
             if (lo > -INFINITY && hi < INFINITY) cand = 0.5 * (lo + hi);
@@ -933,6 +941,7 @@ __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void t
             else cand = lo + fmax(1.0, fabs(lo));
           }
           if (!stop && hi - lo <= tol) stop = 1;
+          prev_step = ok ? step : 0.0;
           t = cand;
         }
         if (lane == 0) {
