@@ -830,11 +830,12 @@ __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void t
     // thread t owns pages t, t + 1024, ...: one round of coalesced loads
     float2 ms[PPT];
     double lb = -INFINITY;
-    auto bound = [&](float2 v, int p) {
-      const double n = p == n_b - 1 ? (double)last_n : (double)P;
-      const double r = mode == 0 ? 1.0 / n : (mode == 1 ? 1.0 / sqrt(n) : pow(n, -(double)(a.alpha - 1.f)));
-      return (double)v.x - r;
+    // n^-(alpha-1) for a full page and for the last one, once per thread
+    auto count_term = [&](double n) {
+      return mode == 0 ? 1.0 / n : (mode == 1 ? 1.0 / sqrt(n) : pow(n, -(double)(a.alpha - 1.f)));
     };
+    const double r_full = count_term((double)P), r_last = count_term((double)last_n);
+    auto bound = [&](float2 v, int p) { return (double)v.x - (p == n_b - 1 ? r_last : r_full); };
     if (in_regs) {
 #pragma unroll
       for (int i = 0; i < PPT; ++i) {
@@ -987,14 +988,25 @@ __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void t
     if (tid == 0) a.sel_count[unit] = 0;
     return;
   }
-  double tg[G];
   const float* ehg[G];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const size_t bhh = (size_t)b * a.n_q_heads + (size_t)g * G + hh;
-    tg[hh] = __hip_atomic_load(a.tau_hat + bhh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    ehg[hh] = a.ehat + bhh * a.max_pages;
-  }
+  for (int hh = 0; hh < G; ++hh) ehg[hh] = a.ehat + ((size_t)b * a.n_q_heads + (size_t)g * G + hh) * a.max_pages;
+  constexpr int CU = G <= 4 ? 4 : 2;  // chunks per wave whose loads travel together
+  float ev[CU][G];
+  auto load_round = [&](int base, int c0) {
+#pragma unroll
+    for (int j = 0; j < CU; ++j) {
+      const int p = base + 64 * (c0 + j * NW) + lane;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) ev[j][hh] = load_or(ehg[hh], p, n_b, -INFINITY);
+    }
+  };
+  load_round(0, w);  // the first round's estimates travel with the tau_hat loads below
+  double tg[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+    tg[hh] = __hip_atomic_load(a.tau_hat + (size_t)b * a.n_q_heads + (size_t)g * G + hh, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
   const double ndelta = -(double)a.delta;
   uint64_t* s_mask = reinterpret_cast<uint64_t*>(live);  // the live list is no longer needed
   int* s_off = reinterpret_cast<int*>(s_mask + kTauHatThreads);
@@ -1003,15 +1015,8 @@ __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void t
   int run = 0;
   for (int base = 0; base < n_b; base += 64 * kTauHatThreads) {  // block-uniform
     const int nch = min(kTauHatThreads, (n_b - base + 63) / 64);
-    constexpr int CU = G <= 4 ? 4 : 2;  // chunks per wave whose loads travel together
     for (int c0 = w; c0 < nch; c0 += CU * NW) {
-      float ev[CU][G];
-#pragma unroll
-      for (int j = 0; j < CU; ++j) {
-        const int p = base + 64 * (c0 + j * NW) + lane;
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) ev[j][hh] = load_or(ehg[hh], p, n_b, -INFINITY);
-      }
+      if (base > 0 || c0 != w) load_round(base, c0);  // (the first round is in already)
 #pragma unroll
       for (int j = 0; j < CU; ++j) {
         const int c = c0 + j * NW;
