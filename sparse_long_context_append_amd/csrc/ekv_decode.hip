@@ -711,6 +711,16 @@ __device__ double solve_threshold(const float* xs, int N, double m, double thr, 
 // follows from the closed form on the support (alpha 2 or 1.5) or from
 // Newton's method on it, started below tau at the largest excluded score
 // (other alpha).  All threads of the block take part and get the result.
+// tau from the support's count c and the sums s1, s2 of (x - m) and
+// (x - m)^2 over it: sum_S (x - tau) = 1 (alpha 2), sum_S (x - tau)^2 = 1
+// (alpha 1.5, the larger root of the quadratic).
+template <int AK> __device__ __forceinline__ double support_tau(double c, double s1, double s2, double m) {
+  if (AK == 0) return m + (s1 - 1.0) / c;
+  const double mu = s1 / c;
+  const double disc = (1.0 - c * (s2 / c - mu * mu)) / c;
+  return m + mu - sqrt(fmax(disc, 0.0));
+}
+
 template <int AK>
 __device__ double solve_pairwise(const float* xs, int N, double m, float alpha_f, double* red) {
   const int i = threadIdx.x, lane = i & 63;
@@ -748,12 +758,7 @@ __device__ double solve_pairwise(const float* xs, int N, double m, float alpha_f
   const double y = xi - m;
   double c = in ? 1.0 : 0.0, s1 = in ? y : 0.0, s2 = in ? y * y : 0.0;
   block_sum3(c, s1, s2, red);
-  if (sparsemax) return m + (s1 - 1.0) / c;
-  if (ent15) {
-    const double mu = s1 / c;
-    const double disc = (1.0 - c * (s2 / c - mu * mu)) / c;
-    return m + mu - sqrt(fmax(disc, 0.0));
-  }
+  if (sparsemax || ent15) return support_tau<AK>(c, s1, s2, m);
   // other alpha: Newton on g(t) = sum_S (x - t)^beta - 1 from the largest excluded score
   double lo = (has && !in) ? xi : m - 1.0;
   lo = block_max(lo, red);
@@ -780,6 +785,7 @@ __device__ double solve_pairwise(const float* xs, int N, double m, float alpha_f
 // for CAP candidates: kLdsCands, or kLdsCandsBig (about 115 KB) when every
 // block of the launch has a compute unit of its own anyway.
 constexpr int kLdsCandsBig = 8192;
+constexpr int kWaveCands = 128;  // candidates the single-wave threshold path takes (two per lane)
 template <int CAP> struct TauSmem {
   float lx[CAP];
   int lt[CAP];
@@ -791,6 +797,8 @@ template <int CAP> struct TauSmem {
   double redd[48];  // block reductions (up to three values per wave)
   int redi[17];
   double s_tau;
+  double s_ps;  // the single-wave threshold path's outputs
+  int s_nsup;
   uint32_t s_mkey[4];
   int s_kcnt[4];
   int s_flag;
@@ -1256,8 +1264,98 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
   // ---- threshold: one wave when the candidates are few, else the block ----
   double tau;
   double& s_tau = sm.s_tau;
-  // (other alpha: the pairwise test would take N^2 fp64 powers; Newton's
-  // method takes a few passes instead)
+  const double beta = 1.0 / ((double)a.alpha - 1.0);
+  double ps = 0.0;
+  int nsup = 0;
+  auto emit = [&](int pos, double p, int tok) {
+    if (a.support_idx && pos < a.support_cap) a.support_idx[bh * a.support_cap + pos] = tok;
+    if (a.support_p && pos < a.support_cap) a.support_p[bh * a.support_cap + pos] = (float)p;
+  };
+  if (AK != 2 && in_lds && N >= 1 && N <= kWaveCands) {
+    // At most 128 candidates (alpha 2 and 1.5), on chip: wave 0 holds them,
+    // candidate l + 64 r in slot r of lane l, and takes the pairwise support
+    // test, tau, the weights and the compaction by itself, with lane
+    // exchanges and ballots instead of block barriers; the other waves wait
+    // at the one barrier below.  Same tests and closed forms as the block
+    // path, the support in the same (candidate) order.
+    if (tid_w == 0) {
+      constexpr int K = kWaveCands / kWave;
+      const int l = tid & 63;
+      float xf[K];
+      int tk[K], rw[K];
+      bool has[K];
+#pragma unroll
+      for (int r = 0; r < K; ++r) {
+        const int i = l + kWave * r;
+        has[r] = i < N;
+        xf[r] = has[r] ? lx[i] : 0.f;
+        tk[r] = has[r] ? lt[i] : 0;
+        rw[r] = has[r] ? lr[i] : 0;
+      }
+      float ff[K];
+#pragma unroll
+      for (int r = 0; r < K; ++r) ff[r] = 0.f;
+#pragma unroll
+      for (int r2 = 0; r2 < K; ++r2) {
+        const int nr = min(kWave, N - kWave * r2);  // wave-uniform
+        for (int j = 0; j < nr; ++j) {
+          const float xj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xf[r2]), j));
+#pragma unroll
+          for (int r = 0; r < K; ++r) {
+            const float d = fmaxf(xj - xf[r], 0.f);
+            ff[r] += AK == 0 ? d : d * d;
+          }
+        }
+      }
+      double c = 0.0, s1 = 0.0, s2 = 0.0;
+#pragma unroll
+      for (int r = 0; r < K; ++r) {
+        if (has[r] && (double)ff[r] < 1.0) {
+          const double y = (double)xf[r] - m;
+          c += 1.0;
+          s1 += y;
+          s2 += y * y;
+        }
+      }
+      c = wave_sum(c);
+      s1 = wave_sum(s1);
+      s2 = wave_sum(s2);
+      tau = support_tau<AK>(c, s1, s2, m);
+      double p[K];
+      int pos[K], base = 0;
+#pragma unroll
+      for (int r = 0; r < K; ++r) {
+        const bool sup = has[r] && (double)xf[r] > tau;
+        const uint64_t bal = __ballot(sup);
+        pos[r] = sup ? base + __popcll(bal & ((1ull << l) - 1ull)) : -1;
+        base += __popcll(bal);
+        p[r] = sup ? entmax_pow<AK>((double)xf[r] - tau, beta) : 0.0;
+      }
+      double pl = 0.0;
+#pragma unroll
+      for (int r = 0; r < K; ++r) {
+        pl += p[r];
+        // every lane has read its candidates above, so the list is
+        // rewritten in place (p replaces x)
+        if (pos[r] >= 0) {
+          emit(pos[r], p[r], tk[r]);
+          lx[pos[r]] = (float)p[r];
+          lt[pos[r]] = tk[r];
+          lr[pos[r]] = rw[r];
+        }
+      }
+      ps = wave_sum(pl);
+      if (l == 0) {
+        s_tau = tau;
+        sm.s_nsup = base;
+        sm.s_ps = ps;
+      }
+    }
+    __syncthreads();
+    tau = s_tau;
+    nsup = sm.s_nsup;
+    ps = sm.s_ps;
+  } else {
   if (AK != 2 && N <= kTauThreads) {
     tau = solve_pairwise<AK>(xs, N, m, a.alpha, redd);
   } else if (N <= 8 * kWave) {
@@ -1270,15 +1368,8 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
   } else {
     tau = solve_threshold<false, AK>(xs, N, m, thr, a.alpha, redd, sm.vpart, 2048);  // vpart is free until the output
   }
-  const double beta = 1.0 / ((double)a.alpha - 1.0);
 
   // ---- support, weights, compaction in place (p replaces x) ----
-  double ps = 0.0;
-  int nsup = 0;
-  auto emit = [&](int pos, double p, int tok) {
-    if (a.support_idx && pos < a.support_cap) a.support_idx[bh * a.support_cap + pos] = tok;
-    if (a.support_p && pos < a.support_cap) a.support_p[bh * a.support_cap + pos] = (float)p;
-  };
   if (in_lds) {
     // on chip (N <= CAP, at most EW per thread): thread t holds the
     // contiguous candidates [t E, t E + E) in registers, one scan places its
@@ -1375,6 +1466,7 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
     __syncthreads();
   }
   ps = block_sum(ps, redd);
+  }  // the block path
 
   // ---- sum_j p_j v_j ----
   const int rr = tid / LPR, sub = tid % LPR;
