@@ -705,12 +705,6 @@ __device__ double solve_threshold(const float* xs, int N, double m, double thr, 
   return tau;
 }
 
-// Exact threshold of at most blockDim.x candidates by the pairwise support
-// test: with f(t) = sum_j (x_j - t)_+^e decreasing and f(tau) = 1, x_i is in
-// the support iff f(x_i) < 1.  Thread i evaluates f(x_i) (float64); then tau
-// follows from the closed form on the support (alpha 2 or 1.5) or from
-// Newton's method on it, started below tau at the largest excluded score
-// (other alpha).  All threads of the block take part and get the result.
 // tau from the support's count c and the sums s1, s2 of (x - m) and
 // (x - m)^2 over it: sum_S (x - tau) = 1 (alpha 2), sum_S (x - tau)^2 = 1
 // (alpha 1.5, the larger root of the quadratic).
@@ -721,64 +715,41 @@ template <int AK> __device__ __forceinline__ double support_tau(double c, double
   return m + mu - sqrt(fmax(disc, 0.0));
 }
 
+// Exact threshold of at most blockDim.x candidates (in LDS) by the pairwise
+// support test, alpha 2 and 1.5: with f(t) = sum_j (x_j - t)_+^e decreasing
+// and f(tau) = 1, x_i is in the support iff f(x_i) < 1.  Thread i evaluates
+// f(x_i); tau follows from the closed form on the support.  All threads of
+// the block take part and get the result.
 template <int AK>
-__device__ double solve_pairwise(const float* xs, int N, double m, float alpha_f, double* red) {
-  const int i = threadIdx.x, lane = i & 63;
-  constexpr bool sparsemax = AK == 0, ent15 = AK == 1;
-  const double beta = 1.0 / ((double)alpha_f - 1.0);
+__device__ double solve_pairwise(const float* lx, int N, double m, double* red) {
+  static_assert(AK == 0 || AK == 1, "closed forms for alpha 2 and 1.5 only");
+  const int i = threadIdx.x;
   const bool has = i < N;
-  const double xi = has ? (double)xs[i] : 0.0;
-  // every wave keeps all N scores in registers (lane l holds x[l + 64 r]) and
-  // broadcasts them with readlane, so the inner loop makes no memory access
-  constexpr int R = kTauThreads / kWave;
-  float xr[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) xr[r] = (lane + kWave * r < N) ? xs[lane + kWave * r] : 0.f;
-  // alpha 2 and 1.5: f in float32 (its rounding, about N 2^-24 f, only
-  // matters for scores that lie within that distance of tau); otherwise float64
-  double f = 0.0;
+  const float xif = has ? lx[i] : 0.f;
+  // f in float32 (its rounding, about N 2^-24 f, only matters for scores
+  // that lie within that distance of tau), the x_j in ascending j; every
+  // lane reads four of them with one broadcast LDS load
   float ff = 0.f;
-  const float xif = has ? xs[i] : 0.f;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int nr = min(kWave, N - kWave * r);
-    for (int l = 0; l < nr; ++l) {
-      const float xj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xr[r]), l));
-      if (AK == 2) {
-        const double d = (double)xj - xi;
-        if (d > 0.0) f += entmax_pow<AK>(d, beta);
-      } else {
-        const float d = fmaxf(xj - xif, 0.f);
-        ff += AK == 0 ? d : d * d;
-      }
-    }
+  auto acc = [&](float xj) {
+    const float d = fmaxf(xj - xif, 0.f);
+    ff += AK == 0 ? d : d * d;
+  };
+  const float4* x4 = reinterpret_cast<const float4*>(lx);
+  const int n4 = N >> 2;
+#pragma unroll 4
+  for (int q = 0; q < n4; ++q) {
+    const float4 v = x4[q];
+    acc(v.x);
+    acc(v.y);
+    acc(v.z);
+    acc(v.w);
   }
-  if (AK != 2) f = ff;
-  const bool in = has && f < 1.0;
-  const double y = xi - m;
+  for (int j = 4 * n4; j < N; ++j) acc(lx[j]);
+  const bool in = has && (double)ff < 1.0;
+  const double y = (double)xif - m;
   double c = in ? 1.0 : 0.0, s1 = in ? y : 0.0, s2 = in ? y * y : 0.0;
   block_sum3(c, s1, s2, red);
-  if (sparsemax || ent15) return support_tau<AK>(c, s1, s2, m);
-  // other alpha: Newton on g(t) = sum_S (x - t)^beta - 1 from the largest excluded score
-  double lo = (has && !in) ? xi : m - 1.0;
-  lo = block_max(lo, red);
-  double t = lo;
-  for (int it = 0; it < 100; ++it) {
-    double g = 0.0, gd = 0.0;
-    if (in) {
-      const double d = xi - t;
-      const double pw = entmax_pow<AK>(d, beta);
-      g = pw;
-      gd = beta * pw / d;
-    }
-    g = block_sum(g, red);
-    gd = block_sum(gd, red);
-    const double step = (g - 1.0) / gd;
-    if (!(step > 0.0)) break;
-    t += step;
-    if (step <= 1e-15 * fmax(1.0, fabs(t))) break;
-  }
-  return t;
+  return support_tau<AK>(c, s1, s2, m);
 }
 
 // On-chip scratch of the threshold stage (one instance per block), with room
@@ -787,7 +758,7 @@ __device__ double solve_pairwise(const float* xs, int N, double m, float alpha_f
 constexpr int kLdsCandsBig = 8192;
 constexpr int kWaveCands = 128;  // candidates the single-wave threshold path takes (two per lane)
 template <int CAP> struct TauSmem {
-  float lx[CAP];
+  alignas(16) float lx[CAP];  // (read four at a time by the pairwise test)
   int lt[CAP];
   int lr[CAP];
   int s_pre[kTauItemChunk + 1];
@@ -1356,8 +1327,14 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
     nsup = sm.s_nsup;
     ps = sm.s_ps;
   } else {
-  if (AK != 2 && N <= kTauThreads) {
-    tau = solve_pairwise<AK>(xs, N, m, a.alpha, redd);
+  bool pairwise = false;
+  if constexpr (AK != 2) {
+    if (N <= kTauThreads) {  // (then the list is on chip)
+      tau = solve_pairwise<AK>(lx, N, m, redd);
+      pairwise = true;
+    }
+  }
+  if (pairwise) {
   } else if (N <= 8 * kWave) {
     if (tid_w == 0) {
       tau = solve_threshold<true, AK>(xs, N, m, thr, a.alpha, redd);
