@@ -763,6 +763,7 @@ template <int CAP> struct TauSmem {
   int lr[CAP];
   int s_pre[kTauItemChunk + 1];
   int s_item[kTauItemChunk];
+  int s_icnt[kTauItemChunk];  // candidate counts of the listed items (on-chip collection)
   int s_tab[2][65];  // per-item kept counts of one collection round, their offsets
   float vpart[2048];  // row-group partial outputs (RPB x D <= 2048)
   double redd[48];  // block reductions (up to three values per wave)
@@ -941,11 +942,13 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
   }
 
   // Kept candidates (above thr) of the listed items s_item[0, n_list),
-  // appended in item and token order to the on-chip list from position N.
-  // One wave per item, lane r reading the item's candidate r, so a wave's
-  // loads are contiguous; kCollectU items per wave per round, and one wave
-  // scans the round's 4 kCollectU per-item counts.  False, with the list
-  // abandoned, once it would exceed CAP.
+  // whose candidate counts are in s_icnt, appended in item and token order
+  // to the on-chip list from position N.  One wave per item, lane r reading
+  // the item's candidate r, so a wave's loads are contiguous; lanes past the
+  // item's count read its last candidate again, so an item of c candidates
+  // costs the cache lines of c, not of 64.  kCollectU items per wave per
+  // round, and one wave scans the round's 4 kCollectU per-item counts.
+  // False, with the list abandoned, once it would exceed CAP.
   auto collect_lds = [&](int n_list, int& N) -> bool {
     constexpr int U = kCollectU;
     const int lane = tid & 63;
@@ -955,9 +958,11 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         const int k = r0 + tid_w * U + j;
-        const int it = sm.s_item[k < n_list ? k : n_list - 1];
-        const size_t at = (size_t)it * kItemTokens + lane;  // within the unit's item slots
-        const int c = icnt[it];
+        const int kk = k < n_list ? k : n_list - 1;
+        const int it = sm.s_item[kk];
+        const int c = sm.s_icnt[kk];
+        // (within the unit's item slots; c >= 1 for a listed item)
+        const size_t at = (size_t)it * kItemTokens + min(lane, max(c - 1, 0));
         cv[j] = k < n_list ? c : 0;
         xv[j] = cx[at];
         tv[j] = ct[at];
@@ -1011,7 +1016,11 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
     int rank = block_exclusive_scan(nz, redi, &n_ne);
 #pragma unroll
     for (int i = 0; i < IPT; ++i)
-      if (loc[i] > 0) sm.s_item[rank++] = IPT * tid + i;
+      if (loc[i] > 0) {
+        sm.s_item[rank] = IPT * tid + i;
+        sm.s_icnt[rank] = min(loc[i], kItemTokens);
+        ++rank;
+      }
     __syncthreads();
     done = collect_lds(n_ne, N);
     if (!done) {
@@ -1102,6 +1111,8 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
         }
         __syncthreads();
         if (!lds_full) {
+          for (int k = tid; k < n_sv; k += kTauThreads) sm.s_icnt[k] = min(icnt[sm.s_item[k]], kItemTokens);
+          __syncthreads();
           done = collect_lds(n_sv, N);
           if (!done) N = 0;
         }
