@@ -954,15 +954,22 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
     const int lane = tid & 63;
     for (int r0 = 0; r0 < n_list; r0 += 4 * U) {
       float xv[U];
-      int tv[U], rv[U], cv[U];
+      int tv[U], rv[U], cv[U], iv[U];
+      // the round's items and counts first, then every load (one wait for
+      // the LDS reads, not one per item)
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         const int k = r0 + tid_w * U + j;
         const int kk = k < n_list ? k : n_list - 1;
-        const int it = sm.s_item[kk];
-        const int c = sm.s_icnt[kk];
+        iv[j] = sm.s_item[kk];
+        cv[j] = sm.s_icnt[kk];
+      }
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int k = r0 + tid_w * U + j;
+        const int c = cv[j];
         // (within the unit's item slots; c >= 1 for a listed item)
-        const size_t at = (size_t)it * kItemTokens + min(lane, max(c - 1, 0));
+        const size_t at = (size_t)iv[j] * kItemTokens + min(lane, max(c - 1, 0));
         cv[j] = k < n_list ? c : 0;
         xv[j] = cx[at];
         tv[j] = ct[at];
@@ -986,10 +993,13 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
       __syncthreads();
       const int n_end = sm.s_tab[1][64];
       if (n_end > CAP) return false;
+      int off[U];  // every item's offset first: one wait, not one per item
+#pragma unroll
+      for (int j = 0; j < U; ++j) off[j] = sm.s_tab[1][tid_w * U + j];
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         if ((mk[j] >> lane) & 1ull) {
-          const int pos = sm.s_tab[1][tid_w * U + j] + __popcll(mk[j] & ((1ull << lane) - 1ull));
+          const int pos = off[j] + __popcll(mk[j] & ((1ull << lane) - 1ull));
           lx[pos] = xv[j];
           lt[pos] = tv[j];
           lr[pos] = rv[j];

@@ -186,6 +186,21 @@ def test_c4_reduced():
     check_step(spec, run_step(sess, spec, q, sparse=False), q, [(0, 1)], sparse=False, kv_cache=cache)
 
 
+def test_c4g_reduced_many_listed_items():
+    """Clustered keys with the Gaussian selector on 2049 pages of 64: more
+    than 1024 items per head, of which many reach above the threshold
+    stage's bound, so the candidates are collected in score-only rounds and
+    their ids and rows read afterwards; sparse on every unit, and the full
+    cache (every item listed) on one."""
+    spec = W.make_spec("c4g", context=131072 + 45, n_q_heads=8, n_kv_heads=2)
+    sess, _ = _session(spec)
+    q = W.queries(spec)
+    cache = {}
+    check_step(spec, run_step(sess, spec, q), q, all_units(spec), kv_cache=cache)
+    check_step(spec, run_step(sess, spec, q, sparse=False), q, [(0, 1)], sparse=False, kv_cache=cache)
+    assert sess.device_status() == 0
+
+
 def test_c5_reduced_with_appends():
     """Permuted physical pages, mixed lengths, one appended token per sequence
     per step, metadata maintained in the loop."""
