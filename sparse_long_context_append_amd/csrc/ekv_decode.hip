@@ -1347,7 +1347,9 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
     tau = s_tau;
     nsup = sm.s_nsup;
     ps = sm.s_ps;
-  } else {
+  } else {  // the block path
+  // (other alpha: the pairwise test would take N^2 fp64 powers; Newton's
+  // method takes a few passes instead)
   bool pairwise = false;
   if constexpr (AK != 2) {
     if (N <= kTauThreads) {  // (then the list is on chip)
@@ -1355,16 +1357,17 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
       pairwise = true;
     }
   }
-  if (pairwise) {
-  } else if (N <= 8 * kWave) {
-    if (tid_w == 0) {
-      tau = solve_threshold<true, AK>(xs, N, m, thr, a.alpha, redd);
-      if ((tid & 63) == 0) s_tau = tau;
+  if (!pairwise) {
+    if (N <= 8 * kWave) {
+      if (tid_w == 0) {
+        tau = solve_threshold<true, AK>(xs, N, m, thr, a.alpha, redd);
+        if ((tid & 63) == 0) s_tau = tau;
+      }
+      __syncthreads();
+      tau = s_tau;
+    } else {
+      tau = solve_threshold<false, AK>(xs, N, m, thr, a.alpha, redd, sm.vpart, 2048);  // vpart is free until the output
     }
-    __syncthreads();
-    tau = s_tau;
-  } else {
-    tau = solve_threshold<false, AK>(xs, N, m, thr, a.alpha, redd, sm.vpart, 2048);  // vpart is free until the output
   }
 
   // ---- support, weights, compaction in place (p replaces x) ----
