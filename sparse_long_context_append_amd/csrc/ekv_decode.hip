@@ -771,6 +771,7 @@ template <int CAP> struct TauSmem {
   double s_tau;
   double s_ps;  // the single-wave threshold path's outputs
   int s_nsup;
+  float pc[kWaveCands];  // its weights by candidate (0 off the support), when waves 1..3 prefetch the V rows
   uint32_t s_mkey[4];
   int s_kcnt[4];
   int s_flag;
@@ -1263,13 +1264,24 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
     if (a.support_idx && pos < a.support_cap) a.support_idx[bh * a.support_cap + pos] = tok;
     if (a.support_p && pos < a.support_cap) a.support_p[bh * a.support_cap + pos] = (float)p;
   };
+  // V rows prefetched by waves 1..3 during the single-wave solve: VGR row
+  // groups of LPR lanes, VPR rows each (every candidate of the single-wave
+  // path at d = 128 in bf16)
+  constexpr int VGR = (kTauThreads - kWave) / LPR;
+  constexpr int VPR = (kWaveCands + VGR - 1) / VGR < 12 ? (kWaveCands + VGR - 1) / VGR : 12;
+  bool vpre = false;
+  uint4 vq[VPR];
   if (AK != 2 && in_lds && N >= 1 && N <= kWaveCands) {
     // At most 128 candidates (alpha 2 and 1.5), on chip: wave 0 holds them,
     // candidate l + 64 r in slot r of lane l, and takes the pairwise support
-    // test, tau, the weights and the compaction by itself, with lane
-    // exchanges and ballots instead of block barriers; the other waves wait
-    // at the one barrier below.  Same tests and closed forms as the block
-    // path, the support in the same (candidate) order.
+    // test, tau and the weights by itself, with lane exchanges and ballots
+    // instead of block barriers.  Same tests and closed forms as the block
+    // path, the support in the same (candidate) order.  Meanwhile, when the
+    // candidates are few enough, waves 1..3 load every candidate's V row
+    // (most are in the support); wave 0 then leaves the list in place and
+    // hands over the weights by candidate.  Otherwise waves 1..3 wait at the
+    // barrier, and wave 0 compacts the list in place for the usual V sum.
+    vpre = N <= VPR * VGR;  // block-uniform
     if (tid_w == 0) {
       constexpr int K = kWaveCands / kWave;
       const int l = tid & 63;
@@ -1327,10 +1339,12 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
 #pragma unroll
       for (int r = 0; r < K; ++r) {
         pl += p[r];
-        // every lane has read its candidates above, so the list is
-        // rewritten in place (p replaces x)
-        if (pos[r] >= 0) {
-          emit(pos[r], p[r], tk[r]);
+        if (pos[r] >= 0) emit(pos[r], p[r], tk[r]);
+        if (vpre) {
+          if (l + kWave * r < N) sm.pc[l + kWave * r] = (float)p[r];
+        } else if (pos[r] >= 0) {
+          // every lane has read its candidates above, so the list is
+          // rewritten in place (p replaces x)
           lx[pos[r]] = (float)p[r];
           lt[pos[r]] = tk[r];
           lr[pos[r]] = rw[r];
@@ -1341,6 +1355,17 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
         s_tau = tau;
         sm.s_nsup = base;
         sm.s_ps = ps;
+      }
+    } else if (vpre) {
+      // candidate gq + VGR q's row, the lane's 16 bytes of it (the last
+      // candidate stands in past the end; lr is not rewritten on this path)
+      const int gq = (tid - kWave) / LPR, sub = tid % LPR;
+#pragma unroll
+      for (int q = 0; q < VPR; ++q) {
+        const int row = lr[min(gq + VGR * q, N - 1)];
+        const int phys = row >> __builtin_ctz(P), slot = row & (P - 1);  // P is a power of two
+        vq[q] = ldg16(reinterpret_cast<const char*>(a.v) +
+                      ((((size_t)phys * a.hkv_mem + (g >> a.kv_shift)) * P + slot) * D + (size_t)sub * EPL) * E::kBytes);
       }
     }
     __syncthreads();
@@ -1474,9 +1499,27 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  if (vpre) {
+    // the rows loaded during the solve, weighted by candidate (0 off the
+    // support), in candidate order
+    if (tid_w > 0) {
+      const int gq = (tid - kWave) / LPR;
+#pragma unroll
+      for (int q = 0; q < VPR; ++q) {
+        const int i = gq + VGR * q;
+        if (i < N) {
+          const float pw = sm.pc[i];
+          float f[EPL];
+          E::unpack(vq[q], f);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pw, f[e], acc[e]);
+        }
+      }
+    }
+  }
   // kVRows rows in flight per thread: every load of a round first (the last
   // row stands in past the end), then the products in row order
-  for (int s0 = rr; s0 < nsup; s0 += kVRows * RPB) {
+  for (int s0 = rr; !vpre && s0 < nsup; s0 += kVRows * RPB) {
     uint4 vv[kVRows];
     float pv[kVRows];
 #pragma unroll
