@@ -20,6 +20,8 @@
 //               combine, so results are bitwise reproducible).
 #include "ekv_kernels.h"
 
+#include <type_traits>
+
 namespace ekv {
 
 constexpr int kDecThreads = 256;
@@ -1296,21 +1298,35 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
         tk[r] = has[r] ? lt[i] : 0;
         rw[r] = has[r] ? lr[i] : 0;
       }
+      // f(x) = sum_j (x_j - x)_+^e over the candidates in ascending j, the
+      // x_j read four at a time with broadcast LDS loads; the second slot
+      // only when there are more than 64 candidates
       float ff[K];
 #pragma unroll
       for (int r = 0; r < K; ++r) ff[r] = 0.f;
+      auto pass = [&](auto nslots) {
+        constexpr int KS = decltype(nslots)::value;
+        auto acc = [&](float xj) {
 #pragma unroll
-      for (int r2 = 0; r2 < K; ++r2) {
-        const int nr = min(kWave, N - kWave * r2);  // wave-uniform
-        for (int j = 0; j < nr; ++j) {
-          const float xj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xf[r2]), j));
-#pragma unroll
-          for (int r = 0; r < K; ++r) {
+          for (int r = 0; r < KS; ++r) {
             const float d = fmaxf(xj - xf[r], 0.f);
             ff[r] += AK == 0 ? d : d * d;
           }
+        };
+        const float4* x4 = reinterpret_cast<const float4*>(lx);
+        const int n4 = N >> 2;
+#pragma unroll 2
+        for (int q = 0; q < n4; ++q) {
+          const float4 v = x4[q];
+          acc(v.x);
+          acc(v.y);
+          acc(v.z);
+          acc(v.w);
         }
-      }
+        for (int j = 4 * n4; j < N; ++j) acc(lx[j]);
+      };
+      if (N > kWave) pass(std::integral_constant<int, K>{});
+      else pass(std::integral_constant<int, 1>{});
       double c = 0.0, s1 = 0.0, s2 = 0.0;
 #pragma unroll
       for (int r = 0; r < K; ++r) {
