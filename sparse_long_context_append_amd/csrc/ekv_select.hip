@@ -744,15 +744,15 @@ __device__ void gauss_mass_table(float mu, float sd, float tf, float beta, const
 // no second derivative, ddF is left unchanged).
 template <bool GEN>
 __device__ __forceinline__ void live_term(float2 v, float P, float last_n, float tf, int mode, float beta,
-                                          const MomTable<GEN>& T, double& F, double& dF, double& ddF) {
+                                          const MomTable<GEN>& T, double& F, float& dF, float& ddF) {
   float n = P, sd = v.y;
   if (sd < 0.f) { sd = -sd - 1.f; n = last_n; }
   float e, de, dde = 0.f;
   if constexpr (GEN) gauss_mass_table(v.x, sd, tf, beta, T, e, de);
   else gauss_mass(v.x, sd, tf, mode == 1, e, de, dde);
   F += (double)n * (double)e;
-  dF += (double)n * (double)de;
-  ddF += (double)n * (double)dde;
+  dF = fmaf(n, de, dF);
+  ddF = fmaf(n, dde, ddF);
 }
 
 // The single page of the largest margin max_h (e_hat - tau_hat) (lowest id
@@ -876,21 +876,23 @@ __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void t
     t = t0;
     for (int it = 0; it < 200; ++it) {
       const float tf = (float)t;
-      double F = 0.0, dF = 0.0, ddF = 0.0;
+      // F in fp64 (it decides the root); its derivatives only shape the
+      // step, so their sums within a wave are fp32
+      double F = 0.0;
+      float dFf = 0.f, ddFf = 0.f;
       if (use_live) {
         for (int i = tid; i < n_live; i += kTauHatThreads)
-          live_term<GEN>(live[i], Pf, last_n, tf, mode, beta, mom, F, dF, ddF);
+          live_term<GEN>(live[i], Pf, last_n, tf, mode, beta, mom, F, dFf, ddFf);
       } else {
         for (int p = tid; p < n_b; p += kTauHatThreads) {
           float2 v = st[p];
           if (p == n_b - 1 && last_n != Pf) v.y = -v.y - 1.f;
-          live_term<GEN>(v, Pf, last_n, tf, mode, beta, mom, F, dF, ddF);
+          live_term<GEN>(v, Pf, last_n, tf, mode, beta, mom, F, dFf, ddFf);
         }
       }
       // wave partials -> wave 0 computes the step -> every wave reads it
       F = wave_sum(F);
-      dF = wave_sum(dF);
-      ddF = wave_sum(ddF);
+      double dF = wave_sum(dFf), ddF = wave_sum(ddFf);
       if (lane == 0) {
         part[0][w][0] = F;
         part[0][w][1] = dF;
