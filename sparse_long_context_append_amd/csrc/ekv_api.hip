@@ -228,6 +228,8 @@ static ekv_status prepare_select(const ekv_cache* cache, const ekv_seqs* seqs, c
   a->ehat = at<float>(workspace, L->ehat);
   a->stats_out = nullptr;
   a->tau_hat = at<double>(workspace, L->tau_hat);
+  a->keep_bits = at<uint64_t>(workspace, L->keep_bits);
+  a->keep_words = ekv::keep_words(a->max_pages);
   a->done = at<uint32_t>(workspace, L->sel_done);
   a->status = at<uint32_t>(workspace, L->status);
   return EKV_OK;

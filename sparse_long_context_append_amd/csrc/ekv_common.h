@@ -27,6 +27,7 @@ struct Layout {
   size_t ehat;      // f32 [B*Hq*max_pages] estimated page maximum
   size_t tau_hat;   // f64 [B*Hq]
   size_t smx_part;  // f32 [B*Hq][kSmxMaxSlots][head_dim + 2] softmax block partials
+  size_t keep_bits; // u64 [B*Hq][keep_words(max_pages)] Gaussian keep decisions per query head
   // the entmax decode's per-item regions, sized for lists of item_pages pages
   size_t item_cnt;  // i32 [B*Hq*max_items] candidates kept by each decode work item
   size_t item_max;  // f32 [B*Hq*max_items] per item maximum score
@@ -44,6 +45,8 @@ struct Layout {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // row stride of the internal page-score buffer: 16-byte aligned rows
 inline int score_stride(int max_pages) { return (max_pages + 3) & ~3; }
+// 64-page words of a query head's keep bitmap
+inline int keep_words(int max_pages) { return (max_pages + 63) / 64; }
 
 constexpr int kSmxMaxSlots = 256;  // softmax decode blocks per (sequence, KV head), at most
 
@@ -81,6 +84,7 @@ inline Layout make_layout(int B, int Hkv, int Hq, int max_pages, int P, int D, i
   L.ehat = off;     off = align256(off + 4 * bh * max_pages);
   L.tau_hat = off;  off = align256(off + 8 * bh);
   L.smx_part = off; off = align256(off + 4 * bh * kSmxMaxSlots * size_t(D + 2));
+  L.keep_bits = off; off = align256(off + 8 * bh * size_t(keep_words(max_pages)));
   L.total = carve_items(L, off, bh, P, item_pages);
   return L;
 }

@@ -500,10 +500,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_gauss_kernel(SelectArgs a
 // variance) leaves an error far below the tolerance, so it is taken as the
 // last step, without one more evaluation of F to confirm it.
 //
-// The last block of a (sequence, KV head) to finish (arrival counter) keeps
-// the pages whose estimated maximum beats tau_hat - delta for some head of
-// the group, in ascending order, at least one page (the best margin, lowest
-// id on ties).
+// Each head marks the pages whose estimated maximum beats its tau_hat -
+// delta in a bitmap; the last block of a (sequence, KV head) to finish
+// (arrival counter) keeps the pages some head of the group marked, in
+// ascending order, at least one page (the best margin, lowest id on ties).
 // ---------------------------------------------------------------------------
 // The standard normal density and distribution function at u from one
 // exponential.  erfc is the Chebyshev fit of Press, Teukolsky, Vetterling
@@ -819,6 +819,8 @@ __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void t
   __shared__ int s_last;
   double t = 0.0;
   const bool in_regs = n_b <= PPT * kTauHatThreads;
+  const float* eh_row = a.ehat + bh * a.max_pages;
+  float ehv[PPT];  // this head's estimated maxima (pages tid, tid + 1024, ...), for its keep decisions
   if (n_b > 0) {
     const int mode = GEN ? 2 : (a.alpha == 1.5f ? 1 : 0);
     const float beta = 1.f / (a.alpha - 1.f);
@@ -869,6 +871,10 @@ __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void t
           }
         }
       }
+      // the estimated maxima are requested now, in the registers of the
+      // page records (no longer needed); they arrive while the iteration runs
+#pragma unroll
+      for (int i = 0; i < PPT; ++i) ehv[i] = load_or(eh_row, i * kTauHatThreads + tid, n_b, -INFINITY);
       __syncthreads();
     }
     double lo = -INFINITY, hi = INFINITY;
@@ -958,6 +964,26 @@ __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void t
       if (stop) break;
     }
   }
+  // this head's keep decisions, e_hat - tau_hat > -delta, one word per
+  // 64-page chunk (a ballot of one wave; pages past n_b are never kept),
+  // read by the group's last block
+  if (n_b > 0) {
+    uint64_t* kb = a.keep_bits + bh * a.keep_words;
+    const double ndelta = -(double)a.delta;
+    if (in_regs) {
+#pragma unroll
+      for (int i = 0; i < PPT; ++i) {
+        const int c = i * NW + w;  // pages 64 c .. 64 c + 63
+        const uint64_t m = __ballot((double)ehv[i] - t > ndelta);
+        if (lane == 0 && 64 * c < n_b) st_dev(kb + c, m);
+      }
+    } else {
+      for (int c = w; 64 * c < n_b; c += NW) {
+        const uint64_t m = __ballot((double)load_or(eh_row, 64 * c + lane, n_b, -INFINITY) - t > ndelta);
+        if (lane == 0) st_dev(kb + c, m);
+      }
+    }
+  }
   if (tid == 0) {
     st_dev(a.tau_hat + bh, t);  // read by the group's last block
     if (a.tau_hat_out) a.tau_hat_out[bh] = (float)t;
@@ -971,45 +997,25 @@ __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void t
   }
   __syncthreads();
   if (!s_last) return;
-  // The last block reads the other heads' tau_hat with agent-scope atomic
-  // loads, which return the coherent value: each writer's store completed
-  // before its release and arrival, and this block saw every arrival.  (An
-  // acquire fence here would invalidate this compute unit's caches and
-  // slow the loads below by microseconds.)  The estimated maxima come from
-  // the scoring kernel, which finished before this one started.
+  // The last block reads the other heads' keep words (and, for the floor,
+  // their tau_hat) with agent-scope atomic loads, which return the coherent
+  // value: each writer's stores completed before its release and arrival,
+  // and this block saw every arrival.  (An acquire fence here would
+  // invalidate this compute unit's caches and slow the loads below by
+  // microseconds.)
   if (tid == 0) st_dev(a.done + unit, 0u);  // ready for the next call
 
   // ---- the group's last block: the pages some head keeps, ascending ids.
-  // Pages go in chunks of 64 (chunk c: pages 64 c .. 64 c + 63), wave w
-  // taking chunks w, w + NW, ...: lane l reads page 64 c + l of each head
-  // (one coalesced row per load), the keep decisions of a chunk are one
-  // ballot, and one scan over the chunks' counts places every kept page.
-  // Sequences of more than 64 Ki pages go in passes of 1024 chunks. ----
+  // Pages go in chunks of 64 (chunk c: pages 64 c .. 64 c + 63, one keep
+  // word per head), thread c taking chunk c; one scan over the chunks'
+  // counts places every kept page.  Sequences of more than 64 Ki pages go in
+  // passes of 1024 chunks. ----
   int32_t* out = a.sel + (size_t)unit * a.cap;
   if (n_b == 0) {
     if (tid == 0) a.sel_count[unit] = 0;
     return;
   }
-  const float* ehg[G];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) ehg[hh] = a.ehat + ((size_t)b * a.n_q_heads + (size_t)g * G + hh) * a.max_pages;
-  constexpr int CU = G <= 4 ? 4 : 2;  // chunks per wave whose loads travel together
-  float ev[CU][G];
-  auto load_round = [&](int base, int c0) {
-#pragma unroll
-    for (int j = 0; j < CU; ++j) {
-      const int p = base + 64 * (c0 + j * NW) + lane;
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) ev[j][hh] = load_or(ehg[hh], p, n_b, -INFINITY);
-    }
-  };
-  load_round(0, w);  // the first round's estimates travel with the tau_hat loads below
-  double tg[G];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh)
-    tg[hh] = __hip_atomic_load(a.tau_hat + (size_t)b * a.n_q_heads + (size_t)g * G + hh, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-  const double ndelta = -(double)a.delta;
+  const uint64_t* kb0 = a.keep_bits + ((size_t)b * a.n_q_heads + (size_t)g * G) * a.keep_words;
   uint64_t* s_mask = reinterpret_cast<uint64_t*>(live);  // the live list is no longer needed
   int* s_off = reinterpret_cast<int*>(s_mask + kTauHatThreads);
   static_assert(LIVE * sizeof(float2) >= kTauHatThreads * (sizeof(uint64_t) + sizeof(int)), "union scratch");
@@ -1017,17 +1023,15 @@ __attribute__((amdgpu_waves_per_eu(!GEN && LIVE <= kTauHatLive ? 8 : 4))) void t
   int run = 0;
   for (int base = 0; base < n_b; base += 64 * kTauHatThreads) {  // block-uniform
     const int nch = min(kTauHatThreads, (n_b - base + 63) / 64);
-    for (int c0 = w; c0 < nch; c0 += CU * NW) {
-      if (base > 0 || c0 != w) load_round(base, c0);  // (the first round is in already)
+    // a page is kept when some head of the group keeps it: the OR of the
+    // heads' words, read with agent-scope atomic loads
+    if (tid < nch) {
+      uint64_t m = 0;
 #pragma unroll
-      for (int j = 0; j < CU; ++j) {
-        const int c = c0 + j * NW;
-        double mg = -INFINITY;
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) mg = fmax(mg, (double)ev[j][hh] - tg[hh]);
-        const uint64_t m = __ballot(mg > ndelta);  // pages past n_b read -inf: never kept
-        if (lane == 0 && c < nch) s_mask[c] = m;
-      }
+      for (int hh = 0; hh < G; ++hh)
+        m |= __hip_atomic_load(kb0 + (size_t)hh * a.keep_words + base / 64 + tid, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      s_mask[tid] = m;
     }
     __syncthreads();
     const int cnt = tid < nch ? __popcll(s_mask[tid]) : 0;
