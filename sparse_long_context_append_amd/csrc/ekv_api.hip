@@ -254,6 +254,10 @@ ekv_status ekv_select_pages(const ekv_cache* cache, const ekv_seqs* seqs, const 
   // query head, the bound is written per head and the top-k, threshold
   // estimate and keep test run on (sequence, query head) units.
   const bool per_head = params->per_head && a.group > 1;
+  if (!per_head) {  // room for the scoring blocks' top-k candidate lists; the launchers decide whether to use them
+    a.cand = at<uint64_t>(workspace, L.cand);
+    a.cand_cut = at<uint32_t>(workspace, L.cand_cut);
+  }
   const ekv::SelectArgs u = per_head ? per_query_head_view(a) : a;
   if (params->policy == EKV_SELECT_BBOX_TOPK) {
     a.per_head_scores = per_head;

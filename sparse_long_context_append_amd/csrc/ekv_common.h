@@ -28,6 +28,9 @@ struct Layout {
   size_t tau_hat;   // f64 [B*Hq]
   size_t smx_part;  // f32 [B*Hq][kSmxMaxSlots][head_dim + 2] softmax block partials
   size_t keep_bits; // u64 [B*Hq][keep_words(max_pages)] Gaussian keep decisions per query head
+  size_t cand;      // u64 [B*Hkv][cand_lists(max_pages)][kCandPerList] per 64 pages, their
+                    // largest scores as (key << 32 | page), in page order, zero-padded
+  size_t cand_cut;  // u32 [B*Hkv][cand_lists(max_pages)] largest key a list left out (0: none)
   // the entmax decode's per-item regions, sized for lists of item_pages pages
   size_t item_cnt;  // i32 [B*Hq*max_items] candidates kept by each decode work item
   size_t item_max;  // f32 [B*Hq*max_items] per item maximum score
@@ -47,6 +50,15 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int score_stride(int max_pages) { return (max_pages + 3) & ~3; }
 // 64-page words of a query head's keep bitmap
 inline int keep_words(int max_pages) { return (max_pages + 63) / 64; }
+// Top-k candidate lists: every kCandListPages pages (one wave of a scoring
+// block of kCandBlockPages pages) keep their kCandPerList largest scores for
+// the top-k select.
+constexpr int kCandBlockPages = 256;
+constexpr int kCandListPages = 64;
+constexpr int kCandPerList = 8;
+inline int cand_lists(int max_pages) {
+  return (max_pages + kCandBlockPages - 1) / kCandBlockPages * (kCandBlockPages / kCandListPages);
+}
 
 constexpr int kSmxMaxSlots = 256;  // softmax decode blocks per (sequence, KV head), at most
 
@@ -71,7 +83,6 @@ inline size_t carve_items(Layout& L, size_t off, size_t bh, int P, int item_page
 // reads (the list capacity of sparse calls; max_pages for the full cache).
 // Everything before item_cnt is independent of it.
 inline Layout make_layout(int B, int Hkv, int Hq, int max_pages, int P, int D, int item_pages) {
-  (void)Hkv;  // every per-unit array is sized for B * Hq units
   Layout L{};
   size_t off = 0;
   const size_t bh = size_t(B) * Hq;
@@ -85,6 +96,10 @@ inline Layout make_layout(int B, int Hkv, int Hq, int max_pages, int P, int D, i
   L.tau_hat = off;  off = align256(off + 8 * bh);
   L.smx_part = off; off = align256(off + 4 * bh * kSmxMaxSlots * size_t(D + 2));
   L.keep_bits = off; off = align256(off + 8 * bh * size_t(keep_words(max_pages)));
+  // candidate lists exist for shared (sequence, KV head) selections only
+  const size_t bk = size_t(B) * Hkv * cand_lists(max_pages);
+  L.cand = off;     off = align256(off + 8 * bk * kCandPerList);
+  L.cand_cut = off; off = align256(off + 4 * bk);
   L.total = carve_items(L, off, bh, P, item_pages);
   return L;
 }

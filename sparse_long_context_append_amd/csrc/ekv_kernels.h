@@ -50,6 +50,9 @@ struct SelectArgs {
   double* tau_hat;     // [B*Hq]
   uint64_t* keep_bits; // [B*Hq][keep_words] keep decisions of each query head (bit p: page p)
   int keep_words;
+  uint64_t* cand;      // [B*Hkv][cand_lists][kCandPerList] top-k candidate lists (NULL: none)
+  uint32_t* cand_cut;  // [B*Hkv][cand_lists]
+  int cand_lists;      // candidate lists per unit written by the scoring; 0: top-k reads every score
   uint32_t* done;      // [B*Hkv] arrival counters, zero between calls
   uint32_t* status;
 };

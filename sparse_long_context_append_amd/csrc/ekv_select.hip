@@ -61,6 +61,61 @@ __device__ __forceinline__ int page_phys(const SelectArgs& a, int b, int p, int 
   return phys;
 }
 
+// Top-k candidate list of one wave's kCandListPages pages, one page per
+// lane: key is the lane's page score key (0 past the sequence end).  The
+// values v = (key << 6 | 63 - lane) are distinct and order the pages by
+// score, ties to the lower page.  The (kCandPerList + 1)-th largest value is
+// found bit by bit (one ballot per bit, from the highest bit where the values
+// differ until one value is left); the pages above it are listed in page
+// order with zero padding, and its key is the list's cut (0 when no page is
+// left out).
+__device__ __forceinline__ void write_candidates(const SelectArgs& a, uint32_t key, int unit, int list, int page0) {
+  static_assert(kCandListPages == kWave, "one page per lane");
+  const int lane = threadIdx.x & 63;
+  const uint64_t v = (uint64_t)key << 6 | (uint32_t)(kCandListPages - 1 - lane);
+  const uint32_t vhi = (uint32_t)(v >> 32), vlo = (uint32_t)v;
+  // the highest bit where the values differ is the highest bit of max ^ min
+  // (every value lies between them); equal keys differ in the low 6 bits
+  const uint32_t kmax = wave_max(key), kmin = wave_min(key);
+  int bit = kmax != kmin ? 31 - __clz(kmax ^ kmin) + 6 : 5;
+  uint64_t alive = ~0ull;  // lanes whose value agrees with the wanted one on the bits so far
+  int want = kCandPerList + 1;  // rank of the wanted value among the alive ones, 1 = largest
+  int n_alive = kCandListPages;
+  // eight bits per round: the ballots do not depend on the search, so they
+  // are issued together and only the scalar counts run in sequence.  Bits
+  // past the last one (and bits after one value is left) keep the alive set
+  for (; bit >= 0 && n_alive > 1; bit -= 8) {
+    uint64_t B[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int bb = bit - i;
+      const uint32_t word = bb >= 32 ? vhi : vlo;
+      const uint64_t past = (uint64_t)((int64_t)bb >> 63);  // all ones below bit 0
+      B[i] = __ballot((word >> (bb & 31)) & 1u) & ~past;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint64_t x1 = alive & B[i], x0 = alive ^ x1;  // alive values with this bit 1, 0
+      const int c1 = __popcll(x1);
+      const bool one = c1 >= want;
+      alive = one ? x1 : x0;
+      want = one ? want : want - c1;
+      n_alive = one ? c1 : n_alive - c1;
+    }
+  }
+  const int l = __ffsll((long long)alive) - 1;  // the one value left
+  const uint64_t kw = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)vhi, l) << 32 |
+                      (uint32_t)__builtin_amdgcn_readlane((int)vlo, l);
+  const bool in = v > kw && (v >> 6) != 0ull;
+  const uint64_t I = __ballot(in);
+  const int pos = __popcll(I & ((1ull << lane) - 1ull)), tot = __popcll(I);
+  const size_t row = (size_t)unit * a.cand_lists + list;
+  uint64_t* cl = a.cand + row * kCandPerList;
+  if (in) cl[pos] = (v >> 6) << 32 | (uint32_t)(page0 + lane);
+  if (lane >= tot && lane < kCandPerList) cl[lane] = 0ull;
+  if (lane == 0) a.cand_cut[row] = (uint32_t)(kw >> 6);
+}
+
 // ---------------------------------------------------------------------------
 // Bounding-box score on the matrix cores.
 //
@@ -80,6 +135,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_bbox_mfma_kernel(SelectAr
   constexpr int KB = K / 32;  // k blocks
   constexpr int NH = (G + 3) / 4;  // 16-row operands (four heads each)
   __shared__ u32x4_t s_a[NH * KB][kWave];
+  __shared__ uint32_t s_key[NG == 4 ? kCandBlockPages : 1];  // the block's page score keys (top-k lists)
   const int b = blockIdx.z, g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -146,8 +202,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_bbox_mfma_kernel(SelectAr
     for (int hh = 0; hh < NH; ++hh) S = 4 * hh + grp < G ? fmax(S, U[hh]) : S;
     S = fmax(S, __shfl_xor(S, 16, kWave));
     S = fmax(S, __shfl_xor(S, 32, kWave));
-    if (grp == 0 && p < a.max_pages)
-      a.scores[((size_t)b * Hkv + g) * a.score_stride + p] = phys[ng] >= 0 ? float(S * (double)a.scale) : -INFINITY;
+    const float sc = phys[ng] >= 0 ? float(S * (double)a.scale) : -INFINITY;
+    if (grp == 0 && p < a.max_pages) a.scores[((size_t)b * Hkv + g) * a.score_stride + p] = sc;
+    if (NG == 4 && grp == 0) s_key[NG == 4 ? (ng * 4 + w) * 16 + col : 0] = p < n_b ? f2key(sc) : 0u;
+  }
+  if (NG == 4 && a.cand_lists > 0) {
+    // wave w lists the block's pages 64 w .. 64 w + 63, one per lane
+    __syncthreads();
+    write_candidates(a, s_key[NG == 4 ? w * kCandListPages + lane : 0], b * Hkv + g, blockIdx.x * 4 + w,
+                     blockIdx.x * kCandBlockPages + w * kCandListPages);
   }
 }
 
@@ -223,122 +286,152 @@ __global__ __launch_bounds__(kScoreThreads) void score_bbox_valu_kernel(SelectAr
 // slots at or past it are masked afterwards.  With E == 0 (more than 16384
 // pages) thread t owns ceil(n / 1024) pages and re-reads them from L2.
 // ---------------------------------------------------------------------------
-// Visit this thread's keys in page order: from registers (E > 0, loop fully
-// unrolled so the array stays in registers) or from memory (E == 0).
-#define EKV_FOR_KEYS(BODY)                                  \
-  if (E > 0) {                                              \
-    _Pragma("unroll") for (int i = 0; i < KE; ++i) {        \
-      if (i < cnt) {                                        \
-        const uint32_t k = keys[i];                         \
-        BODY                                                \
-      }                                                     \
-    }                                                       \
-  } else {                                                  \
-    for (int i = 0; i < cnt; ++i) {                         \
-      const uint32_t k = f2key(s[e0 + i]);                  \
-      BODY                                                  \
-    }                                                       \
+struct RadixSmem {
+  uint32_t hist[2][256];
+  uint32_t red[4][16];
+  uint32_t redu[16];
+  uint32_t digit[2], above[2], bucket[2];
+};
+
+// The k-th largest key, resolved as far as the selection needs: every key k
+// with (k & mask) > prefix is taken, and `rem` of those with (k & mask) ==
+// prefix, lowest page id first.  prefix is at most every taken key.
+struct KthKey {
+  uint32_t prefix, mask;
+  int rem;
+};
+
+__device__ __forceinline__ void radix_clear(RadixSmem& r) {
+  for (int i = threadIdx.x; i < 512; i += blockDim.x) (&r.hist[0][0])[i] = 0u;
+}
+
+// Radix select over the block's keys, given their AND and OR over the block.
+// for_keys(f) calls f(key) for each key this thread holds.  Digits of up to 8
+// bits, the first ending at the highest bit where the keys differ (the bits
+// above it are common to all keys), so the first histogram spreads the keys
+// over all its bins.  The histograms are zero on entry and on return.  Needs
+// k_eff <= the number of keys.
+template <class ForKeys>
+__device__ __forceinline__ KthKey radix_kth(RadixSmem& r, ForKeys&& for_keys, uint32_t kand, uint32_t kor,
+                                            int k_eff) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t diff = kand ^ kor;
+  if (diff == 0u) return KthKey{kand, 0xffffffffu, k_eff};  // every key equal: the k lowest page ids
+  const int top = 31 - __clz(diff);
+  uint32_t mask = top >= 31 ? 0u : ~((2u << top) - 1u);
+  uint32_t prefix = kand & mask;
+  int rem = k_eff;
+  int buf = 0;
+  for (int hi = top; hi >= 0; hi -= 8, buf ^= 1) {
+    const int shift = max(hi - 7, 0);
+    const uint32_t dmask = (2u << (hi - shift)) - 1u;  // hi - shift <= 7
+    uint32_t* hb = r.hist[buf];
+    for_keys([&](uint32_t k) {
+      if ((k & mask) == prefix) atomicAdd(&hb[(k >> shift) & dmask], 1u);
+    });
+    __syncthreads();
+    if (w == 0) {
+      const uint32_t c0 = hb[4 * lane], c1 = hb[4 * lane + 1], c2 = hb[4 * lane + 2], c3 = hb[4 * lane + 3];
+      // this histogram is used again two passes later: clear it now
+      hb[4 * lane] = 0u; hb[4 * lane + 1] = 0u; hb[4 * lane + 2] = 0u; hb[4 * lane + 3] = 0u;
+      // suffix sums over lanes (bins >= 4 lane, and >= 4 lane + 4) from
+      // the inclusive prefix and the total
+      const uint32_t c = c0 + c1 + c2 + c3;
+      const uint32_t inc = (uint32_t)wave_incl_scan((int)c);
+      const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+      const uint32_t Snext = total - inc;
+      const uint32_t S = Snext + c;
+      if (S >= (uint32_t)rem && Snext < (uint32_t)rem) {
+        uint32_t above = Snext;
+        const uint32_t cs[4] = {c0, c1, c2, c3};
+        int digit = 4 * lane;
+        uint32_t bucket = 0u;
+#pragma unroll
+        for (int bin = 3; bin >= 0; --bin) {
+          if (above + cs[bin] >= (uint32_t)rem) { digit = 4 * lane + bin; bucket = cs[bin]; break; }
+          above += cs[bin];
+        }
+        r.digit[buf] = (uint32_t)digit;
+        r.above[buf] = above;
+        r.bucket[buf] = bucket;
+      }
+    }
+    __syncthreads();
+    prefix |= r.digit[buf] << shift;
+    mask |= dmask << shift;
+    rem -= (int)r.above[buf];
+    // the chosen bucket holds exactly the keys still wanted: all of it is
+    // taken, and its lower digits need not be resolved
+    if (r.bucket[buf] == (uint32_t)rem) break;
   }
+  return KthKey{prefix, mask, rem};
+}
+
+// Writes the selected pages in page order.  for_keys(f) calls f(key, page)
+// for this thread's keys in page order, and the threads' keys follow one
+// another in page order.  One scan of (greater, equal) counts packed in the
+// low and high 16 bits of an unsigned word: each prefix is at most
+// n <= 65535, so neither field carries into the other, and the high field is
+// read without sign extension.
+template <class ForKeys>
+__device__ __forceinline__ void topk_emit(RadixSmem& r, ForKeys&& for_keys, const KthKey& kk, int32_t* out) {
+  uint32_t c_gt = 0u, c_eq = 0u;
+  for_keys([&](uint32_t k, int) {
+    const uint32_t km = k & kk.mask;
+    c_gt += (km > kk.prefix);
+    c_eq += (km == kk.prefix);
+  });
+  uint32_t tot;
+  const uint32_t packed = block_exclusive_scan_u32(c_gt | (c_eq << 16), r.redu, &tot);
+  const int gt_before = (int)(packed & 0xffffu), eq_before = (int)(packed >> 16);
+  int pos = gt_before + min(eq_before, kk.rem);
+  int rr = eq_before;
+  for_keys([&](uint32_t k, int page) {
+    const uint32_t km = k & kk.mask;
+    bool take = km > kk.prefix;
+    if (km == kk.prefix) { take = rr < kk.rem; ++rr; }
+    if (take) out[pos++] = page;
+  });
+}
 
 template <int E>  // keys per thread held in registers (0: read from memory)
 __device__ __forceinline__ void topk_block(const SelectArgs& a, const float* s, const uint32_t (&kin)[E > 0 ? E : 1], int n_b,
                            int k_eff, int32_t* out, int unit) {
   constexpr int KE = E > 0 ? E : 1;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
-  __shared__ uint32_t hist[2][256];
-  __shared__ uint32_t red[2][16];
-  __shared__ uint32_t redu[16];
-  __shared__ uint32_t sh_digit[2], sh_above[2], sh_bucket[2];
+  __shared__ RadixSmem rs;
   const int per = E > 0 ? E : (n_b + blockDim.x - 1) / blockDim.x;
   const int e0 = min(tid * per, n_b), e1 = min(e0 + per, n_b);
   const int cnt = e1 - e0;
   uint32_t keys[KE];
 #pragma unroll
   for (int i = 0; i < KE; ++i) keys[i] = kin[i];
+  // this thread's keys in page order: from registers (E > 0, loop fully
+  // unrolled so the array stays in registers) or from memory (E == 0)
+  auto for_keys = [&](auto&& f) {
+    if (E > 0) {
+#pragma unroll
+      for (int i = 0; i < KE; ++i)
+        if (i < cnt) f(keys[i], e0 + i);
+    } else {
+      for (int i = 0; i < cnt; ++i) f(f2key(s[e0 + i]), e0 + i);
+    }
+  };
   // bits shared by every key (AND and OR in one reduction) and cleared histograms
   uint32_t kand = 0xffffffffu, kor = 0u;
-  EKV_FOR_KEYS(kand &= k; kor |= k;)
+  for_keys([&](uint32_t k, int) { kand &= k; kor |= k; });
   kand = wave_reduce(kand, [](uint32_t u, uint32_t v) { return u & v; });
   kor = wave_reduce(kor, [](uint32_t u, uint32_t v) { return u | v; });
-  for (int i = tid; i < 512; i += blockDim.x) (&hist[0][0])[i] = 0u;
-  if (lane == 0) { red[0][w] = kand; red[1][w] = kor; }
+  radix_clear(rs);
+  if (lane == 0) { rs.red[0][w] = kand; rs.red[1][w] = kor; }
   __syncthreads();
-  kand = red[0][0];
-  kor = red[1][0];
-  for (int i = 1; i < nw; ++i) { kand &= red[0][i]; kor |= red[1][i]; }
-  const uint32_t diff = kand ^ kor;
-  uint32_t prefix, mask = 0u;
-  int rem = k_eff;
-  if (diff == 0u) {
-    prefix = kand;  // every score equal: the k lowest page ids
-    mask = 0xffffffffu;
-  } else {
-    // Digits of up to 8 bits, the first one ending at the highest bit where
-    // the keys differ (the bits above it are common to all keys), so the
-    // first histogram spreads the keys over all its bins.
-    const int top = 31 - __clz(diff);
-    mask = top >= 31 ? 0u : ~((2u << top) - 1u);
-    prefix = kand & mask;
-    int buf = 0;
-    for (int hi = top; hi >= 0; hi -= 8, buf ^= 1) {
-      const int shift = max(hi - 7, 0);
-      const uint32_t dmask = (2u << (hi - shift)) - 1u;  // hi - shift <= 7
-      uint32_t* hb = hist[buf];
-      EKV_FOR_KEYS(if ((k & mask) == prefix) atomicAdd(&hb[(k >> shift) & dmask], 1u);)
-      __syncthreads();
-      if (w == 0) {
-        const uint32_t c0 = hb[4 * lane], c1 = hb[4 * lane + 1], c2 = hb[4 * lane + 2], c3 = hb[4 * lane + 3];
-        // this histogram is used again two passes later: clear it now
-        hb[4 * lane] = 0u; hb[4 * lane + 1] = 0u; hb[4 * lane + 2] = 0u; hb[4 * lane + 3] = 0u;
-        // suffix sums over lanes (bins >= 4 lane, and >= 4 lane + 4) from
-        // the inclusive prefix and the total
-        const uint32_t c = c0 + c1 + c2 + c3;
-        const uint32_t inc = (uint32_t)wave_incl_scan((int)c);
-        const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
-        const uint32_t Snext = total - inc;
-        const uint32_t S = Snext + c;
-        if (S >= (uint32_t)rem && Snext < (uint32_t)rem) {
-          uint32_t above = Snext;
-          const uint32_t cs[4] = {c0, c1, c2, c3};
-          int digit = 4 * lane;
-          uint32_t bucket = 0u;
-#pragma unroll
-          for (int bin = 3; bin >= 0; --bin) {
-            if (above + cs[bin] >= (uint32_t)rem) { digit = 4 * lane + bin; bucket = cs[bin]; break; }
-            above += cs[bin];
-          }
-          sh_digit[buf] = (uint32_t)digit;
-          sh_above[buf] = above;
-          sh_bucket[buf] = bucket;
-        }
-      }
-      __syncthreads();
-      prefix |= sh_digit[buf] << shift;
-      mask |= dmask << shift;
-      rem -= (int)sh_above[buf];
-      // the chosen bucket holds exactly the keys still wanted: all of it is
-      // taken, and its lower digits need not be resolved
-      if (sh_bucket[buf] == (uint32_t)rem) break;
-    }
-  }
-  // keys compared on the resolved digits: above kstar are taken, and `rem`
-  // of those equal to it, lowest page id first
-  const uint32_t kstar = prefix;
-  // one scan of (greater, equal) counts packed in the low and high 16 bits
-  // of an unsigned word: each prefix is at most n <= 65535, so neither field
-  // carries into the other, and the high field is read without sign extension
-  uint32_t c_gt = 0u, c_eq = 0u;
-  EKV_FOR_KEYS(const uint32_t km = k & mask; c_gt += (km > kstar); c_eq += (km == kstar);)
-  uint32_t tot;
-  const uint32_t packed = block_exclusive_scan_u32(c_gt | (c_eq << 16), redu, &tot);
-  const int gt_before = (int)(packed & 0xffffu), eq_before = (int)(packed >> 16);
-  int pos = gt_before + min(eq_before, rem);
-  int r = eq_before;
-  EKV_FOR_KEYS(const uint32_t km = k & mask; bool take = km > kstar;
-               if (km == kstar) { take = r < rem; ++r; } if (take) out[pos++] = e0 + i;)
+  kand = rs.red[0][0];
+  kor = rs.red[1][0];
+  for (int i = 1; i < nw; ++i) { kand &= rs.red[0][i]; kor |= rs.red[1][i]; }
+  const KthKey kk = radix_kth(rs, [&](auto&& f) { for_keys([&](uint32_t k, int) { f(k); }); }, kand, kor, k_eff);
+  topk_emit(rs, for_keys, kk, out);
   if (tid == 0) a.sel_count[unit] = k_eff;
 }
-#undef EKV_FOR_KEYS
 
 template <int E>
 __global__ __launch_bounds__(kSelThreads) void topk_kernel(SelectArgs a) {
@@ -378,6 +471,99 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(SelectArgs a) {
     return;
   }
   topk_block<E>(a, s, keys, n_b, k_eff, out, unit);
+}
+
+// ---------------------------------------------------------------------------
+// Top-k over the scoring's candidate lists.  Every kCandListPages pages
+// listed their kCandPerList largest scores (ties to the lower page) in page
+// order, and the list's cut: the largest score it left out.  The k largest
+// entries of the lists are the k largest pages of the row whenever every cut
+// lies below all of them, since a page left out then scores below every
+// selected page.  That fails only when kCandListPages pages hold more than
+// kCandPerList of the k pages (clustered or equal scores); the block then
+// selects over the whole score row as topk_kernel does.  Empty list slots
+// hold key 0, below every score.
+// ---------------------------------------------------------------------------
+template <int EU, int E>  // list entries per thread; score keys per thread for the whole row
+__global__ __launch_bounds__(kSelThreads) void topk_cand_kernel(SelectArgs a) {
+  constexpr int KE = E > 0 ? E : 1;
+  static_assert(EU % 2 == 0, "entries are loaded in pairs");
+  __shared__ RadixSmem rs;
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int unit = b * a.n_kv_heads + g;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
+  const int nc = a.cand_lists * kCandPerList;  // even, and <= EU * blockDim.x
+  // the lists and the cuts, requested with the length; an index clamped to
+  // the last pair keeps every load inside the unit's lists
+  const uint64_t* cl = a.cand + (size_t)unit * nc;
+  uint32_t keys[EU];
+  int pid[EU];
+#pragma unroll
+  for (int i = 0; i < EU; i += 2) {
+    const int at = tid * EU + i;
+    const uint4 v = *reinterpret_cast<const uint4*>(cl + min(at, nc - 2));
+    const bool ok = at < nc;
+    keys[i] = ok ? v.y : 0u;
+    pid[i] = (int)v.x;
+    keys[i + 1] = ok ? v.w : 0u;
+    pid[i + 1] = (int)v.z;
+  }
+  uint32_t cmax = tid < a.cand_lists ? a.cand_cut[(size_t)unit * a.cand_lists + tid] : 0u;  // lists <= threads
+  const int L = clamp_len(a.seq_lens[b], a.max_pages, a.page_size, a.status);
+  const int n_b = pages_of(L, a.page_size);
+  const int k_eff = min(a.top_k, n_b);
+  int32_t* out = a.sel + (size_t)unit * a.cap;
+  if (k_eff >= n_b) {
+    for (int p = tid; p < n_b; p += blockDim.x) out[p] = p;
+    if (tid == 0) a.sel_count[unit] = n_b;
+    return;
+  }
+  if (n_b > 65535) {  // packed 16-bit counts would overflow: the host rejects such shapes
+    set_status(a.status, EKV_DEV_OVERFLOW);
+    if (tid == 0) a.sel_count[unit] = 0;
+    return;
+  }
+  // listed pages in page order (empty slots skipped)
+  auto for_cand = [&](auto&& f) {
+#pragma unroll
+    for (int i = 0; i < EU; ++i)
+      if (keys[i] != 0u) f(keys[i], pid[i]);
+  };
+  uint32_t kand = 0xffffffffu, kor = 0u, nlist = 0u;
+  for_cand([&](uint32_t k, int) { kand &= k; kor |= k; ++nlist; });
+  kand = wave_reduce(kand, [](uint32_t u, uint32_t v) { return u & v; });
+  kor = wave_reduce(kor, [](uint32_t u, uint32_t v) { return u | v; });
+  nlist = wave_sum(nlist);
+  cmax = wave_max(cmax);
+  radix_clear(rs);
+  if (lane == 0) { rs.red[0][w] = kand; rs.red[1][w] = kor; rs.red[2][w] = nlist; rs.red[3][w] = cmax; }
+  __syncthreads();
+  kand = rs.red[0][0]; kor = rs.red[1][0]; nlist = rs.red[2][0]; cmax = rs.red[3][0];
+  for (int i = 1; i < nw; ++i) {
+    kand &= rs.red[0][i]; kor |= rs.red[1][i]; nlist += rs.red[2][i]; cmax = max(cmax, rs.red[3][i]);
+  }
+  if ((int)nlist >= k_eff) {  // fewer listed pages than k: some block left out a page, use the row
+    const KthKey kk = radix_kth(rs, [&](auto&& f) { for_cand([&](uint32_t k, int) { f(k); }); }, kand, kor, k_eff);
+    if (cmax < kk.prefix) {  // every page left out scores below every selected page
+      topk_emit(rs, for_cand, kk, out);
+      if (tid == 0) a.sel_count[unit] = k_eff;
+      return;
+    }
+  }
+  const float* s = a.scores + (size_t)unit * a.score_stride;
+  uint32_t rk[KE];
+  if (E > 0) {
+#pragma unroll
+    for (int i = 0; i < KE; i += 4) {
+      const int at = min(tid * KE + i, a.score_stride - 4);
+      const float4 v = *reinterpret_cast<const float4*>(s + at);
+      rk[i] = f2key(v.x); rk[(i + 1) % KE] = f2key(v.y);
+      rk[(i + 2) % KE] = f2key(v.z); rk[(i + 3) % KE] = f2key(v.w);
+    }
+  } else {
+    rk[0] = 0u;  // unused: the keys are read from memory
+  }
+  topk_block<E>(a, s, rk, n_b, k_eff, out, unit);
 }
 
 // ---------------------------------------------------------------------------
@@ -1111,13 +1297,32 @@ __global__ __launch_bounds__(kSelThreads) void gauss_floor_kernel(SelectArgs a) 
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+// bf16 records are scored four 16-page groups per wave (256 pages per block)
+// when that still leaves >= 512 blocks
+static bool bbox_fat(const SelectArgs& a) {
+  return a.kv_dtype == EKV_BF16 && (long long)a.max_pages * a.n_kv_heads * a.batch >= 512LL * 256;
+}
+
+// Candidate lists per unit that the scoring writes for the top-k, or 0:
+// lists need the 256-page scoring blocks and a shared selection, fit the
+// top-k block's registers, and are used when they hold at least four times
+// the k pages (at most two of the k pages per list on average, so that no
+// list is likely to hold fewer than its share).
+static int topk_cand_lists(const SelectArgs& a) {
+  if (!a.cand || !a.cand_cut || a.per_head_scores || !bbox_fat(a)) return 0;
+  const int nl = cand_lists(a.max_pages);
+  const long long nc = (long long)nl * kCandPerList;
+  if (nl > kSelThreads || nc > 8LL * kSelThreads || 4LL * a.top_k > nc) return 0;
+  return nl;
+}
+
 template <int DT, int D>
-static hipError_t bbox_dispatch(const SelectArgs& a, hipStream_t s) {
+static hipError_t bbox_dispatch(const SelectArgs& a0, hipStream_t s) {
   const dim3 blk(kScoreThreads);
+  SelectArgs a = a0;
+  a.cand_lists = topk_cand_lists(a0);
   if (DT == EKV_BF16) {
-    // four 16-page groups per wave when that still leaves >= 512 blocks
-    const long long recs = (long long)a.max_pages * a.n_kv_heads * a.batch;
-    const bool fat = recs >= 512LL * 256;
+    const bool fat = bbox_fat(a);
     const int ppb = fat ? 256 : 64;
     const dim3 grid((a.max_pages + ppb - 1) / ppb, a.n_kv_heads, a.batch);
 #define EKV_BBOX(GG)                                                                                 \
@@ -1149,9 +1354,24 @@ hipError_t launch_score_bbox(const SelectArgs& a, hipStream_t s) {
   return a.head_dim == 128 ? bbox_dispatch<EKV_F32, 128>(a, s) : bbox_dispatch<EKV_F32, 64>(a, s);
 }
 
-hipError_t launch_topk(const SelectArgs& a, hipStream_t s) {
+template <int EU>
+static void topk_cand_dispatch(const SelectArgs& a, dim3 grid, int per, hipStream_t s) {
+  if (per <= 16) hipLaunchKernelGGL((topk_cand_kernel<EU, 16>), grid, dim3(kSelThreads), 0, s, a);
+  else hipLaunchKernelGGL((topk_cand_kernel<EU, 0>), grid, dim3(kSelThreads), 0, s, a);
+}
+
+hipError_t launch_topk(const SelectArgs& a0, hipStream_t s) {
+  SelectArgs a = a0;
+  a.cand_lists = topk_cand_lists(a0);  // the scoring launch decided the same
   const dim3 grid(a.n_kv_heads, a.batch);
   const int per = (a.max_pages + kSelThreads - 1) / kSelThreads;
+  if (a.cand_lists > 0) {
+    const int nc = a.cand_lists * kCandPerList;
+    if (nc <= 2 * kSelThreads) topk_cand_dispatch<2>(a, grid, per, s);
+    else if (nc <= 4 * kSelThreads) topk_cand_dispatch<4>(a, grid, per, s);
+    else topk_cand_dispatch<8>(a, grid, per, s);
+    return hipGetLastError();
+  }
   if (per <= 4) hipLaunchKernelGGL((topk_kernel<4>), grid, dim3(kSelThreads), 0, s, a);
   else if (per <= 16) hipLaunchKernelGGL((topk_kernel<16>), grid, dim3(kSelThreads), 0, s, a);
   else hipLaunchKernelGGL((topk_kernel<0>), grid, dim3(kSelThreads), 0, s, a);
