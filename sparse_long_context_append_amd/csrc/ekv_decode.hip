@@ -766,7 +766,7 @@ template <int CAP> struct TauSmem {
   int s_pre[kTauItemChunk + 1];
   int s_item[kTauItemChunk];
   int s_icnt[kTauItemChunk];  // candidate counts of the listed items (on-chip collection)
-  int s_tab[2][65];  // per-item kept counts of one collection round, their offsets
+  int s_tab[2][65];  // per-item kept counts of a collection round (rounds alternate halves)
   float vpart[2048];  // row-group partial outputs (RPB x D <= 2048)
   double redd[48];  // block reductions (up to three values per wave)
   int redi[17];
@@ -891,6 +891,12 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
   // on the item maxima: n items with maximum at or above a level l hold n
   // scores there, so tau >= l - n^-(alpha-1); levels m - 1/32 .. m - 1/4.
   double thr = fmax(m - 1.0, (double)lbf);
+  // With few items, those above this first bound are listed in the same
+  // pair of barriers as the count bound's sums (a superset of the items
+  // above the final bound, whose candidates the collection filters); n_pre
+  // is their number, or -1 when they are too many for one collection round
+  // and are listed against the final bound instead.
+  int n_pre = -1;
   {
     float lvl[4];
     int nk[4];
@@ -918,9 +924,17 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
           for (int k = 0; k < 4; ++k) nk[k] += vm[u] >= lvl[k];
       }
     }
-    // integer block sums of the four counts (one pair of barriers)
+    // this thread's items above the first bound (few items)
+    int nz0 = 0;
+    if (few_items) {
+#pragma unroll
+      for (int i = 0; i < IPT; ++i) nz0 += loc[i] > 0 && (double)lmx[i] > thr;
+    }
+    // integer block sums of the four counts and, with few items, the
+    // exclusive scan of nz0 (one pair of barriers)
+    constexpr int NWV = kTauThreads / kWave;
+    const int inc0 = wave_incl_scan(nz0);
     {
-      constexpr int NWV = kTauThreads / kWave;
 #pragma unroll
       for (int k = 0; k < 4; ++k) nk[k] = wave_sum(nk[k]);
       __syncthreads();
@@ -928,6 +942,7 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
 #pragma unroll
         for (int k = 0; k < 4; ++k) redi[4 * tid_w + k] = nk[k];
       }
+      if ((tid & 63) == 63) sm.s_tab[0][tid_w] = inc0;  // (the collection's table is free here)
       __syncthreads();
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -941,7 +956,28 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       if (nk[k] > 0) cb = fmax(cb, (double)lvl[k] - count_pow(nk[k], a.alpha));
+    const double thr0 = thr;
     thr = fmax(thr, cb - 1e-6 * fmax(1.0, fabs(m)));
+    if (few_items) {
+      int before = 0, n0 = 0;
+#pragma unroll
+      for (int i = 0; i < NWV; ++i) {
+        const int t = sm.s_tab[0][i];
+        before += i < tid_w ? t : 0;
+        n0 += t;
+      }
+      if (n0 <= 4 * kCollectU) {  // block-uniform: one collection round takes them all
+        int rank = before + inc0 - nz0;
+#pragma unroll
+        for (int i = 0; i < IPT; ++i)
+          if (loc[i] > 0 && (double)lmx[i] > thr0) {
+            sm.s_item[rank] = IPT * tid + i;
+            sm.s_icnt[rank] = min(loc[i], kItemTokens);
+            ++rank;
+          }
+        n_pre = n0;
+      }
+    }
   }
 
   // Kept candidates (above thr) of the listed items s_item[0, n_list),
@@ -985,20 +1021,22 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
         mk[j] = __ballot(lane < cv[j] && (double)xv[j] > thr);
         mine = lane == j ? __popcll(mk[j]) : mine;
       }
-      if (lane < U) sm.s_tab[0][tid_w * U + lane] = mine;
+      // the round's 4 U = 64 counts go to one half of the table (rounds
+      // alternate halves, so a round's writes never meet a slower wave's
+      // reads of the round before); after one barrier every wave scans all
+      // of them itself
+      static_assert(4 * U == kWave, "one count per lane");
+      int* tab = sm.s_tab[(r0 / (4 * U)) & 1];
+      if (lane < U) tab[tid_w * U + lane] = mine;
       __syncthreads();
-      if (tid_w == 0) {
-        const int v = sm.s_tab[0][lane];
-        const int inc = wave_incl_scan(v);
-        sm.s_tab[1][lane] = N + inc - v;
-        if (lane == 63) sm.s_tab[1][64] = N + inc;
-      }
-      __syncthreads();
-      const int n_end = sm.s_tab[1][64];
+      const int v = tab[lane];
+      const int inc = wave_incl_scan(v);
+      const int n_end = N + __builtin_amdgcn_readlane(inc, 63);
       if (n_end > CAP) return false;
-      int off[U];  // every item's offset first: one wait, not one per item
+      const int ex = inc - v;
+      int off[U];
 #pragma unroll
-      for (int j = 0; j < U; ++j) off[j] = sm.s_tab[1][tid_w * U + j];
+      for (int j = 0; j < U; ++j) off[j] = N + __shfl(ex, tid_w * U + j, kWave);
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         if ((mk[j] >> lane) & 1ull) {
@@ -1018,22 +1056,24 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
   int N = 0;
   bool in_lds = true, done = false, lds_full = false;
   if (few_items) {
-    int nz = 0;
+    int n_ne = n_pre;
+    if (n_pre < 0) {  // block-uniform
+      int nz = 0;
 #pragma unroll
-    for (int i = 0; i < IPT; ++i) {
-      if (!((double)lmx[i] > thr)) loc[i] = 0;
-      nz += loc[i] > 0;
-    }
-    // the non-empty items, in order: one scan
-    int n_ne;
-    int rank = block_exclusive_scan(nz, redi, &n_ne);
-#pragma unroll
-    for (int i = 0; i < IPT; ++i)
-      if (loc[i] > 0) {
-        sm.s_item[rank] = IPT * tid + i;
-        sm.s_icnt[rank] = min(loc[i], kItemTokens);
-        ++rank;
+      for (int i = 0; i < IPT; ++i) {
+        if (!((double)lmx[i] > thr)) loc[i] = 0;
+        nz += loc[i] > 0;
       }
+      // the non-empty items, in order: one scan
+      int rank = block_exclusive_scan(nz, redi, &n_ne);
+#pragma unroll
+      for (int i = 0; i < IPT; ++i)
+        if (loc[i] > 0) {
+          sm.s_item[rank] = IPT * tid + i;
+          sm.s_icnt[rank] = min(loc[i], kItemTokens);
+          ++rank;
+        }
+    }
     __syncthreads();
     done = collect_lds(n_ne, N);
     if (!done) {
