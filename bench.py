@@ -713,7 +713,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c4", help="workload the headline value is measured on")
-    ap.add_argument("--also", default="c3,c5,c2,c1",
+    ap.add_argument("--also", default="c3,c5,c4g,c2,c1",
                     help="comma-separated workloads reported beside the headline one in the same line ('' for none)")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
