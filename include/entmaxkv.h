@@ -256,7 +256,7 @@ ekv_status ekv_entmax_decode(const ekv_cache* cache, const ekv_seqs* seqs, const
  * ekv_entmax_decode, except:
  *   - scratch: a fixed 64 MiB device array inside the library, one per
  *     device, held from the library's load until the process ends.  Its
- *     per-item regions take 6 * 64 * 4 + 12 = 1548 bytes per (sequence, query
+ *     per-item regions take 6 * 64 * 4 + 16 = 1552 bytes per (sequence, query
  *     head, 64-token item of the longest list): a call whose lists (cap pages,
  *     or the whole cache when sel == NULL) need more returns
  *     EKV_ERR_WORKSPACE before launching anything.  The call allocates

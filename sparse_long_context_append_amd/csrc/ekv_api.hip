@@ -338,6 +338,7 @@ void decode_regions(ekv::DecodeArgs* a, void* base, const ekv::Layout& L) {
   a->item_cnt = at<int32_t>(base, L.item_cnt);
   a->item_max = at<float>(base, L.item_max);
   a->item_lb = at<float>(base, L.item_lb);
+  a->item_lvl = at<uint32_t>(base, L.item_lvl);
   a->cand_x = at<float>(base, L.cand_x);
   a->cand_t = at<int32_t>(base, L.cand_t);
   a->cand_r = at<int32_t>(base, L.cand_r);

@@ -41,6 +41,8 @@ struct Layout {
   size_t ovf_x;     // f32 [B*Hq*max_items*64] compacted candidates (large sets)
   size_t ovf_t;     // i32 [...]
   size_t ovf_r;     // i32 [...]
+  size_t item_lvl;  // u32 [B*Hq*max_items] per item: its scores at or above max - 1/32, - 1/16, - 1/8 (8 bits each;
+                    // written and read for heads of more than 1024 items only)
   size_t total;
   size_t max_items; // per (sequence, query head)
 };
@@ -76,6 +78,7 @@ inline size_t carve_items(Layout& L, size_t off, size_t bh, int P, int item_page
   L.ovf_x = off;    off = align256(off + 4 * bh * tok);
   L.ovf_t = off;    off = align256(off + 4 * bh * tok);
   L.ovf_r = off;    off = align256(off + 4 * bh * tok);
+  L.item_lvl = off; off = align256(off + 4 * bh * L.max_items);
   return off;
 }
 

@@ -26,6 +26,11 @@ namespace ekv {
 
 constexpr int kDecThreads = 256;
 constexpr int kTauThreads = 256;
+// A head of at most this many items keeps its item records in the threshold
+// kernel's registers (four per thread); only larger heads use the per-item
+// level counts, so the gather computes them only where some unit may have
+// more (chosen on the host from the list capacity).
+constexpr int kTauFewItems = 4 * kTauThreads;
 constexpr int kTauItemChunk = 1024;
 constexpr int kCollectU = 16;  // items per wave per on-chip collection round
 constexpr int kVRows = 8;      // V rows in flight per thread in the weighted sum
@@ -259,7 +264,9 @@ __device__ __forceinline__ void unit_locate(const UnitWalk& uw, int gs, int* u, 
   *sj = gs - __builtin_amdgcn_readlane(p, owner);
 }
 
-template <int D, int G, int SUB, bool BAL>
+// LVL: some unit may have more than kTauFewItems items, whose per-item level
+// counts the threshold kernel reads (every unit's are written then)
+template <int D, int G, int SUB, bool BAL, bool LVL>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(BAL || G > 4 ? 2 : 4))) void gather_mfma_kernel(
     DecodeArgs a, int slots) {
   constexpr int KB = D / 32;
@@ -406,7 +413,20 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(BAL
         keep[hh][s] = hv && msup[hh] > -INFINITY && (double)x[hh][s] > lb[hh];
         const unsigned long long bal = __ballot(keep[hh][s]);
         bits[hh][s] = (uint32_t)(bal >> (16 * grp)) & 0xffffu;
-        if (col == 0) reinterpret_cast<int*>(&s_cnt[hh][s][grp])[w] = __popc(bits[hh][s]);
+        // with LVL, the item's scores at or above its maximum - 1/32, - 1/16,
+        // - 1/8 (the threshold kernel's count bound on heads of many items),
+        // packed beside the kept count in 8-bit fields (at most 16 per wave,
+        // 64 per item)
+        uint32_t pk = __popc(bits[hh][s]);
+        if (LVL) {
+#pragma unroll
+          for (int k = 0; k < 3; ++k) {
+            const float lv = m[hh][s] - 0.03125f * (float)(1 << k);
+            const unsigned long long bl = __ballot(hv && x[hh][s] >= lv);
+            pk |= (uint32_t)__popc((uint32_t)(bl >> (16 * grp)) & 0xffffu) << (8 * (k + 1));
+          }
+        }
+        if (col == 0) reinterpret_cast<int*>(&s_cnt[hh][s][grp])[w] = (int)pk;
       }
     }
     if (has_next) refs_finish<SUB>(a, nxt, &ctx, tr);
@@ -421,8 +441,10 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(BAL
         const int j = sj * SUB + s;
         if (j >= n_items_cur) break;
         const int4 cv = s_cnt[hh][s][grp];
-        const int off = (w > 0 ? cv.x : 0) + (w > 1 ? cv.y : 0) + (w > 2 ? cv.z : 0);
-        const int tot = (cv.x + cv.y) + (cv.z + cv.w);
+        constexpr int FM = LVL ? 0xff : -1;  // the kept-count field (LVL packs level counts above it)
+        const int off = (w > 0 ? cv.x & FM : 0) + (w > 1 ? cv.y & FM : 0) + (w > 2 ? cv.z & FM : 0);
+        const uint32_t pks = (uint32_t)((cv.x + cv.y) + (cv.z + cv.w));  // the fields' sums (<= 64 each)
+        const int tot = (int)(pks & (uint32_t)FM);
         if (keep[hh][s]) {
           const int pos = off + __popc(bits[hh][s] & ((1u << col) - 1u));
           const size_t at = bh * tok_per_bh + (size_t)j * kItemTokens + pos;
@@ -434,6 +456,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(BAL
           a.item_cnt[bh * a.max_items + j] = tot;
           a.item_max[bh * a.max_items + j] = m[hh][s];
           a.item_lb[bh * a.max_items + j] = msup[hh] > -INFINITY ? __double2float_rd(lb[hh]) : -INFINITY;
+          if (LVL) a.item_lvl[bh * a.max_items + j] = pks >> 8;
         }
       }
     }
@@ -543,10 +566,16 @@ __global__ __launch_bounds__(kDecThreads) void gather_valu_kernel(DecodeArgs a, 
         a.cand_t[at] = s_t[lane];
         a.cand_r[at] = s_r[lane];
       }
+      uint32_t lv3 = 0u;  // scores at or above m - 1/32, - 1/16, - 1/8 (heads of many items)
+      if (ctx.n_items > kTauFewItems) {  // block-uniform
+#pragma unroll
+        for (int k = 0; k < 3; ++k) lv3 |= (uint32_t)__popcll(__ballot(x >= m - 0.03125f * (float)(1 << k))) << (8 * k);
+      }
       if (lane == 0) {
         a.item_cnt[bh * a.max_items + j] = __popcll(bal);
         a.item_max[bh * a.max_items + j] = m;
         a.item_lb[bh * a.max_items + j] = m > -INFINITY ? __double2float_rd((double)m - 1.0) : -INFINITY;
+        if (ctx.n_items > kTauFewItems) a.item_lvl[bh * a.max_items + j] = m > -INFINITY ? lv3 : 0u;
       }
     }
     __syncthreads();
@@ -782,7 +811,7 @@ template <int CAP> struct TauSmem {
 // Threshold, support and output of query head h of sequence b from the
 // candidate lists of its unit; the whole block takes part.
 template <int DT, int D, int AK, int CAP>
-__device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm) {
+__device__ __forceinline__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm) {
   using E = Elem<DT>;
   const int tid = threadIdx.x;
   const int G = a.group, g = h / G, Hkv = a.n_kv_heads, P = a.page_size;
@@ -803,10 +832,11 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
   const int32_t* icnt = a.item_cnt + bh * a.max_items;
   const float* imax = a.item_max + bh * a.max_items;
   const float* ilb = a.item_lb + bh * a.max_items;
+  const uint32_t* ilv = a.item_lvl + bh * a.max_items;
   // the first IPT * kTauThreads items' records are requested before the
   // unit's size is known (indices clamped to the unit's item slots, the
   // values past the unit's items masked once it is)
-  constexpr int IPT = 4;  // items per thread when n_items <= 1024
+  constexpr int IPT = kTauFewItems / kTauThreads;  // items per thread with few items
   int loc[IPT];
   float lmx[IPT], lbv[IPT];
 #pragma unroll
@@ -825,7 +855,7 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
   // ---- item counts and maxima (one round of loads) ----
   constexpr int RPT = 16;  // raw candidates per thread per round of the workspace path
   const int tid_w = tid >> 6;
-  const bool few_items = n_items <= IPT * kTauThreads;
+  const bool few_items = n_items <= kTauFewItems;
   float lmax = -INFINITY, llb = -INFINITY;
   if (few_items) {
 #pragma unroll
@@ -897,7 +927,64 @@ __device__ void tau_v_block(const DecodeArgs& a, int b, int h, TauSmem<CAP>& sm)
   // is their number, or -1 when they are too many for one collection round
   // and are listed against the final bound instead.
   int n_pre = -1;
-  {
+  if (!few_items) {  // block-uniform
+    // A head of many items (a long context of clustered keys) may have its
+    // top score standing alone, with the mass lower down: levels m - 1/32,
+    // - 1/16, - 1/8 and m - 1/4 .. m - 3/4 in steps of 1/8, and each item
+    // adds the most scores it is known to hold at or above a level: its
+    // counts at its own maximum M - 1/32, - 1/16, - 1/8 (the gather's, at the
+    // same float levels) where those lie at or above the level, else one
+    // score when M does.
+    constexpr int NL = 8;
+    float lvl[NL];
+    int nk[NL];
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      lvl[k] = mf - (k < 3 ? 0.03125f * (float)(1 << k) : 0.125f * (float)(k - 1));  // exact in float
+      nk[k] = 0;
+    }
+    for (int j0 = tid; j0 < n_items; j0 += 8 * kTauThreads) {
+      float vm[8];
+      uint32_t vv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u * kTauThreads;
+        vm[u] = load_or(imax, j, n_items, -INFINITY);
+        vv[u] = load_or(ilv, j, n_items, 0u);
+      }
+#pragma unroll 1
+      for (int u = 0; u < 8; ++u) {  // (not unrolled: keeps the kernel's code compact)
+        const float M = vm[u];
+        const float l1 = M - 0.03125f, l2 = M - 0.0625f, l3 = M - 0.125f;
+        const uint32_t lv = vv[u];
+        const int c1 = (int)(lv & 0xffu), c2 = (int)((lv >> 8) & 0xffu), c3 = (int)((lv >> 16) & 0xffu);
+#pragma unroll
+        for (int k = 0; k < NL; ++k)
+          nk[k] += l3 >= lvl[k] ? c3 : l2 >= lvl[k] ? c2 : l1 >= lvl[k] ? c1 : M >= lvl[k] ? 1 : 0;
+      }
+    }
+    // integer block sums of the level counts (one pair of barriers; the
+    // collection's table is free here)
+    constexpr int NWV = kTauThreads / kWave;
+    static_assert(NL * NWV <= 65, "level sums in one table half");
+#pragma unroll
+    for (int k = 0; k < NL; ++k) nk[k] = wave_sum(nk[k]);
+    __syncthreads();
+    if ((tid & 63) == 0) {
+#pragma unroll
+      for (int k = 0; k < NL; ++k) sm.s_tab[1][NL * tid_w + k] = nk[k];
+    }
+    __syncthreads();
+    double cb = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      int t = 0;
+#pragma unroll
+      for (int i = 0; i < NWV; ++i) t += sm.s_tab[1][NL * i + k];
+      if (t > 0) cb = fmax(cb, (double)lvl[k] - count_pow(t, a.alpha));
+    }
+    thr = fmax(thr, cb - 1e-6 * fmax(1.0, fabs(m)));
+  } else {
     float lvl[4];
     int nk[4];
 #pragma unroll
@@ -1647,10 +1734,13 @@ template <int DT, int D>
 static hipError_t decode_dispatch(const DecodeArgs& a, int slots, int bal_blocks, int cus, hipStream_t s) {
   const dim3 g1(slots, a.batch * a.n_kv_heads), b1(kDecThreads);
   const bool mfma = DT == EKV_BF16;
+  const bool lvl = a.max_items > kTauFewItems;  // some unit may have that many items
   if (mfma && bal_blocks > 0) {
-#define EKV_BAL(GG)                                                                               \
-  hipLaunchKernelGGL((gather_mfma_kernel<D, GG, 4, true>),                                        \
-                     dim3(resident_grid<gather_mfma_kernel<D, GG, 4, true>>(cus, bal_blocks)), b1, 0, s, a, 0)
+#define EKV_BAL1(GG, LV)                                                                          \
+  hipLaunchKernelGGL((gather_mfma_kernel<D, GG, 4, true, LV>),                                    \
+                     dim3(resident_grid<gather_mfma_kernel<D, GG, 4, true, LV>>(cus, bal_blocks)), b1, 0, s, a, 0)
+#define EKV_BAL(GG) \
+  if (lvl) EKV_BAL1(GG, true); else EKV_BAL1(GG, false)
     switch (a.group) {
       case 1: EKV_BAL(1); break;
       case 2: EKV_BAL(2); break;
@@ -1658,13 +1748,18 @@ static hipError_t decode_dispatch(const DecodeArgs& a, int slots, int bal_blocks
       default: EKV_BAL(8); break;
     }
 #undef EKV_BAL
+#undef EKV_BAL1
   } else if (mfma) {
+#define EKV_G(GG)                                                                                  \
+  if (lvl) hipLaunchKernelGGL((gather_mfma_kernel<D, GG, 4, false, true>), g1, b1, 0, s, a, slots); \
+  else hipLaunchKernelGGL((gather_mfma_kernel<D, GG, 4, false, false>), g1, b1, 0, s, a, slots)
     switch (a.group) {
-      case 1: hipLaunchKernelGGL((gather_mfma_kernel<D, 1, 4, false>), g1, b1, 0, s, a, slots); break;
-      case 2: hipLaunchKernelGGL((gather_mfma_kernel<D, 2, 4, false>), g1, b1, 0, s, a, slots); break;
-      case 4: hipLaunchKernelGGL((gather_mfma_kernel<D, 4, 4, false>), g1, b1, 0, s, a, slots); break;
-      default: hipLaunchKernelGGL((gather_mfma_kernel<D, 8, 4, false>), g1, b1, 0, s, a, slots); break;
+      case 1: EKV_G(1); break;
+      case 2: EKV_G(2); break;
+      case 4: EKV_G(4); break;
+      default: EKV_G(8); break;
     }
+#undef EKV_G
   } else {
     switch (a.group) {
       case 1: hipLaunchKernelGGL((gather_valu_kernel<DT, D, 1>), g1, b1, 0, s, a, slots); break;

@@ -82,6 +82,7 @@ struct DecodeArgs {
   int32_t* item_cnt;
   float* item_max;
   float* item_lb;
+  uint32_t* item_lvl;
   float* cand_x;
   int32_t* cand_t;
   int32_t* cand_r;

@@ -109,10 +109,10 @@ def test_select_validation(L):
     assert call_select(L, s=big, cap=70000, p=sp(min_pages=2, **g)) == B.EKV_ERR_UNSUPPORTED
     # selection needs only the cap-independent part of the workspace: the
     # size for one-page lists less its per-item regions (one 64-token item
-    # per query head: three per-item arrays, six per-token arrays, 256-byte
+    # per query head: four per-item arrays, six per-token arrays, 256-byte
     # aligned), one byte short
     a256 = lambda x: (x + 255) // 256 * 256
-    items1 = 3 * a256(4 * 32) + 6 * a256(4 * 32 * 64)
+    items1 = 4 * a256(4 * 32) + 6 * a256(4 * 32 * 64)
     assert call_select(L, wsb=ws_size(L, cap=1) - items1 - 1) == B.EKV_ERR_WORKSPACE
 
 

@@ -86,7 +86,7 @@ def test_noalloc_rejects_oversized_lists():
     sess = DecodeSession(batch=1, n_kv_heads=8, n_q_heads=64, head_dim=128, page_size=64,
                          kv_dtype=ekv.EKV_BF16, n_phys_pages=1, page_table=table, cap=4096, full_decode=False)
     q = torch.zeros((1, 64, 128), dtype=torch.float32, device="cuda")
-    # the full cache: 64 heads x 4096 items x 1548 bytes, above 64 MiB
+    # the full cache: 64 heads x 4096 items x 1552 bytes, above 64 MiB
     with pytest.raises(ekv.EntmaxKVError) as e:
         ekv.entmax_decode_noalloc(sess.cache, sess.seqs, q, 64, alpha=1.5, scale=0.1, out=sess.out)
     assert e.value.status == ekv.EKV_ERR_WORKSPACE and "scratch" in str(e.value)
