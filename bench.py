@@ -722,7 +722,7 @@ def main():
     ap.add_argument("--alpha", type=float, default=0.0, help="override the workload's entmax alpha")
     ap.add_argument("--q-heads", type=int, default=0,
                     help="override the workload's query-head count (query groups of other sizes)")
-    ap.add_argument("--cpu-units", type=int, default=4, help="(sequence, KV head) units the CPU oracle is timed on")
+    ap.add_argument("--cpu-units", type=int, default=8, help="(sequence, KV head) units the CPU oracle is timed on")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline line: context sweep 32K..1M of the top-2%% and Gaussian "
                          "million-token workloads (one JSON line with a 'sweep' list)")
@@ -801,9 +801,10 @@ def main():
             "kind": "oracle",
             "sample": (f"float64 numpy oracle on the host, inputs prepared outside the timing: sparse step "
                        f"({spec.policy} scoring from prebuilt page metadata, selection, exact entmax over the "
-                       f"kept pages) on {len(units)} of {n_units} (sequence, KV head) units of {spec.name}, "
-                       f"median of 3 per unit, scaled to all units; full-cache entmax on {len(dense_units)} "
-                       f"units, scaled"),
+                       f"kept pages) on " + (f"all {n_units}" if len(units) == n_units else f"{len(units)} of {n_units}")
+                       + f" (sequence, KV head) units of {spec.name}, median of 3 per unit"
+                       + ("" if len(units) == n_units else ", scaled to all units")
+                       + f"; full-cache entmax on {len(dense_units)} units, scaled"),
         }
     med_us = main_sum["us_per_step"]
     sm_us = main_sum["score_kernel_us"]
